@@ -1,0 +1,207 @@
+/*
+ * mf.h -- C ABI of the packed 2D-RoPE variable-length attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the data-parallel hot path of native-resolution
+ * packed joint self-attention as the Mage-Flow pages describe it:
+ *   - variable-length text and image-latent token segments packed into one
+ *     contiguous stream under a token budget, with per-sample (row, col)
+ *     positions (Mage-Flow paper section 3.2.1 "Model Architecture and Native
+ *     Packing", paperlayer.ai summary; rcap.io post, "native-resolution packed
+ *     step" pseudo-code);
+ *   - per-sample 2D rotary position embedding on Q and K (same pseudo-code;
+ *     ai.thesatyajit.com explainer, "A backbone that doesn't crop");
+ *   - block-diagonal, non-causal multi-head attention over the packed stream,
+ *     forward with log-sum-exp and backward (paper section 3.2.1; the pages
+ *     name variable-length attention kernels for this step).
+ * Packed classifier-free guidance needs no call of its own: the conditional
+ * and unconditional branches of a prompt are two consecutive samples
+ * (paper section 3.2.1; hyper.ai summary, "Experiment").
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  Inputs are
+ *     const; outputs are written only where documented.  The library keeps
+ *     no global state and never allocates device memory: scratch space comes
+ *     from the caller's `workspace`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and never synchronises.
+ *   - Every call validates its host arguments first; on an error it returns a
+ *     negative mf_status and launches nothing.  A launch failure reported by
+ *     the HIP runtime returns MF_ERR_HIP.
+ *   - Tensors q, k, v, o, dout, dq, dk, dv have layout [n_tokens][n_heads]
+ *     [head_dim], contiguous, 16-byte aligned.  q and k hold UN-rotated
+ *     values; the library applies the rotation.  lse is [n_heads][n_tokens]
+ *     float32 (natural log).
+ *   - dtype MF_BF16: bfloat16 tensors; MF_F32: float32 tensors, rounded to
+ *     bfloat16 (round-to-nearest-even) for the matrix products, with float32
+ *     outputs.  Accumulation and softmax are float32 in both cases.
+ *   - Positions, offsets and counts are int32.  pos is [n_tokens][2] =
+ *     (row, col).
+ *
+ * Readings taken where the pages give no formula
+ *   - pack: the longest order-preserving prefix of the samples that fits the
+ *     budget; each sample is [its text tokens | its image grid, row-major];
+ *   - positions: text token u of a sample is at (u, u); image token (r, c)
+ *     is at (text_len + r, text_len + c);
+ *   - rotation: dims [0, D/2) turn by the row and [D/2, D) by the column;
+ *     adjacent pairs (2j, 2j+1), j < D/4, turn by p * theta^(-2j/(D/2))
+ *     (the original rotary pairing);
+ *   - softmax scale 1/sqrt(head_dim) unless given.
+ */
+#ifndef MF_H_
+#define MF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mf_status;
+
+#define MF_OK 0
+#define MF_ERR_INVALID_ARG (-1)  /* null pointer, bad size, misaligned pointer */
+#define MF_ERR_UNSUPPORTED (-2)  /* head_dim not 64/128, unknown dtype */
+#define MF_ERR_WORKSPACE (-3)    /* workspace smaller than the size query returns */
+#define MF_ERR_HIP (-4)          /* the HIP runtime reported a launch error */
+
+#define MF_BF16 0
+#define MF_F32 1
+
+#define MF_ABI_VERSION 1
+
+/* One sample descriptor: text tokens, then a grid_h x grid_w latent grid. */
+typedef struct mf_sample {
+  int32_t text_len;
+  int32_t grid_h;
+  int32_t grid_w;
+} mf_sample;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* mf_status_string(mf_status status);
+
+/* MF_ABI_VERSION of the built library. */
+int32_t mf_abi_version(void);
+
+/*
+ * mf_pack -- native-resolution packing (Mage-Flow paper section 3.2.1
+ * "Model Architecture and Native Packing": variable-length text and image
+ * sequences packed under a fixed token budget without text padding, each
+ * image keeping its native latent grid; rcap.io post, the `pack(...,
+ * budget=50_000)` step of its pseudo-code).
+ *
+ * samples      [n_samples] device array of descriptors (n_samples >= 0).
+ * token_budget maximum packed tokens (>= 0).  The longest prefix of samples
+ *              whose lengths text_len + grid_h * grid_w sum to at most the
+ *              budget is packed; nothing is reordered, split or skipped.
+ * cu_seqlens   [n_samples + 1] out.  cu_seqlens[i] = start of sample i for
+ *              i <= n_packed; entries past n_packed hold n_tokens, so the
+ *              array can be handed to the attention calls with
+ *              n_segments = n_samples (trailing segments are empty).
+ * cu_pieces    [2 * n_samples + 1] out, or NULL.  cu_pieces[2i] = start of
+ *              sample i, cu_pieces[2i+1] = start of its image tokens; entries
+ *              past 2 * n_packed hold n_tokens.
+ * pos          [token_budget][2] out: (row, col) of packed token t for
+ *              t < n_tokens; later rows are not written.
+ * counts       [4] out: {n_packed, n_tokens, max_seqlen, max_pos} where
+ *              max_pos = 1 + the largest coordinate in pos (0 if empty).  A
+ *              negative field in any descriptor, or a sample longer than
+ *              2^31 - 1 tokens, gives counts = {-1, 0, 0, 0} and all-zero
+ *              offsets.
+ * text_rows, image_rows
+ *              [n_samples] device arrays of device pointers, or both NULL.
+ *              text_rows[i] holds text_len rows, image_rows[i] holds
+ *              grid_h * grid_w rows in row-major grid order, row_bytes each.
+ *              A pointer for an empty part may be NULL.
+ * row_bytes    bytes per row (> 0 when gathering).
+ * packed       [token_budget][row_bytes] out, or NULL: packed row t is a bit
+ *              copy of its source row, for t < n_tokens.
+ * Two kernels: a single-workgroup scan, then a fill of positions and rows.
+ */
+mf_status mf_pack(const mf_sample* samples, int32_t n_samples, int32_t token_budget,
+                  int32_t* cu_seqlens, int32_t* cu_pieces, int32_t* pos, int32_t* counts,
+                  const void* const* text_rows, const void* const* image_rows,
+                  int64_t row_bytes, void* packed, void* stream);
+
+/* Bytes of workspace mf_rope2d_apply needs: the cos/sin table. */
+size_t mf_rope2d_workspace_size(int32_t head_dim, int32_t max_pos);
+
+/*
+ * mf_rope2d_apply -- per-sample axial 2D rotary embedding, in place (rcap.io
+ * post, `per_sample_2d_rope` in the "native-resolution packed step"
+ * pseudo-code; Mage-Flow paper section 3.3 lists RoPE among the fused
+ * memory-bound chains).
+ *
+ * x        [n_tokens][n_heads][head_dim] in/out, dtype MF_BF16 or MF_F32.
+ * pos      [n_tokens][2] (row, col); every coordinate must lie in
+ *          [0, max_pos) (coordinates outside are clamped into it).
+ * theta    frequency base (> 0), 10000 in the workloads here.
+ * inverse  0: rotate by +angle; 1: by -angle (the transpose).
+ * workspace >= mf_rope2d_workspace_size(head_dim, max_pos) bytes, 256-byte
+ *          aligned.
+ */
+mf_status mf_rope2d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens,
+                          int32_t n_heads, int32_t head_dim, double theta, int32_t max_pos,
+                          int32_t inverse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Bytes of workspace the attention calls need (backward != 0: backward). */
+size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                     int32_t n_segments, int32_t max_pos, int32_t dtype,
+                                     int32_t backward);
+
+/*
+ * mf_varlen_attn_fwd -- block-diagonal multi-head attention over packed
+ * segments, with 2D RoPE on Q and K (Mage-Flow paper section 3.2.1: joint
+ * self-attention over the concatenated text and image tokens of a sample;
+ * packed samples never attend to each other).
+ *
+ * For every segment s = [cu_seqlens[s], cu_seqlens[s+1]) and head h:
+ *   S = softmax_scale * R(pos) q . (R(pos) k)^T   (non-causal, inside s)
+ *   o = softmax(S) v,  lse = log(sum(exp(S))) per row.
+ * q, k, v      [n_tokens][n_heads][head_dim] in.
+ * o            same shape, out; rows outside every segment are not written.
+ * lse          [n_heads][n_tokens] float32 out, or NULL.
+ * cu_seqlens   [n_segments + 1] non-decreasing offsets within [0, n_tokens].
+ * max_seqlen   an upper bound on every segment length (host value).
+ * pos          [n_tokens][2] positions in [0, max_pos), or NULL for no
+ *              rotation (then theta and max_pos are ignored).
+ * softmax_scale 0 selects 1/sqrt(head_dim).
+ * head_dim     64 or 128.
+ * workspace    >= mf_varlen_attn_workspace_size(..., backward = 0) bytes.
+ */
+mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
+                             int32_t max_seqlen, const int32_t* pos, double theta,
+                             int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                             int32_t head_dim, float softmax_scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * mf_varlen_attn_bwd -- gradients of the attention above with respect to
+ * the un-rotated q and k and to v, given dout (the training step the pages
+ * sketch runs backward through the packed blocks: rcap.io pseudo-code; paper
+ * section 3.3 reports fused forward-and-backward steps).
+ *
+ * o, lse       the forward's outputs on the same q, k, v.
+ * dout         [n_tokens][n_heads][head_dim] in.
+ * dq, dk, dv   same shape, out; rows outside every segment are not written.
+ * With P = softmax(S): dv = P^T dout, dS = P * (dout v^T - rowsum(dout*o)),
+ * dq = R(pos)^T (scale dS kr), dk = R(pos)^T (scale dS^T qr).  Deterministic:
+ * no atomics, the same inputs give bit-identical outputs.
+ * workspace    >= mf_varlen_attn_workspace_size(..., backward = 1) bytes.
+ */
+mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
+                             int32_t max_seqlen, const int32_t* pos, double theta,
+                             int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                             int32_t head_dim, float softmax_scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MF_H_ */

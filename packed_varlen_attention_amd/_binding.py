@@ -1,0 +1,186 @@
+"""ctypes binding of libmf.so (include/mf.h).
+
+Argument marshalling only: every function here passes device pointers, sizes
+and the current HIP stream to the C ABI call of the same name and raises
+``MFError`` on a negative status.  All computation happens in the HIP
+kernels; there is no fallback of any kind.  PyTorch supplies device memory and
+the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmf.so")
+
+MF_OK = 0
+MF_ERR_INVALID_ARG = -1
+MF_ERR_UNSUPPORTED = -2
+MF_ERR_WORKSPACE = -3
+MF_ERR_HIP = -4
+MF_BF16 = 0
+MF_F32 = 1
+
+EXPORTED = (
+    "mf_status_string", "mf_abi_version", "mf_pack", "mf_rope2d_workspace_size",
+    "mf_rope2d_apply", "mf_varlen_attn_workspace_size", "mf_varlen_attn_fwd",
+    "mf_varlen_attn_bwd",
+)
+
+
+class MFError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed with status {status}: {status_string(status)}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_dbl = ctypes.c_double
+_f32 = ctypes.c_float
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmf.so (built in-tree by packed_varlen_attention_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m packed_varlen_attention_amd.build` "
+            "(hipcc for gfx950); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    lib.mf_status_string.restype = ctypes.c_char_p
+    lib.mf_status_string.argtypes = [_i32]
+    lib.mf_abi_version.restype = _i32
+    lib.mf_abi_version.argtypes = []
+    lib.mf_pack.restype = _i32
+    lib.mf_pack.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp]
+    lib.mf_rope2d_workspace_size.restype = _sz
+    lib.mf_rope2d_workspace_size.argtypes = [_i32, _i32]
+    lib.mf_rope2d_apply.restype = _i32
+    lib.mf_rope2d_apply.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, _dbl, _i32, _i32, _vp, _sz, _vp]
+    lib.mf_varlen_attn_workspace_size.restype = _sz
+    lib.mf_varlen_attn_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+    lib.mf_varlen_attn_fwd.restype = _i32
+    lib.mf_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _dbl, _i32,
+                                       _i32, _i32, _i32, _f32, _vp, _sz, _vp]
+    lib.mf_varlen_attn_bwd.restype = _i32
+    lib.mf_varlen_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                       _vp, _dbl, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]
+    _lib = lib
+    return lib
+
+
+def lib() -> ctypes.CDLL:
+    return _lib if _lib is not None else load_library()
+
+
+def status_string(status: int) -> str:
+    return lib().mf_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().mf_abi_version())
+
+
+def _check(status: int, call: str) -> None:
+    if status != MF_OK:
+        raise MFError(int(status), call)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MF_BF16
+    if t.dtype == torch.float32:
+        return MF_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# 1:1 wrappers of the C ABI
+# ---------------------------------------------------------------------------
+
+def mf_pack(samples: torch.Tensor, token_budget: int, cu_seqlens: torch.Tensor,
+            cu_pieces: Optional[torch.Tensor], pos: torch.Tensor, counts: torch.Tensor,
+            text_rows: Optional[torch.Tensor] = None, image_rows: Optional[torch.Tensor] = None,
+            row_bytes: int = 0, packed: Optional[torch.Tensor] = None, stream=None) -> None:
+    """samples: int32 [S, 3] on the GPU; text_rows/image_rows: int64 [S] device
+    tensors holding row-buffer addresses."""
+    if samples.dtype != torch.int32 or samples.dim() != 2 or samples.shape[1] != 3:
+        raise ValueError("samples must be an int32 [S, 3] tensor")
+    st = lib().mf_pack(_ptr(samples), int(samples.shape[0]), int(token_budget), _ptr(cu_seqlens),
+                       _ptr(cu_pieces), _ptr(pos), _ptr(counts), _ptr(text_rows), _ptr(image_rows),
+                       int(row_bytes), _ptr(packed), _stream(stream))
+    _check(st, "mf_pack")
+
+
+def mf_rope2d_workspace_size(head_dim: int, max_pos: int) -> int:
+    return int(lib().mf_rope2d_workspace_size(int(head_dim), int(max_pos)))
+
+
+def mf_rope2d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: int,
+                    inverse: bool, workspace: torch.Tensor, stream=None) -> None:
+    n, h, d = x.shape
+    st = lib().mf_rope2d_apply(_ptr(x), dtype_code(x), _ptr(pos), int(n), int(h), int(d), float(theta),
+                               int(max_pos), int(bool(inverse)), _ptr(workspace),
+                               int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(st, "mf_rope2d_apply")
+
+
+def mf_varlen_attn_workspace_size(n_tokens: int, n_heads: int, head_dim: int, n_segments: int,
+                                  max_pos: int, dtype: int, backward: bool) -> int:
+    return int(lib().mf_varlen_attn_workspace_size(int(n_tokens), int(n_heads), int(head_dim),
+                                                   int(n_segments), int(max_pos), int(dtype),
+                                                   int(bool(backward))))
+
+
+def mf_varlen_attn_fwd(q, k, v, o, lse, cu_seqlens, n_segments: int, max_seqlen: int, pos,
+                       theta: float, max_pos: int, softmax_scale: float, workspace, stream=None) -> None:
+    n, h, d = q.shape
+    st = lib().mf_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dtype_code(q),
+                                  _ptr(cu_seqlens), int(n_segments), int(max_seqlen), _ptr(pos),
+                                  float(theta), int(max_pos), int(n), int(h), int(d), float(softmax_scale),
+                                  _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                  _stream(stream))
+    _check(st, "mf_varlen_attn_fwd")
+
+
+def mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, n_segments: int, max_seqlen: int,
+                       pos, theta: float, max_pos: int, softmax_scale: float, workspace,
+                       stream=None) -> None:
+    n, h, d = q.shape
+    st = lib().mf_varlen_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), dtype_code(q), _ptr(cu_seqlens), int(n_segments),
+                                  int(max_seqlen), _ptr(pos), float(theta), int(max_pos), int(n), int(h),
+                                  int(d), float(softmax_scale), _ptr(workspace),
+                                  int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(st, "mf_varlen_attn_bwd")

@@ -1,0 +1,85 @@
+"""Allocation helpers over the C ABI wrappers.
+
+Each helper allocates its outputs (and workspace, unless one is passed) with
+PyTorch on the inputs' device and makes exactly one C ABI call.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _binding as B
+
+
+@dataclass
+class PackResult:
+    cu_seqlens: torch.Tensor  # int32 [S + 1]
+    cu_pieces: torch.Tensor   # int32 [2 S + 1]
+    pos: torch.Tensor         # int32 [token_budget, 2]
+    counts: torch.Tensor      # int32 [4]: n_packed, n_tokens, max_seqlen, max_pos
+    packed: Optional[torch.Tensor]  # uint8 [token_budget, row_bytes] or None
+
+
+def pack(samples: torch.Tensor, token_budget: int, text_rows: Optional[torch.Tensor] = None,
+         image_rows: Optional[torch.Tensor] = None, row_bytes: int = 0, stream=None) -> PackResult:
+    dev = samples.device
+    s = int(samples.shape[0])
+    cu = torch.empty(s + 1, dtype=torch.int32, device=dev)
+    pieces = torch.empty(2 * s + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((max(int(token_budget), 1), 2), dtype=torch.int32, device=dev)
+    counts = torch.empty(4, dtype=torch.int32, device=dev)
+    packed = None
+    if text_rows is not None:
+        packed = torch.empty((max(int(token_budget), 1), int(row_bytes)), dtype=torch.uint8, device=dev)
+    B.mf_pack(samples, token_budget, cu, pieces, pos, counts, text_rows, image_rows, row_bytes, packed, stream)
+    return PackResult(cu, pieces, pos, counts, packed)
+
+
+def rope2d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: int, inverse: bool = False,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if workspace is None:
+        workspace = torch.empty(max(B.mf_rope2d_workspace_size(x.shape[2], max_pos), 1), dtype=torch.uint8,
+                                device=x.device)
+    B.mf_rope2d_apply(x, pos, theta, max_pos, inverse, workspace, stream)
+    return x
+
+
+def attn_workspace(q: torch.Tensor, n_segments: int, max_pos: int, backward: bool) -> torch.Tensor:
+    n, h, d = q.shape
+    size = B.mf_varlen_attn_workspace_size(n, h, d, n_segments, max_pos, B.dtype_code(q), backward)
+    return torch.empty(max(size, 1), dtype=torch.uint8, device=q.device)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+             pos: Optional[torch.Tensor] = None, theta: float = 10000.0, max_pos: int = 0,
+             softmax_scale: float = 0.0, with_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    n, h, _ = q.shape
+    nseg = int(cu_seqlens.numel()) - 1
+    o = torch.empty_like(q) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty((h, n), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, False)
+    B.mf_varlen_attn_fwd(q, k, v, o, lse if with_lse else None, cu_seqlens, nseg, max_seqlen, pos, theta,
+                         max_pos, softmax_scale, workspace, stream)
+    return o, (lse if with_lse else None)
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, pos: Optional[torch.Tensor] = None,
+             theta: float = 10000.0, max_pos: int = 0, softmax_scale: float = 0.0,
+             workspace: Optional[torch.Tensor] = None, grads=None,
+             stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    nseg = int(cu_seqlens.numel()) - 1
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    if workspace is None:
+        workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, True)
+    B.mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nseg, max_seqlen, pos, theta, max_pos,
+                         softmax_scale, workspace, stream)
+    return dq, dk, dv

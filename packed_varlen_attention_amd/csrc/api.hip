@@ -1,0 +1,269 @@
+// Public C ABI (include/mf.h): host-side argument checks, workspace layout and
+// kernel launches.  Nothing here synchronises; every error is detected
+// before the first launch of a call.
+#include "../../include/mf.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "mf_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mf_status from_hip(hipError_t e) { return e == hipSuccess ? MF_OK : MF_ERR_HIP; }
+
+size_t elem_bytes(int32_t dtype) { return dtype == MF_F32 ? 4 : 2; }
+
+// Workspace of the attention calls, in order; each part 256-byte aligned.
+struct AttnWorkspace {
+  size_t tab = 0, kr = 0, qr = 0, vb = 0, dob = 0, delta = 0, total = 0;
+  size_t tab_off = 0, kr_off = 0, qr_off = 0, vb_off = 0, dob_off = 0, delta_off = 0;
+};
+
+AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t max_pos, int32_t dtype,
+                             bool backward) {
+  AttnWorkspace w;
+  const size_t tensor_bf16 = static_cast<size_t>(n_tokens) * n_heads * head_dim * 2;
+  w.tab = static_cast<size_t>(max_pos > 0 ? max_pos : 0) * (head_dim / 4) * sizeof(float2);
+  w.kr = tensor_bf16;  // rotated (or converted) K
+  w.qr = backward ? tensor_bf16 : 0;
+  w.vb = dtype == MF_F32 ? tensor_bf16 : 0;
+  w.dob = (backward && dtype == MF_F32) ? tensor_bf16 : 0;
+  w.delta = backward ? static_cast<size_t>(n_tokens) * n_heads * sizeof(float) : 0;
+  size_t off = 0;
+  w.tab_off = off;
+  off += align_up(w.tab);
+  w.kr_off = off;
+  off += align_up(w.kr);
+  w.qr_off = off;
+  off += align_up(w.qr);
+  w.vb_off = off;
+  off += align_up(w.vb);
+  w.dob_off = off;
+  off += align_up(w.dob);
+  w.delta_off = off;
+  off += align_up(w.delta);
+  w.total = off;
+  return w;
+}
+
+mf_status check_attn_common(int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                            const int32_t* pos, double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                            int32_t head_dim, float softmax_scale) {
+  if (dtype != MF_BF16 && dtype != MF_F32) return MF_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return MF_ERR_UNSUPPORTED;
+  if (cu_seqlens == nullptr) return MF_ERR_INVALID_ARG;
+  if (n_segments < 0 || n_segments > 65535 || max_seqlen < 0 || n_tokens < 0 || n_heads < 1 ||
+      n_heads > 65535)
+    return MF_ERR_INVALID_ARG;
+  if (!(softmax_scale >= 0.0f) || isinf(softmax_scale)) return MF_ERR_INVALID_ARG;
+  if (pos != nullptr) {
+    if (max_pos < 1 || !(theta > 0.0) || isinf(theta)) return MF_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(pos) & 7u) != 0) return MF_ERR_INVALID_ARG;
+  }
+  return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mf_status_string(mf_status status) {
+  switch (status) {
+    case MF_OK:
+      return "ok";
+    case MF_ERR_INVALID_ARG:
+      return "invalid argument (null pointer, bad size or misaligned pointer)";
+    case MF_ERR_UNSUPPORTED:
+      return "unsupported configuration (head_dim must be 64 or 128; dtype MF_BF16 or MF_F32)";
+    case MF_ERR_WORKSPACE:
+      return "workspace too small";
+    case MF_ERR_HIP:
+      return "HIP runtime error at launch";
+    default:
+      return "unknown status";
+  }
+}
+
+int32_t mf_abi_version(void) { return MF_ABI_VERSION; }
+
+mf_status mf_pack(const mf_sample* samples, int32_t n_samples, int32_t token_budget, int32_t* cu_seqlens,
+                  int32_t* cu_pieces, int32_t* pos, int32_t* counts, const void* const* text_rows,
+                  const void* const* image_rows, int64_t row_bytes, void* packed, void* stream) {
+  if (n_samples < 0 || token_budget < 0) return MF_ERR_INVALID_ARG;
+  if (n_samples > (0x7fffffff - 1) / 2) return MF_ERR_INVALID_ARG;
+  if (cu_seqlens == nullptr || counts == nullptr) return MF_ERR_INVALID_ARG;
+  if (n_samples > 0 && samples == nullptr) return MF_ERR_INVALID_ARG;
+  if (token_budget > 0 && pos == nullptr) return MF_ERR_INVALID_ARG;
+  if (pos != nullptr && (reinterpret_cast<uintptr_t>(pos) & 7u) != 0) return MF_ERR_INVALID_ARG;
+  if (packed != nullptr) {
+    if (row_bytes <= 0 || text_rows == nullptr || image_rows == nullptr) return MF_ERR_INVALID_ARG;
+  } else if (text_rows != nullptr || image_rows != nullptr) {
+    return MF_ERR_INVALID_ARG;
+  }
+  return from_hip(mf::launch_pack(samples, n_samples, token_budget, cu_seqlens, cu_pieces, pos, counts, text_rows,
+                                  image_rows, packed ? row_bytes : 0, packed, static_cast<hipStream_t>(stream)));
+}
+
+size_t mf_rope2d_workspace_size(int32_t head_dim, int32_t max_pos) {
+  if (head_dim <= 0 || max_pos <= 0) return 0;
+  return align_up(static_cast<size_t>(max_pos) * (head_dim / 4) * sizeof(float2));
+}
+
+mf_status mf_rope2d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens, int32_t n_heads,
+                          int32_t head_dim, double theta, int32_t max_pos, int32_t inverse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (dtype != MF_BF16 && dtype != MF_F32) return MF_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return MF_ERR_UNSUPPORTED;
+  if (n_tokens < 0 || n_heads < 1 || max_pos < 1 || !(theta > 0.0) || isinf(theta)) return MF_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MF_OK;
+  if (x == nullptr || pos == nullptr || workspace == nullptr) return MF_ERR_INVALID_ARG;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(pos) & 7u) != 0 || !aligned16(workspace))
+    return MF_ERR_INVALID_ARG;
+  if (workspace_bytes < mf_rope2d_workspace_size(head_dim, max_pos)) return MF_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* tab = static_cast<float2*>(workspace);
+  hipError_t e = mf::launch_rope_table(tab, max_pos, head_dim, theta, s);
+  if (e != hipSuccess) return MF_ERR_HIP;
+  return from_hip(mf::launch_rope_apply(x, dtype, x, dtype, pos, tab, max_pos, n_tokens, n_heads, head_dim, true,
+                                        inverse != 0, s));
+}
+
+size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
+                                     int32_t max_pos, int32_t dtype, int32_t backward) {
+  (void)n_segments;
+  if (n_tokens < 0 || n_heads < 1 || (head_dim != 64 && head_dim != 128)) return 0;
+  return attn_workspace(n_tokens, n_heads, head_dim, max_pos, dtype, backward != 0).total;
+}
+
+mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                             const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
+                             double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
+                                   n_heads, head_dim, softmax_scale);
+  if (st != MF_OK) return st;
+  if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return MF_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MF_ERR_INVALID_ARG;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return MF_ERR_INVALID_ARG;
+  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, pos ? max_pos : 0, dtype, false);
+  if (workspace_bytes < w.total) return MF_ERR_WORKSPACE;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float2* tab = reinterpret_cast<float2*>(ws + w.tab_off);
+  const void* kr = k;
+  const void* vb = v;
+  hipError_t e = hipSuccess;
+  if (pos != nullptr) e = mf::launch_rope_table(tab, max_pos, head_dim, theta, s);
+  if (e != hipSuccess) return MF_ERR_HIP;
+  // K rotated once into bf16 (also converts float32 input); Q is rotated
+  // inside the attention kernel when it is loaded.
+  if (pos != nullptr || dtype == MF_F32) {
+    kr = ws + w.kr_off;
+    e = mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads, head_dim,
+                              pos != nullptr, false, s);
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
+  if (dtype == MF_F32) {
+    void* vconv = ws + w.vb_off;
+    e = mf::launch_rope_apply(v, dtype, vconv, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads, head_dim, false,
+                              false, s);
+    if (e != hipSuccess) return MF_ERR_HIP;
+    vb = vconv;
+  }
+  mf::AttnArgs a;
+  a.cu_seqlens = cu_seqlens;
+  a.n_segments = n_segments;
+  a.max_seqlen = max_seqlen;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.pos = pos;
+  a.tab = tab;
+  a.max_pos = max_pos;
+  a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  return from_hip(mf::launch_attn_fwd(a, q, kr, vb, o, lse, s));
+}
+
+mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, int32_t dtype, const int32_t* cu_seqlens,
+                             int32_t n_segments, int32_t max_seqlen, const int32_t* pos, double theta,
+                             int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
+                                   n_heads, head_dim, softmax_scale);
+  if (st != MF_OK) return st;
+  if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return MF_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return MF_ERR_INVALID_ARG;
+  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, pos ? max_pos : 0, dtype, true);
+  if (workspace_bytes < w.total) return MF_ERR_WORKSPACE;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float2* tab = reinterpret_cast<float2*>(ws + w.tab_off);
+  const void* kr = k;
+  const void* qr = q;
+  float* delta = reinterpret_cast<float*>(ws + w.delta_off);
+  const void* vb = v;
+  const void* dob = dout;
+  hipError_t e = hipSuccess;
+  if (pos != nullptr) e = mf::launch_rope_table(tab, max_pos, head_dim, theta, s);
+  if (e != hipSuccess) return MF_ERR_HIP;
+  if (pos != nullptr || dtype == MF_F32) {
+    qr = ws + w.qr_off;
+    kr = ws + w.kr_off;
+    e = mf::launch_rope_apply(q, dtype, ws + w.qr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads, head_dim,
+                              pos != nullptr, false, s);
+    if (e != hipSuccess) return MF_ERR_HIP;
+    e = mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads, head_dim,
+                              pos != nullptr, false, s);
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
+  if (dtype == MF_F32) {
+    void* vconv = ws + w.vb_off;
+    void* dconv = ws + w.dob_off;
+    e = mf::launch_rope_apply(v, dtype, vconv, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads, head_dim, false,
+                              false, s);
+    if (e != hipSuccess) return MF_ERR_HIP;
+    e = mf::launch_rope_apply(dout, dtype, dconv, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads, head_dim, false,
+                              false, s);
+    if (e != hipSuccess) return MF_ERR_HIP;
+    vb = vconv;
+    dob = dconv;
+  }
+  mf::AttnArgs a;
+  a.cu_seqlens = cu_seqlens;
+  a.n_segments = n_segments;
+  a.max_seqlen = max_seqlen;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.pos = pos;
+  a.tab = tab;
+  a.max_pos = max_pos;
+  a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  e = mf::launch_attn_bwd_delta(a, o, dout, delta, s);
+  if (e != hipSuccess) return MF_ERR_HIP;
+  e = mf::launch_attn_bwd_dkdv(a, qr, kr, vb, dob, lse, delta, dk, dv, s);
+  if (e != hipSuccess) return MF_ERR_HIP;
+  return from_hip(mf::launch_attn_bwd_dq(a, qr, kr, vb, dob, lse, delta, dq, s));
+}
+
+}  // extern "C"

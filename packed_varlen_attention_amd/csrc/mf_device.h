@@ -1,0 +1,205 @@
+// Device-side building blocks shared by the gfx950 kernels of this library:
+// vector types, bf16 conversion, the 32x32x16 bf16 MFMA, and LDS tile
+// addressing with the fragment loads the attention kernels feed to it.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 operand layout (wave64, h = lane / 32):
+//   A (32 x 16, M x K): lane holds A[m = lane % 32][k = 8h .. 8h + 7]
+//   B (16 x 32, K x N): lane holds B[k = 8h .. 8h + 7][n = lane % 32]
+//   C (32 x 32):        lane element i holds C[m = 8(i/4) + 4h + i%4][n = lane % 32]
+//
+// ds_read_b64_tr_b16 (LDS transpose read): inside each group of 16 lanes,
+// lane i receives, in slot t, element (i % 4) of the 8 bytes fetched by lane
+// 4t + i/4 of the same group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mf {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row permutation applied to A operands loaded from LDS: swaps bits 2 and 3
+// of the row index.  With it, accumulator element i of lane (h = lane / 32)
+// belongs to tile row 16(i/8) + 8h + (i % 8): each lane then holds 8
+// consecutive rows per 16-row chunk, exactly the K-operand fragment of the
+// next product, so no cross-lane shuffle is needed between the two products.
+__device__ __forceinline__ int perm32(int m) {
+  return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Tile row of accumulator element i for lane half h (after perm32 rows).
+__device__ __forceinline__ int acc_row(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
+
+// A [rows][D] bf16 tile in LDS, rows of D*2 bytes, 16-byte chunks XOR-swizzled
+// per row so that both row-fragment and transpose reads spread over banks.
+template <int D>
+struct Tile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (D == 128) {
+      return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+      return (row >> 1) & 7;
+    }
+  }
+  __device__ static __forceinline__ int off(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+  }
+};
+
+// A-operand fragment of rows [rbase, rbase + 32) (perm32 applied), columns
+// 16*kk + 8h .. +8:  X[rbase + perm32(lane % 32)][16 kk + 8h + j].
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_frag(const lds_char* tile, int rbase, int kk, int lane) {
+  const int row = rbase + perm32(lane & 31);
+  const int chunk = 2 * kk + (lane >> 5);
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + Tile<D>::off(row, chunk));
+}
+
+// Transposed fragment: X[rbase + 8h + j][dbase + lane % 32] for j = 0..7, as
+// the A operand of a product that reduces over rows (or its B operand with
+// the roles of m and n exchanged).  Two transpose reads of 4 rows each.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col_frag(const lds_char* tile, int rbase, int dbase, int lane) {
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int h = lane >> 5;
+  const int col = dbase + 16 * (g & 1) + 4 * (l16 & 3);
+  const int chunk = col >> 3;
+  const int half = (col >> 2) & 1;
+  const int row0 = rbase + 8 * h + (l16 >> 2);
+  const lds_char* p0 = tile + Tile<D>::off(row0, chunk) + half * 8;
+  const lds_char* p1 = tile + Tile<D>::off(row0 + 4, chunk) + half * 8;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p0)));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p1)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Load 8 consecutive elements of a bf16 or f32 row as float.
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __uint_as_float(v[j] << 16);
+    x[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = a[j];
+    x[4 + j] = b[j];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float (&x)[8]) {
+  u32x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = x[j];
+    b[j] = x[4 + j];
+  }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+
+// Store 4 consecutive elements.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+  u32x2 v;
+  v[0] = pack_bf16x2(a, b);
+  v[1] = pack_bf16x2(c, d);
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// Rotate 8 consecutive elements x[0..7] of one head row starting at element
+// e0 (a multiple of 8) by the axial 2D rotation of position (row, col).
+// tab holds float2 (cos, sin) of p * theta^(-2j/(D/2)), [max_pos][D/4].
+// sign = +1 forward, -1 inverse.
+template <int D>
+__device__ __forceinline__ void rotate8(float (&x)[8], int e0, int prow, int pcol,
+                                        const float2* __restrict__ tab, int max_pos, float sign) {
+  const int half = e0 / (D / 2);
+  int p = half ? pcol : prow;
+  p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+  const int j0 = (e0 % (D / 2)) / 2;
+  const float2* t = tab + static_cast<size_t>(p) * (D / 4) + j0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float2 cs = t[j];
+    const float c = cs.x;
+    const float s = sign * cs.y;
+    const float a = x[2 * j];
+    const float b = x[2 * j + 1];
+    x[2 * j] = a * c - b * s;
+    x[2 * j + 1] = a * s + b * c;
+  }
+}
+
+}  // namespace mf

@@ -1,0 +1,54 @@
+// Host-side launchers of the library's kernels (internal; the public C ABI
+// lives in include/mf.h and csrc/api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace mf {
+
+constexpr int kDtypeBf16 = 0;
+constexpr int kDtypeF32 = 1;
+
+hipError_t launch_pack(const void* samples, int n, int budget, int* cu_seqlens, int* cu_pieces, int* pos,
+                       int* counts, const void* const* text_rows, const void* const* image_rows,
+                       long long row_bytes, void* packed, hipStream_t stream);
+
+hipError_t launch_rope_table(float2* tab, int max_pos, int head_dim, double theta, hipStream_t stream);
+
+// dst = rotate(src) (or a plain copy/convert when rotate is false).
+hipError_t launch_rope_apply(const void* src, int src_dtype, void* dst, int dst_dtype, const int* pos,
+                             const float2* tab, int max_pos, int n_tokens, int heads, int head_dim,
+                             bool rotate, bool inverse, hipStream_t stream);
+
+struct AttnArgs {
+  const int* cu_seqlens;
+  int n_segments;
+  int max_seqlen;
+  int n_tokens;
+  int n_heads;
+  int head_dim;
+  int dtype;  // of q/k/v/o/dout/dq/dk/dv
+  const int* pos;  // nullptr: no rotation
+  const float2* tab;
+  int max_pos;
+  float scale;
+};
+
+// q: caller's (rotated in-kernel), kr/vb: bf16 [N][H][D] (kr already rotated).
+hipError_t launch_attn_fwd(const AttnArgs& a, const void* q, const void* kr, const void* vb, void* o,
+                           float* lse, hipStream_t stream);
+
+hipError_t launch_attn_bwd_delta(const AttnArgs& a, const void* o, const void* dout, float* delta,
+                                 hipStream_t stream);
+
+// qr/kr rotated bf16, vb/dob bf16; outputs in a.dtype.
+hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, const void* qr, const void* kr, const void* vb,
+                                const void* dob, const float* lse, const float* delta, void* dk, void* dv,
+                                hipStream_t stream);
+
+hipError_t launch_attn_bwd_dq(const AttnArgs& a, const void* qr, const void* kr, const void* vb,
+                              const void* dob, const float* lse, const float* delta, void* dq,
+                              hipStream_t stream);
+
+}  // namespace mf

@@ -1,0 +1,110 @@
+"""Helpers shared by the GPU parity tests (host <-> device marshalling and
+error metrics).  Expected values always come from ``oracle``."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+THETA = 10000.0
+
+
+def note(msg: str) -> None:
+    """Name the case about to run on the GPU (flushed, so it survives a crash)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return workloads.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def samples_dev(samples) -> torch.Tensor:
+    return torch.tensor(np.asarray(samples, dtype=np.int32).reshape(-1, 3)).cuda()
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    diff = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    return float(diff.max()) if diff.size else 0.0, float(diff.mean()) if diff.size else 0.0
+
+
+def assert_close(got, ref, max_abs: float, mean_abs: float, label: str) -> None:
+    mx, mn = errors(got, ref)
+    ref = np.asarray(ref)
+    rel = float(np.sqrt(np.mean((np.asarray(got) - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30)) \
+        if ref.size else 0.0
+    print(f"  {label}: max_abs={mx:.3e} mean_abs={mn:.3e} rel_rms={rel:.3e} max|ref|={np.abs(ref).max() if ref.size else 0:.3e}",
+          flush=True)
+    assert np.isfinite(np.asarray(got)).all(), f"{label}: non-finite values"
+    assert mx <= max_abs, f"{label}: max-abs {mx} > {max_abs}"
+    assert mn <= mean_abs, f"{label}: mean-abs {mn} > {mean_abs}"
+
+
+def assert_close_scaled(got, ref, label: str, rel_rms_max: float = 8e-3) -> None:
+    """Bar for inputs scaled away from N(0, 1) (the peaky gates): the fixed
+    2e-2 max-abs bar holds for outputs up to |4|, so it grows with max|ref|
+    beyond that; the relative RMS error must stay at the bf16 level."""
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = max(1.0, float(np.abs(ref).max()) / 4.0) if ref.size else 1.0
+    mx, mn = errors(got, ref)
+    rel = float(np.sqrt(np.mean((np.asarray(got) - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
+    print(f"  {label}: max_abs={mx:.3e} (bar {2e-2 * scale:.3e}) rel_rms={rel:.3e} max|ref|={np.abs(ref).max():.3e}",
+          flush=True)
+    assert np.isfinite(np.asarray(got)).all(), f"{label}: non-finite values"
+    assert mx <= 2e-2 * scale, f"{label}: max-abs {mx} > {2e-2 * scale}"
+    assert rel <= rel_rms_max, f"{label}: relative rms {rel} > {rel_rms_max}"
+
+
+class Case:
+    """A packed workload with inputs on host (as exact float32 values) and GPU."""
+
+    def __init__(self, samples, budget, heads, head_dim, dtype, seed, qscale=1.0, with_dout=False):
+        self.samples = [tuple(int(v) for v in s) for s in samples]
+        self.budget = budget
+        p = oracle.pack(self.samples, budget)
+        self.pack = p
+        self.n = p["n_tokens"]
+        self.cu = p["cu_seqlens"]
+        self.pos = oracle.positions(self.samples, p["n_packed"])
+        self.max_seqlen = p["max_seqlen"]
+        self.max_pos = max(p["max_pos"], 1)
+        self.heads, self.d, self.dtype = heads, head_dim, dtype
+        q, k, v = workloads.qkv(seed, self.n, heads, head_dim, dtype)
+        if qscale != 1.0:
+            q = workloads.normal(seed, workloads.STREAM_Q, (self.n, heads, head_dim), dtype, scale=qscale)
+        self.q_bits, self.k_bits, self.v_bits = q, k, v
+        self.q = self._f32(q)
+        self.k = self._f32(k)
+        self.v = self._f32(v)
+        self.dq_dev = None
+        if with_dout:
+            self.do_bits = workloads.dout(seed, self.n, heads, head_dim, dtype)
+            self.do = self._f32(self.do_bits)
+        self.tq = dev(q, dtype)
+        self.tk = dev(k, dtype)
+        self.tv = dev(v, dtype)
+        self.tcu = torch.from_numpy(self.cu.astype(np.int32)).cuda()
+        self.tpos = torch.from_numpy(self.pos.astype(np.int32).reshape(-1, 2)).cuda() if self.n else \
+            torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+        if with_dout:
+            self.tdo = dev(self.do_bits, dtype)
+
+    def _f32(self, x):
+        return workloads.bf16_bits_to_f32(x) if self.dtype == "bf16" else np.asarray(x, dtype=np.float32)
+
+    def describe(self) -> str:
+        return (f"N={self.n} segments={len(self.cu) - 1} H={self.heads} D={self.d} {self.dtype} "
+                f"max_seqlen={self.max_seqlen}")

@@ -1,0 +1,123 @@
+"""CPU checks of the C ABI library: it loads, exports every function that
+include/mf.h declares, and rejects bad host arguments before launching
+anything (these calls never reach a kernel, so no GPU is needed)."""
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "mf.h"
+LIB = ROOT / "packed_varlen_attention_amd" / "libmf.so"
+
+
+def _declared():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mf_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not LIB.exists():
+        pytest.fail(f"{LIB} not built: run `python -m packed_varlen_attention_amd.build`")
+    import packed_varlen_attention_amd as m
+    return m._binding.lib()
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("mf_pack", "mf_rope2d_apply", "mf_varlen_attn_fwd", "mf_varlen_attn_bwd"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(str(LIB))
+    for name in _declared():
+        assert hasattr(raw, name), name
+    import packed_varlen_attention_amd as m
+    assert set(m.EXPORTED) == set(_declared())
+
+
+def test_status_strings_and_version(lib):
+    import packed_varlen_attention_amd as m
+    assert m.abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert len(m.status_string(code)) > 0
+    assert m.status_string(7) == "unknown status"
+
+
+FAKE = 1 << 20  # a 256-byte-aligned non-null address; never dereferenced by these calls
+
+
+def _fwd(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dtype=0, cu=FAKE, nseg=1, maxlen=8, pos=FAKE,
+                theta=10000.0, max_pos=16, n=8, h=1, d=128, scale=0.0, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.mf_varlen_attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dtype"],
+                                  args["cu"], args["nseg"], args["maxlen"], args["pos"], args["theta"],
+                                  args["max_pos"], args["n"], args["h"], args["d"], args["scale"], args["ws"],
+                                  args["wsb"], args["stream"])
+
+
+def test_forward_argument_errors(lib):
+    assert _fwd(lib, d=96) == -2
+    assert _fwd(lib, dtype=3) == -2
+    assert _fwd(lib, q=None) == -1
+    assert _fwd(lib, cu=None) == -1
+    assert _fwd(lib, q=FAKE + 8) == -1       # misaligned
+    assert _fwd(lib, h=0) == -1
+    assert _fwd(lib, n=-1) == -1
+    assert _fwd(lib, max_pos=0) == -1
+    assert _fwd(lib, theta=-1.0) == -1
+    assert _fwd(lib, scale=-1.0) == -1
+    assert _fwd(lib, wsb=16) == -3
+    assert _fwd(lib, ws=None) == -1
+    # nothing to do is OK and launches nothing
+    assert _fwd(lib, n=0) == 0
+    assert _fwd(lib, nseg=0) == 0
+
+
+def test_backward_argument_errors(lib):
+    def bwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, dtype=0, cu=FAKE,
+                 nseg=1, maxlen=8, pos=FAKE, theta=1e4, max_pos=16, n=8, h=2, d=64, scale=0.0, ws=FAKE,
+                 wsb=1 << 30)
+        a.update(kw)
+        return lib.mf_varlen_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                      a["dv"], a["dtype"], a["cu"], a["nseg"], a["maxlen"], a["pos"], a["theta"],
+                                      a["max_pos"], a["n"], a["h"], a["d"], a["scale"], a["ws"], a["wsb"], None)
+    assert bwd(lse=None) == -1
+    assert bwd(dq=None) == -1
+    assert bwd(d=32) == -2
+    assert bwd(wsb=1) == -3
+    assert bwd(dk=FAKE + 4) == -1
+
+
+def test_pack_and_rope_argument_errors(lib):
+    assert lib.mf_pack(FAKE, -1, 10, FAKE, None, FAKE, FAKE, None, None, 0, None, None) == -1
+    assert lib.mf_pack(FAKE, 2, -5, FAKE, None, FAKE, FAKE, None, None, 0, None, None) == -1
+    assert lib.mf_pack(FAKE, 2, 10, None, None, FAKE, FAKE, None, None, 0, None, None) == -1
+    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE + 4, FAKE, None, None, 0, None, None) == -1
+    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE, FAKE, FAKE, None, 16, FAKE, None) == -1  # image_rows missing
+    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == -1   # row_bytes 0
+    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 8, 1, 48, 1e4, 16, 0, FAKE, 1 << 20, None) == -2
+    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 8, 1, 64, 1e4, 16, 0, FAKE, 8, None) == -3
+    assert lib.mf_rope2d_apply(FAKE, 0, None, 8, 1, 64, 1e4, 16, 0, FAKE, 1 << 20, None) == -1
+    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 0, 1, 64, 1e4, 16, 0, FAKE, 1 << 20, None) == 0
+
+
+def test_workspace_sizes(lib):
+    n, h = 1000, 4
+    fwd_bf16 = lib.mf_varlen_attn_workspace_size(n, h, 128, 3, 640, 0, 0)
+    bwd_bf16 = lib.mf_varlen_attn_workspace_size(n, h, 128, 3, 640, 0, 1)
+    fwd_f32 = lib.mf_varlen_attn_workspace_size(n, h, 128, 3, 640, 1, 0)
+    table = 640 * 32 * 8
+    tensor = n * h * 128 * 2
+    assert fwd_bf16 >= table + tensor
+    assert bwd_bf16 >= table + 2 * tensor + n * h * 4
+    assert fwd_f32 >= fwd_bf16 + tensor
+    assert fwd_bf16 % 256 == 0 and bwd_bf16 % 256 == 0
+    assert lib.mf_varlen_attn_workspace_size(n, h, 96, 3, 640, 0, 0) == 0
+    assert lib.mf_rope2d_workspace_size(128, 640) == table
