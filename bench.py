@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed 2D-RoPE variable-length attention hot path.
+
+One step = one pass of the whole path over one synthetic batch:
+  mf_pack             budget cut + offsets (scan), per-token (row, col) and the
+                      gather of 3072-wide bf16 hidden rows into the packed buffer
+  mf_varlen_attn_fwd  2D RoPE + block-diagonal attention, O and LSE
+  mf_varlen_attn_bwd  dQ, dK, dV with the inverse rotation
+on the mixed native-resolution training pack (50 000-token budget, 24 heads x
+head_dim 128, bf16).  Inputs are resident in GPU memory before timing starts.
+
+Prints ONE JSON line.  value = (forward + backward algorithmic FLOPs) / step
+time, with forward = 4 sum(L_i^2) D H and backward = 10 sum(L_i^2) D H.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ROW_BYTES = 3072 * 2        # one packed hidden row (hidden 3072, bf16)
+
+# Algorithmic FLOPs per unit sum(L^2) * D * H, and algorithmic bytes per launch,
+# for each kernel the library launches.
+KERNEL_FLOP_FACTOR = {"attn_fwd": 4.0, "attn_bwd_dkdv": 8.0, "attn_bwd_dq": 2.0}
+KERNEL_SOURCE = {
+    "attn_fwd": "attn_fwd.hip", "attn_bwd_dkdv": "attn_bwd.hip", "attn_bwd_dq": "attn_bwd.hip",
+    "attn_bwd_delta": "attn_bwd.hip", "rope_q": "rope.hip", "rope_k": "rope.hip", "rope_table": "rope.hip",
+    "pack_scan": "pack.hip", "pack_fill": "pack.hip",
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixed50k", choices=["mixed50k", "cfg1024", "stress"],
+                    help="bench line workload (mixed50k is the metric's; others for exploration)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU timing")
+    ap.add_argument("--cpu-threads", type=int, default=16, help="BLAS threads for the oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (reference for HBM counters)")
+    return ap.parse_args()
+
+
+def source_digest(name: str) -> str:
+    path = os.path.join(ROOT, "packed_varlen_attention_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kernel_bytes(name: str, n: int, h: int, d: int, n_samples: int) -> float:
+    """Algorithmic HBM bytes of the memory-bound kernels (per launch)."""
+    t = n * h * d * 2
+    if name in ("rope_q", "rope_k"):
+        return 2.0 * t + 8.0 * n
+    if name == "attn_bwd_delta":
+        return 2.0 * t + 4.0 * n * h
+    if name == "pack_fill":
+        return 2.0 * n * ROW_BYTES + 8.0 * n
+    if name == "pack_scan":
+        return 12.0 * n_samples + 4.0 * (3 * n_samples + 2) + 16
+    return 0.0
+
+
+def load_traffic(kernel: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(kernel)
+    if not rec or rec.get("source_sha256_16") != source_digest(KERNEL_SOURCE[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, samples, q, k, v, do, threads: int, min_seconds: float = 10.0):
+    """Time the oracle (test infrastructure, never the product path) on a
+    bounded sample: forward + backward of whole heads over every packed
+    segment, adding heads until about ``min_seconds`` of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    import workloads
+
+    avail = len(os.sched_getaffinity(0))
+    use = max(1, min(threads, avail))
+    p = oracle.pack(samples, w.budget)
+    pos = oracle.positions(samples, p["n_packed"])
+    cu = p["cu_seqlens"]
+    sum_l2 = float(np.sum(np.diff(cu).astype(np.float64) ** 2))
+    secs = 0.0
+    heads = 0
+    with threadpool_limits(limits=use):
+        info = threadpool_info()
+        nthreads = max([i.get("num_threads", 1) for i in info] or [1])
+        while heads < w.n_heads and secs < min_seconds:
+            sl = slice(heads, heads + 1)
+            qs, ks, vs, ds = (workloads.bf16_bits_to_f32(x[:, sl]) for x in (q, k, v, do))
+            t0 = time.perf_counter()
+            oracle.attn_fwd(qs, ks, vs, cu, pos, w.theta)
+            oracle.attn_bwd(qs, ks, vs, ds, cu, pos, w.theta)
+            secs += time.perf_counter() - t0
+            heads += 1
+    flops = 14.0 * sum_l2 * w.head_dim * heads  # forward 4 + backward 10 per head
+    return {
+        "value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(nthreads), "kind": "oracle",
+        "sample": f"fp64 numpy oracle, forward+backward of {heads} of {w.n_heads} heads over all "
+                  f"{p['n_packed']} segments ({p['n_tokens']} tokens), {secs:.1f} s",
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the packed segments are independent; see DESIGN.md for how the path shards)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import packed_varlen_attention_amd as mf
+    import workloads
+
+    torch.cuda.set_device(0)
+    w = {"mixed50k": lambda: workloads.mixed50k(backward=True), "cfg1024": workloads.cfg1024,
+         "stress": workloads.stress}[args.workload]()
+    samples = list(w.samples)
+    H, D = w.n_heads, w.head_dim
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+
+    # Per-sample hidden rows (text, then row-major image grid) to gather.
+    t_samples = torch.tensor(np.asarray(samples, dtype=np.int32)).to(dev)
+    bufs, tptr, iptr = [], [], []
+    for (t, gh, gw) in samples:
+        tb = torch.randn((max(t, 1), ROW_BYTES // 2), generator=gen, device=dev, dtype=torch.bfloat16)
+        ib = torch.randn((max(gh * gw, 1), ROW_BYTES // 2), generator=gen, device=dev, dtype=torch.bfloat16)
+        bufs += [tb, ib]
+        tptr.append(tb.data_ptr())
+        iptr.append(ib.data_ptr())
+    t_tptr = torch.tensor(tptr, dtype=torch.int64, device=dev)
+    t_iptr = torch.tensor(iptr, dtype=torch.int64, device=dev)
+
+    packres = mf.pack(t_samples, w.budget, t_tptr, t_iptr, ROW_BYTES)
+    torch.cuda.synchronize()
+    n_packed, N, max_seqlen, max_pos = (int(x) for x in packres.counts.cpu().tolist())
+    cu_host = packres.cu_seqlens.cpu().numpy()[: n_packed + 1].astype(np.int64)
+    sum_l2 = float(np.sum(np.diff(cu_host).astype(np.float64) ** 2))
+
+    q, k, v = workloads.qkv(w.seed, N, H, D, "bf16")
+    do = workloads.dout(w.seed, N, H, D, "bf16")
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    tq, tk, tv, tdo = up(q), up(k), up(v), up(do)
+    o = torch.empty_like(tq)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv))
+    from packed_varlen_attention_amd.api import attn_workspace
+    ws_f = attn_workspace(tq, n_packed, max_pos, False)
+    ws_b = attn_workspace(tq, n_packed, max_pos, True)
+
+    def step(traces=None):
+        tp, tf, tb = traces if traces else (None, None, None)
+        mf.pack(t_samples, w.budget, t_tptr, t_iptr, ROW_BYTES, out=packres, trace=tp)
+        mf.attn_fwd(tq, tk, tv, packres.cu_seqlens, max_seqlen, packres.pos, w.theta, max_pos, out=o, lse=lse,
+                    workspace=ws_f, trace=tf, n_segments=n_packed)
+        mf.attn_bwd(tq, tk, tv, o, lse, tdo, packres.cu_seqlens, max_seqlen, packres.pos, w.theta, max_pos,
+                    workspace=ws_b, grads=grads, trace=tb, n_segments=n_packed)
+
+    for _ in range(args.warmup):
+        step()
+    traces = [(mf.KernelTrace(4), mf.KernelTrace(8), mf.KernelTrace(8)) for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(traces[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel mean duration over the timed steps (events on the launch stream)
+    kern = {}
+    call_ms = {"pack": 0.0, "fwd": 0.0, "bwd": 0.0}
+    for tr in traces:
+        for label, t in zip(("pack", "fwd", "bwd"), tr):
+            for name, ms in t.results():
+                key = name if label != "bwd" or name not in ("rope_table", "rope_k") else name + "@bwd"
+                kern[key] = kern.get(key, 0.0) + ms / args.steps
+                call_ms[label] += ms / args.steps
+
+    fwd_flops = 4.0 * sum_l2 * D * H
+    bwd_flops = 10.0 * sum_l2 * D * H
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+
+    dominant = max(kern, key=kern.get)
+    base = dominant.split("@")[0]
+    if base in KERNEL_FLOP_FACTOR:
+        algo = KERNEL_FLOP_FACTOR[base] * sum_l2 * D * H
+        achieved = algo / (kern[dominant] * 1e-3) / 1e12
+        roof = {"kernel": base, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_flops_per_launch": algo, "ms_per_launch": round(kern[dominant], 4)}
+    else:
+        algo = kernel_bytes(base, N, H, D, len(samples))
+        achieved = algo / (kern[dominant] * 1e-3) / 1e9
+        roof = {"kernel": base, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes_per_launch": algo, "ms_per_launch": round(kern[dominant], 4)}
+    roof["traffic"] = load_traffic(base)
+
+    per_kernel = {}
+    for name, ms in sorted(kern.items(), key=lambda kv: -kv[1]):
+        b = name.split("@")[0]
+        entry = {"ms": round(ms, 4)}
+        if b in KERNEL_FLOP_FACTOR:
+            entry["tflops"] = round(KERNEL_FLOP_FACTOR[b] * sum_l2 * D * H / (ms * 1e-3) / 1e12, 1)
+        elif kernel_bytes(b, N, H, D, len(samples)) > 0:
+            entry["gbs"] = round(kernel_bytes(b, N, H, D, len(samples)) / (ms * 1e-3) / 1e9, 1)
+        per_kernel[name] = entry
+
+    result = {
+        "metric": "packed 2D-RoPE varlen attention TFLOP/s (fwd, bwd) @50k tokens; % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 Q/K/V/dO (PCG64) on a seeded mixed native-resolution pack",
+        "config": {
+            "workload": {"mixed50k": "mixed native-resolution training pack, 50,000-token budget, seed 3: "
+                                     "pack + fwd(LSE) + bwd",
+                         "cfg1024": "1024^2 packed-CFG inference pack (4 prompts x cond/uncond): pack + fwd + bwd",
+                         "stress": "long/ragged stress pack (2048^2 + two 4:1 panoramas + 64 thumbnails): "
+                                   "pack + fwd + bwd"}[args.workload],
+            "n_tokens": N, "segments": n_packed, "heads": H, "head_dim": D, "max_seqlen": max_seqlen,
+            "sum_L2": sum_l2, "gather_row_bytes": ROW_BYTES,
+        },
+        "fwd_tflops": round(fwd_flops / (call_ms["fwd"] * 1e-3) / 1e12, 2),
+        "fwd_frac_peak": round(fwd_flops / (call_ms["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_tflops": round(bwd_flops / (call_ms["bwd"] * 1e-3) / 1e12, 2),
+        "bwd_frac_peak": round(bwd_flops / (call_ms["bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "call_ms": {k2: round(v2, 4) for k2, v2 in call_ms.items()},
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        result["copy_1GiB_gbs"] = round(2 * (1 << 30) * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
+    if not args.no_cpu_baseline and args.workload == "mixed50k":
+        result["cpu_baseline"] = cpu_baseline(w, samples, q, k, v, do, args.cpu_threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

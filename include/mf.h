@@ -28,6 +28,8 @@
  *   - Every call validates its host arguments first; on an error it returns a
  *     negative mf_status and launches nothing.  A launch failure reported by
  *     the HIP runtime returns MF_ERR_HIP.
+ *   - The last argument of every compute call is an optional mf_trace*
+ *     (NULL for none), see below.
  *   - Tensors q, k, v, o, dout, dq, dk, dv have layout [n_tokens][n_heads]
  *     [head_dim], contiguous, 16-byte aligned.  q and k hold UN-rotated
  *     values; the library applies the rotation.  lse is [n_heads][n_tokens]
@@ -78,6 +80,23 @@ typedef struct mf_sample {
   int32_t grid_w;
 } mf_sample;
 
+/*
+ * Optional per-kernel timing, owned by the caller.  When a call receives a
+ * non-NULL trace, it records start[i] before and stop[i] after its i-th
+ * kernel launch (i < capacity) on the call's stream and names the kernel in
+ * names[i]; count receives the number of kernels the call launched.  The
+ * events are hipEvent_t handles the caller created (passed as void*).  A
+ * NULL trace records nothing.  Tracing never changes results.
+ */
+#define MF_TRACE_MAX 16
+typedef struct mf_trace {
+  int32_t capacity;               /* pairs available in start/stop, <= MF_TRACE_MAX */
+  int32_t count;                  /* out: kernels launched by the call */
+  void* start[MF_TRACE_MAX];      /* hipEvent_t */
+  void* stop[MF_TRACE_MAX];       /* hipEvent_t */
+  const char* names[MF_TRACE_MAX];  /* out: static kernel names */
+} mf_trace;
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* mf_status_string(mf_status status);
 
@@ -122,7 +141,7 @@ int32_t mf_abi_version(void);
 mf_status mf_pack(const mf_sample* samples, int32_t n_samples, int32_t token_budget,
                   int32_t* cu_seqlens, int32_t* cu_pieces, int32_t* pos, int32_t* counts,
                   const void* const* text_rows, const void* const* image_rows,
-                  int64_t row_bytes, void* packed, void* stream);
+                  int64_t row_bytes, void* packed, void* stream, mf_trace* trace);
 
 /* Bytes of workspace mf_rope2d_apply needs: the cos/sin table. */
 size_t mf_rope2d_workspace_size(int32_t head_dim, int32_t max_pos);
@@ -144,7 +163,7 @@ size_t mf_rope2d_workspace_size(int32_t head_dim, int32_t max_pos);
 mf_status mf_rope2d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens,
                           int32_t n_heads, int32_t head_dim, double theta, int32_t max_pos,
                           int32_t inverse, void* workspace, size_t workspace_bytes,
-                          void* stream);
+                          void* stream, mf_trace* trace);
 
 /* Bytes of workspace the attention calls need (backward != 0: backward). */
 size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim,
@@ -176,7 +195,7 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
                              int32_t max_seqlen, const int32_t* pos, double theta,
                              int32_t max_pos, int32_t n_tokens, int32_t n_heads,
                              int32_t head_dim, float softmax_scale, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             size_t workspace_bytes, void* stream, mf_trace* trace);
 
 /*
  * mf_varlen_attn_bwd -- gradients of the attention above with respect to
@@ -198,7 +217,7 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
                              int32_t max_seqlen, const int32_t* pos, double theta,
                              int32_t max_pos, int32_t n_tokens, int32_t n_heads,
                              int32_t head_dim, float softmax_scale, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             size_t workspace_bytes, void* stream, mf_trace* trace);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,7 @@ helpers (PyTorch supplies device memory and the HIP stream).  Importing the
 package loads the library and fails loudly if it has not been built.
 """
 from ._binding import (  # noqa: F401
-    EXPORTED, LIB_PATH, MF_BF16, MF_F32, MF_ERR_HIP, MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED,
+    EXPORTED, LIB_PATH, MF_TRACE_MAX, KernelTrace, Trace, MF_BF16, MF_F32, MF_ERR_HIP, MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED,
     MF_ERR_WORKSPACE, MF_OK, MFError, abi_version, dtype_code, load_library, mf_pack,
     mf_rope2d_apply, mf_rope2d_workspace_size, mf_varlen_attn_bwd, mf_varlen_attn_fwd,
     mf_varlen_attn_workspace_size, status_string,

@@ -32,6 +32,47 @@ EXPORTED = (
 )
 
 
+MF_TRACE_MAX = 16
+
+
+class Trace(ctypes.Structure):
+    """mf_trace: caller-owned HIP events recorded around each kernel launch."""
+    _fields_ = [("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("start", ctypes.c_void_p * MF_TRACE_MAX), ("stop", ctypes.c_void_p * MF_TRACE_MAX),
+                ("names", ctypes.c_char_p * MF_TRACE_MAX)]
+
+
+class KernelTrace:
+    """A Trace backed by torch timing events on the current device."""
+
+    def __init__(self, capacity: int = MF_TRACE_MAX):
+        self.capacity = int(capacity)
+        self.starts = [torch.cuda.Event(enable_timing=True) for _ in range(self.capacity)]
+        self.stops = [torch.cuda.Event(enable_timing=True) for _ in range(self.capacity)]
+        for e in self.starts + self.stops:  # creates the underlying hipEvent_t
+            e.record()
+        self.struct = Trace()
+        self.struct.capacity = self.capacity
+        for i in range(self.capacity):
+            self.struct.start[i] = self.starts[i].cuda_event
+            self.struct.stop[i] = self.stops[i].cuda_event
+
+    def results(self):
+        """[(kernel name, milliseconds)] of the last traced call; synchronise first."""
+        out = []
+        for i in range(min(self.struct.count, self.capacity)):
+            out.append((self.struct.names[i].decode(), self.starts[i].elapsed_time(self.stops[i])))
+        return out
+
+
+def _trace(t) -> Optional[object]:
+    if t is None:
+        return None
+    if isinstance(t, KernelTrace):
+        return ctypes.byref(t.struct)
+    return ctypes.byref(t)
+
+
 class MFError(RuntimeError):
     def __init__(self, status: int, call: str):
         self.status = status
@@ -63,19 +104,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mf_abi_version.restype = _i32
     lib.mf_abi_version.argtypes = []
     lib.mf_pack.restype = _i32
-    lib.mf_pack.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp]
+    lib.mf_pack.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]
     lib.mf_rope2d_workspace_size.restype = _sz
     lib.mf_rope2d_workspace_size.argtypes = [_i32, _i32]
     lib.mf_rope2d_apply.restype = _i32
-    lib.mf_rope2d_apply.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, _dbl, _i32, _i32, _vp, _sz, _vp]
+    lib.mf_rope2d_apply.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, _dbl, _i32, _i32, _vp, _sz, _vp, _vp]
     lib.mf_varlen_attn_workspace_size.restype = _sz
     lib.mf_varlen_attn_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.mf_varlen_attn_fwd.restype = _i32
     lib.mf_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _dbl, _i32,
-                                       _i32, _i32, _i32, _f32, _vp, _sz, _vp]
+                                       _i32, _i32, _i32, _f32, _vp, _sz, _vp, _vp]
     lib.mf_varlen_attn_bwd.restype = _i32
     lib.mf_varlen_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
-                                       _vp, _dbl, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]
+                                       _vp, _dbl, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp, _vp]
     _lib = lib
     return lib
 
@@ -132,14 +173,14 @@ def dtype_code(t: torch.Tensor) -> int:
 def mf_pack(samples: torch.Tensor, token_budget: int, cu_seqlens: torch.Tensor,
             cu_pieces: Optional[torch.Tensor], pos: torch.Tensor, counts: torch.Tensor,
             text_rows: Optional[torch.Tensor] = None, image_rows: Optional[torch.Tensor] = None,
-            row_bytes: int = 0, packed: Optional[torch.Tensor] = None, stream=None) -> None:
+            row_bytes: int = 0, packed: Optional[torch.Tensor] = None, stream=None, trace=None) -> None:
     """samples: int32 [S, 3] on the GPU; text_rows/image_rows: int64 [S] device
     tensors holding row-buffer addresses."""
     if samples.dtype != torch.int32 or samples.dim() != 2 or samples.shape[1] != 3:
         raise ValueError("samples must be an int32 [S, 3] tensor")
     st = lib().mf_pack(_ptr(samples), int(samples.shape[0]), int(token_budget), _ptr(cu_seqlens),
                        _ptr(cu_pieces), _ptr(pos), _ptr(counts), _ptr(text_rows), _ptr(image_rows),
-                       int(row_bytes), _ptr(packed), _stream(stream))
+                       int(row_bytes), _ptr(packed), _stream(stream), _trace(trace))
     _check(st, "mf_pack")
 
 
@@ -148,11 +189,12 @@ def mf_rope2d_workspace_size(head_dim: int, max_pos: int) -> int:
 
 
 def mf_rope2d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: int,
-                    inverse: bool, workspace: torch.Tensor, stream=None) -> None:
+                    inverse: bool, workspace: torch.Tensor, stream=None, trace=None) -> None:
     n, h, d = x.shape
     st = lib().mf_rope2d_apply(_ptr(x), dtype_code(x), _ptr(pos), int(n), int(h), int(d), float(theta),
                                int(max_pos), int(bool(inverse)), _ptr(workspace),
-                               int(workspace.numel() * workspace.element_size()), _stream(stream))
+                               int(workspace.numel() * workspace.element_size()), _stream(stream),
+                               _trace(trace))
     _check(st, "mf_rope2d_apply")
 
 
@@ -164,23 +206,25 @@ def mf_varlen_attn_workspace_size(n_tokens: int, n_heads: int, head_dim: int, n_
 
 
 def mf_varlen_attn_fwd(q, k, v, o, lse, cu_seqlens, n_segments: int, max_seqlen: int, pos,
-                       theta: float, max_pos: int, softmax_scale: float, workspace, stream=None) -> None:
+                       theta: float, max_pos: int, softmax_scale: float, workspace, stream=None,
+                       trace=None) -> None:
     n, h, d = q.shape
     st = lib().mf_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dtype_code(q),
                                   _ptr(cu_seqlens), int(n_segments), int(max_seqlen), _ptr(pos),
                                   float(theta), int(max_pos), int(n), int(h), int(d), float(softmax_scale),
                                   _ptr(workspace), int(workspace.numel() * workspace.element_size()),
-                                  _stream(stream))
+                                  _stream(stream), _trace(trace))
     _check(st, "mf_varlen_attn_fwd")
 
 
 def mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, n_segments: int, max_seqlen: int,
                        pos, theta: float, max_pos: int, softmax_scale: float, workspace,
-                       stream=None) -> None:
+                       stream=None, trace=None) -> None:
     n, h, d = q.shape
     st = lib().mf_varlen_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                   _ptr(dk), _ptr(dv), dtype_code(q), _ptr(cu_seqlens), int(n_segments),
                                   int(max_seqlen), _ptr(pos), float(theta), int(max_pos), int(n), int(h),
                                   int(d), float(softmax_scale), _ptr(workspace),
-                                  int(workspace.numel() * workspace.element_size()), _stream(stream))
+                                  int(workspace.numel() * workspace.element_size()), _stream(stream),
+                                  _trace(trace))
     _check(st, "mf_varlen_attn_bwd")

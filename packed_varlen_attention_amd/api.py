@@ -23,26 +23,29 @@ class PackResult:
 
 
 def pack(samples: torch.Tensor, token_budget: int, text_rows: Optional[torch.Tensor] = None,
-         image_rows: Optional[torch.Tensor] = None, row_bytes: int = 0, stream=None) -> PackResult:
-    dev = samples.device
-    s = int(samples.shape[0])
-    cu = torch.empty(s + 1, dtype=torch.int32, device=dev)
-    pieces = torch.empty(2 * s + 1, dtype=torch.int32, device=dev)
-    pos = torch.empty((max(int(token_budget), 1), 2), dtype=torch.int32, device=dev)
-    counts = torch.empty(4, dtype=torch.int32, device=dev)
-    packed = None
-    if text_rows is not None:
-        packed = torch.empty((max(int(token_budget), 1), int(row_bytes)), dtype=torch.uint8, device=dev)
-    B.mf_pack(samples, token_budget, cu, pieces, pos, counts, text_rows, image_rows, row_bytes, packed, stream)
-    return PackResult(cu, pieces, pos, counts, packed)
+         image_rows: Optional[torch.Tensor] = None, row_bytes: int = 0, stream=None, trace=None,
+         out: Optional[PackResult] = None) -> PackResult:
+    if out is None:
+        dev = samples.device
+        s = int(samples.shape[0])
+        packed = None
+        if text_rows is not None:
+            packed = torch.empty((max(int(token_budget), 1), int(row_bytes)), dtype=torch.uint8, device=dev)
+        out = PackResult(torch.empty(s + 1, dtype=torch.int32, device=dev),
+                         torch.empty(2 * s + 1, dtype=torch.int32, device=dev),
+                         torch.empty((max(int(token_budget), 1), 2), dtype=torch.int32, device=dev),
+                         torch.empty(4, dtype=torch.int32, device=dev), packed)
+    B.mf_pack(samples, token_budget, out.cu_seqlens, out.cu_pieces, out.pos, out.counts, text_rows, image_rows,
+              row_bytes, out.packed, stream, trace)
+    return out
 
 
 def rope2d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: int, inverse: bool = False,
-                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                 workspace: Optional[torch.Tensor] = None, stream=None, trace=None) -> torch.Tensor:
     if workspace is None:
         workspace = torch.empty(max(B.mf_rope2d_workspace_size(x.shape[2], max_pos), 1), dtype=torch.uint8,
                                 device=x.device)
-    B.mf_rope2d_apply(x, pos, theta, max_pos, inverse, workspace, stream)
+    B.mf_rope2d_apply(x, pos, theta, max_pos, inverse, workspace, stream, trace)
     return x
 
 
@@ -56,16 +59,16 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
              pos: Optional[torch.Tensor] = None, theta: float = 10000.0, max_pos: int = 0,
              softmax_scale: float = 0.0, with_lse: bool = True, workspace: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+             stream=None, trace=None, n_segments: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     n, h, _ = q.shape
-    nseg = int(cu_seqlens.numel()) - 1
+    nseg = int(cu_seqlens.numel()) - 1 if n_segments is None else int(n_segments)
     o = torch.empty_like(q) if out is None else out
     if with_lse and lse is None:
         lse = torch.empty((h, n), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, False)
     B.mf_varlen_attn_fwd(q, k, v, o, lse if with_lse else None, cu_seqlens, nseg, max_seqlen, pos, theta,
-                         max_pos, softmax_scale, workspace, stream)
+                         max_pos, softmax_scale, workspace, stream, trace)
     return o, (lse if with_lse else None)
 
 
@@ -73,13 +76,14 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, pos: Optional[torch.Tensor] = None,
              theta: float = 10000.0, max_pos: int = 0, softmax_scale: float = 0.0,
              workspace: Optional[torch.Tensor] = None, grads=None,
-             stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    nseg = int(cu_seqlens.numel()) - 1
+             stream=None, trace=None, n_segments: Optional[int] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    nseg = int(cu_seqlens.numel()) - 1 if n_segments is None else int(n_segments)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
     if workspace is None:
         workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, True)
     B.mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nseg, max_seqlen, pos, theta, max_pos,
-                         softmax_scale, workspace, stream)
+                         softmax_scale, workspace, stream, trace)
     return dq, dk, dv

@@ -18,7 +18,41 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 mf_status from_hip(hipError_t e) { return e == hipSuccess ? MF_OK : MF_ERR_HIP; }
 
-size_t elem_bytes(int32_t dtype) { return dtype == MF_F32 ? 4 : 2; }
+// Records the caller's events around each kernel launch of one call.
+class Tracer {
+ public:
+  Tracer(mf_trace* t, hipStream_t s) : t_(t), s_(s) {
+    if (t_ != nullptr) t_->count = 0;
+  }
+  // Runs one launcher between the i-th (start, stop) event pair.
+  template <typename F>
+  hipError_t run(const char* name, F&& launch) {
+    const bool rec = t_ != nullptr && i_ < t_->capacity && i_ < MF_TRACE_MAX;
+    if (rec) {
+      t_->names[i_] = name;
+      if (hipEventRecord(static_cast<hipEvent_t>(t_->start[i_]), s_) != hipSuccess) return hipErrorInvalidValue;
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    if (rec && hipEventRecord(static_cast<hipEvent_t>(t_->stop[i_]), s_) != hipSuccess) return hipErrorInvalidValue;
+    ++i_;
+    if (t_ != nullptr) t_->count = i_;
+    return hipSuccess;
+  }
+
+ private:
+  mf_trace* t_;
+  hipStream_t s_;
+  int i_ = 0;
+};
+
+bool trace_ok(const mf_trace* t) {
+  if (t == nullptr) return true;
+  if (t->capacity < 0 || t->capacity > MF_TRACE_MAX) return false;
+  for (int i = 0; i < t->capacity; ++i)
+    if (t->start[i] == nullptr || t->stop[i] == nullptr) return false;
+  return true;
+}
 
 // Workspace of the attention calls, in order; each part 256-byte aligned.
 struct AttnWorkspace {
@@ -95,7 +129,7 @@ int32_t mf_abi_version(void) { return MF_ABI_VERSION; }
 
 mf_status mf_pack(const mf_sample* samples, int32_t n_samples, int32_t token_budget, int32_t* cu_seqlens,
                   int32_t* cu_pieces, int32_t* pos, int32_t* counts, const void* const* text_rows,
-                  const void* const* image_rows, int64_t row_bytes, void* packed, void* stream) {
+                  const void* const* image_rows, int64_t row_bytes, void* packed, void* stream, mf_trace* trace) {
   if (n_samples < 0 || token_budget < 0) return MF_ERR_INVALID_ARG;
   if (n_samples > (0x7fffffff - 1) / 2) return MF_ERR_INVALID_ARG;
   if (cu_seqlens == nullptr || counts == nullptr) return MF_ERR_INVALID_ARG;
@@ -107,8 +141,19 @@ mf_status mf_pack(const mf_sample* samples, int32_t n_samples, int32_t token_bud
   } else if (text_rows != nullptr || image_rows != nullptr) {
     return MF_ERR_INVALID_ARG;
   }
-  return from_hip(mf::launch_pack(samples, n_samples, token_budget, cu_seqlens, cu_pieces, pos, counts, text_rows,
-                                  image_rows, packed ? row_bytes : 0, packed, static_cast<hipStream_t>(stream)));
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Tracer tr(trace, s);
+  hipError_t e = tr.run("pack_scan", [&] {
+    return mf::launch_pack_scan(samples, n_samples, token_budget, cu_seqlens, cu_pieces, counts, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  if (token_budget == 0 || n_samples == 0) return MF_OK;
+  e = tr.run("pack_fill", [&] {
+    return mf::launch_pack_fill(samples, token_budget, cu_seqlens, counts, pos, text_rows, image_rows,
+                                packed ? row_bytes : 0, packed, s);
+  });
+  return from_hip(e);
 }
 
 size_t mf_rope2d_workspace_size(int32_t head_dim, int32_t max_pos) {
@@ -118,21 +163,26 @@ size_t mf_rope2d_workspace_size(int32_t head_dim, int32_t max_pos) {
 
 mf_status mf_rope2d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens, int32_t n_heads,
                           int32_t head_dim, double theta, int32_t max_pos, int32_t inverse, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, mf_trace* trace) {
   if (dtype != MF_BF16 && dtype != MF_F32) return MF_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return MF_ERR_UNSUPPORTED;
   if (n_tokens < 0 || n_heads < 1 || max_pos < 1 || !(theta > 0.0) || isinf(theta)) return MF_ERR_INVALID_ARG;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
   if (n_tokens == 0) return MF_OK;
   if (x == nullptr || pos == nullptr || workspace == nullptr) return MF_ERR_INVALID_ARG;
   if (!aligned16(x) || (reinterpret_cast<uintptr_t>(pos) & 7u) != 0 || !aligned16(workspace))
     return MF_ERR_INVALID_ARG;
   if (workspace_bytes < mf_rope2d_workspace_size(head_dim, max_pos)) return MF_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Tracer tr(trace, s);
   float2* tab = static_cast<float2*>(workspace);
-  hipError_t e = mf::launch_rope_table(tab, max_pos, head_dim, theta, s);
+  hipError_t e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, theta, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
-  return from_hip(mf::launch_rope_apply(x, dtype, x, dtype, pos, tab, max_pos, n_tokens, n_heads, head_dim, true,
-                                        inverse != 0, s));
+  e = tr.run("rope_apply", [&] {
+    return mf::launch_rope_apply(x, dtype, x, dtype, pos, tab, max_pos, n_tokens, n_heads, head_dim, true,
+                                 inverse != 0, s);
+  });
+  return from_hip(e);
 }
 
 size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
@@ -145,10 +195,12 @@ size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t 
 mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
                              const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
                              double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
+                             mf_trace* trace) {
   mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
                                    n_heads, head_dim, softmax_scale);
   if (st != MF_OK) return st;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
   if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return MF_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MF_ERR_INVALID_ARG;
@@ -158,27 +210,33 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Tracer tr(trace, s);
   char* ws = static_cast<char*>(workspace);
   float2* tab = reinterpret_cast<float2*>(ws + w.tab_off);
   const void* kr = k;
   const void* vb = v;
   hipError_t e = hipSuccess;
-  if (pos != nullptr) e = mf::launch_rope_table(tab, max_pos, head_dim, theta, s);
-  if (e != hipSuccess) return MF_ERR_HIP;
+  if (pos != nullptr) {
+    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, theta, s); });
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
   // K rotated once into bf16 (also converts float32 input); Q is rotated
   // inside the attention kernel when it is loaded.
   if (pos != nullptr || dtype == MF_F32) {
     kr = ws + w.kr_off;
-    e = mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads, head_dim,
-                              pos != nullptr, false, s);
+    e = tr.run("rope_k", [&] {
+      return mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads,
+                                   head_dim, pos != nullptr, false, s);
+    });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
   if (dtype == MF_F32) {
-    void* vconv = ws + w.vb_off;
-    e = mf::launch_rope_apply(v, dtype, vconv, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads, head_dim, false,
-                              false, s);
+    vb = ws + w.vb_off;
+    e = tr.run("convert_v", [&] {
+      return mf::launch_rope_apply(v, dtype, ws + w.vb_off, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads,
+                                   head_dim, false, false, s);
+    });
     if (e != hipSuccess) return MF_ERR_HIP;
-    vb = vconv;
   }
   mf::AttnArgs a;
   a.cu_seqlens = cu_seqlens;
@@ -192,17 +250,20 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   a.tab = tab;
   a.max_pos = max_pos;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
-  return from_hip(mf::launch_attn_fwd(a, q, kr, vb, o, lse, s));
+  e = tr.run("attn_fwd", [&] { return mf::launch_attn_fwd(a, q, kr, vb, o, lse, s); });
+  return from_hip(e);
 }
 
 mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dout, void* dq, void* dk, void* dv, int32_t dtype, const int32_t* cu_seqlens,
                              int32_t n_segments, int32_t max_seqlen, const int32_t* pos, double theta,
                              int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
+                             mf_trace* trace) {
   mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
                                    n_heads, head_dim, softmax_scale);
   if (st != MF_OK) return st;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
   if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
@@ -215,6 +276,7 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Tracer tr(trace, s);
   char* ws = static_cast<char*>(workspace);
   float2* tab = reinterpret_cast<float2*>(ws + w.tab_off);
   const void* kr = k;
@@ -223,29 +285,37 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   const void* vb = v;
   const void* dob = dout;
   hipError_t e = hipSuccess;
-  if (pos != nullptr) e = mf::launch_rope_table(tab, max_pos, head_dim, theta, s);
-  if (e != hipSuccess) return MF_ERR_HIP;
+  if (pos != nullptr) {
+    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, theta, s); });
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
   if (pos != nullptr || dtype == MF_F32) {
     qr = ws + w.qr_off;
     kr = ws + w.kr_off;
-    e = mf::launch_rope_apply(q, dtype, ws + w.qr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads, head_dim,
-                              pos != nullptr, false, s);
+    e = tr.run("rope_q", [&] {
+      return mf::launch_rope_apply(q, dtype, ws + w.qr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads,
+                                   head_dim, pos != nullptr, false, s);
+    });
     if (e != hipSuccess) return MF_ERR_HIP;
-    e = mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads, head_dim,
-                              pos != nullptr, false, s);
+    e = tr.run("rope_k", [&] {
+      return mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads,
+                                   head_dim, pos != nullptr, false, s);
+    });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
   if (dtype == MF_F32) {
-    void* vconv = ws + w.vb_off;
-    void* dconv = ws + w.dob_off;
-    e = mf::launch_rope_apply(v, dtype, vconv, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads, head_dim, false,
-                              false, s);
+    vb = ws + w.vb_off;
+    dob = ws + w.dob_off;
+    e = tr.run("convert_v", [&] {
+      return mf::launch_rope_apply(v, dtype, ws + w.vb_off, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads,
+                                   head_dim, false, false, s);
+    });
     if (e != hipSuccess) return MF_ERR_HIP;
-    e = mf::launch_rope_apply(dout, dtype, dconv, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads, head_dim, false,
-                              false, s);
+    e = tr.run("convert_do", [&] {
+      return mf::launch_rope_apply(dout, dtype, ws + w.dob_off, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads,
+                                   head_dim, false, false, s);
+    });
     if (e != hipSuccess) return MF_ERR_HIP;
-    vb = vconv;
-    dob = dconv;
   }
   mf::AttnArgs a;
   a.cu_seqlens = cu_seqlens;
@@ -259,11 +329,13 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   a.tab = tab;
   a.max_pos = max_pos;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
-  e = mf::launch_attn_bwd_delta(a, o, dout, delta, s);
+  e = tr.run("attn_bwd_delta", [&] { return mf::launch_attn_bwd_delta(a, o, dout, delta, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
-  e = mf::launch_attn_bwd_dkdv(a, qr, kr, vb, dob, lse, delta, dk, dv, s);
+  e = tr.run("attn_bwd_dkdv",
+             [&] { return mf::launch_attn_bwd_dkdv(a, qr, kr, vb, dob, lse, delta, dk, dv, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
-  return from_hip(mf::launch_attn_bwd_dq(a, qr, kr, vb, dob, lse, delta, dq, s));
+  e = tr.run("attn_bwd_dq", [&] { return mf::launch_attn_bwd_dq(a, qr, kr, vb, dob, lse, delta, dq, s); });
+  return from_hip(e);
 }
 
 }  // extern "C"

@@ -10,9 +10,12 @@ namespace mf {
 constexpr int kDtypeBf16 = 0;
 constexpr int kDtypeF32 = 1;
 
-hipError_t launch_pack(const void* samples, int n, int budget, int* cu_seqlens, int* cu_pieces, int* pos,
-                       int* counts, const void* const* text_rows, const void* const* image_rows,
-                       long long row_bytes, void* packed, hipStream_t stream);
+hipError_t launch_pack_scan(const void* samples, int n, int budget, int* cu_seqlens, int* cu_pieces,
+                            int* counts, hipStream_t stream);
+
+hipError_t launch_pack_fill(const void* samples, int budget, const int* cu_seqlens, const int* counts, int* pos,
+                            const void* const* text_rows, const void* const* image_rows, long long row_bytes,
+                            void* packed, hipStream_t stream);
 
 hipError_t launch_rope_table(float2* tab, int max_pos, int head_dim, double theta, hipStream_t stream);
 

@@ -206,15 +206,16 @@ __global__ __launch_bounds__(256) void pack_fill_kernel(
 
 }  // namespace
 
-hipError_t launch_pack(const void* samples, int n, int budget, int* cu_seqlens, int* cu_pieces,
-                       int* pos, int* counts, const void* const* text_rows,
-                       const void* const* image_rows, long long row_bytes, void* packed,
-                       hipStream_t stream) {
+hipError_t launch_pack_scan(const void* samples, int n, int budget, int* cu_seqlens, int* cu_pieces,
+                            int* counts, hipStream_t stream) {
   hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                      static_cast<const Sample*>(samples), n, budget, cu_seqlens, cu_pieces, counts);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (budget == 0 || n == 0) return hipSuccess;
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fill(const void* samples, int budget, const int* cu_seqlens, const int* counts, int* pos,
+                            const void* const* text_rows, const void* const* image_rows, long long row_bytes,
+                            void* packed, hipStream_t stream) {
   // Enough waves to stream the rows at full bandwidth; each loops over tokens.
   long long waves = budget;
   const long long max_waves = 256LL * 8 * 4;  // 8 resident blocks of 4 waves on 256 CUs

@@ -58,7 +58,7 @@ def _fwd(lib, **kw):
     return lib.mf_varlen_attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dtype"],
                                   args["cu"], args["nseg"], args["maxlen"], args["pos"], args["theta"],
                                   args["max_pos"], args["n"], args["h"], args["d"], args["scale"], args["ws"],
-                                  args["wsb"], args["stream"])
+                                  args["wsb"], args["stream"], args.get("trace"))
 
 
 def test_forward_argument_errors(lib):
@@ -77,6 +77,13 @@ def test_forward_argument_errors(lib):
     # nothing to do is OK and launches nothing
     assert _fwd(lib, n=0) == 0
     assert _fwd(lib, nseg=0) == 0
+    # a trace with null events or a bad capacity is rejected before launching
+    import packed_varlen_attention_amd as m
+    t = m.Trace()
+    t.capacity = 2
+    assert _fwd(lib, trace=ctypes.byref(t)) == -1
+    t.capacity = 99
+    assert _fwd(lib, trace=ctypes.byref(t)) == -1
 
 
 def test_backward_argument_errors(lib):
@@ -87,7 +94,7 @@ def test_backward_argument_errors(lib):
         a.update(kw)
         return lib.mf_varlen_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
                                       a["dv"], a["dtype"], a["cu"], a["nseg"], a["maxlen"], a["pos"], a["theta"],
-                                      a["max_pos"], a["n"], a["h"], a["d"], a["scale"], a["ws"], a["wsb"], None)
+                                      a["max_pos"], a["n"], a["h"], a["d"], a["scale"], a["ws"], a["wsb"], None, None)
     assert bwd(lse=None) == -1
     assert bwd(dq=None) == -1
     assert bwd(d=32) == -2
@@ -96,16 +103,16 @@ def test_backward_argument_errors(lib):
 
 
 def test_pack_and_rope_argument_errors(lib):
-    assert lib.mf_pack(FAKE, -1, 10, FAKE, None, FAKE, FAKE, None, None, 0, None, None) == -1
-    assert lib.mf_pack(FAKE, 2, -5, FAKE, None, FAKE, FAKE, None, None, 0, None, None) == -1
-    assert lib.mf_pack(FAKE, 2, 10, None, None, FAKE, FAKE, None, None, 0, None, None) == -1
-    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE + 4, FAKE, None, None, 0, None, None) == -1
-    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE, FAKE, FAKE, None, 16, FAKE, None) == -1  # image_rows missing
-    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == -1   # row_bytes 0
-    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 8, 1, 48, 1e4, 16, 0, FAKE, 1 << 20, None) == -2
-    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 8, 1, 64, 1e4, 16, 0, FAKE, 8, None) == -3
-    assert lib.mf_rope2d_apply(FAKE, 0, None, 8, 1, 64, 1e4, 16, 0, FAKE, 1 << 20, None) == -1
-    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 0, 1, 64, 1e4, 16, 0, FAKE, 1 << 20, None) == 0
+    assert lib.mf_pack(FAKE, -1, 10, FAKE, None, FAKE, FAKE, None, None, 0, None, None, None) == -1
+    assert lib.mf_pack(FAKE, 2, -5, FAKE, None, FAKE, FAKE, None, None, 0, None, None, None) == -1
+    assert lib.mf_pack(FAKE, 2, 10, None, None, FAKE, FAKE, None, None, 0, None, None, None) == -1
+    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE + 4, FAKE, None, None, 0, None, None, None) == -1
+    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE, FAKE, FAKE, None, 16, FAKE, None, None) == -1  # image_rows missing
+    assert lib.mf_pack(FAKE, 2, 10, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None) == -1   # row_bytes 0
+    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 8, 1, 48, 1e4, 16, 0, FAKE, 1 << 20, None, None) == -2
+    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 8, 1, 64, 1e4, 16, 0, FAKE, 8, None, None) == -3
+    assert lib.mf_rope2d_apply(FAKE, 0, None, 8, 1, 64, 1e4, 16, 0, FAKE, 1 << 20, None, None) == -1
+    assert lib.mf_rope2d_apply(FAKE, 0, FAKE, 0, 1, 64, 1e4, 16, 0, FAKE, 1 << 20, None, None) == 0
 
 
 def test_workspace_sizes(lib):
