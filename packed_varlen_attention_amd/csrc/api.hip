@@ -56,13 +56,14 @@ bool trace_ok(const mf_trace* t) {
 
 // Workspace of the attention calls, in order; each part 256-byte aligned.
 struct AttnWorkspace {
-  size_t tab = 0, kr = 0, qr = 0, vb = 0, dob = 0, delta = 0, total = 0;
-  size_t tab_off = 0, kr_off = 0, qr_off = 0, vb_off = 0, dob_off = 0, delta_off = 0;
+  size_t tab = 0, kr = 0, qr = 0, vb = 0, dob = 0, delta = 0, sched = 0, total = 0;
+  size_t tab_off = 0, kr_off = 0, qr_off = 0, vb_off = 0, dob_off = 0, delta_off = 0, sched_off = 0;
 };
 
-AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t max_pos, int32_t dtype,
-                             bool backward) {
+AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
+                             int32_t max_pos, int32_t dtype, bool backward) {
   AttnWorkspace w;
+  w.sched = (2 * static_cast<size_t>(n_segments > 0 ? n_segments : 0) + 1) * sizeof(int32_t);
   const size_t tensor_bf16 = static_cast<size_t>(n_tokens) * n_heads * head_dim * 2;
   w.tab = static_cast<size_t>(max_pos > 0 ? max_pos : 0) * (head_dim / 4) * sizeof(float2);
   w.kr = tensor_bf16;  // rotated (or converted) K
@@ -83,6 +84,8 @@ AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim
   off += align_up(w.dob);
   w.delta_off = off;
   off += align_up(w.delta);
+  w.sched_off = off;
+  off += align_up(w.sched);
   w.total = off;
   return w;
 }
@@ -187,9 +190,9 @@ mf_status mf_rope2d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_
 
 size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
                                      int32_t max_pos, int32_t dtype, int32_t backward) {
-  (void)n_segments;
   if (n_tokens < 0 || n_heads < 1 || (head_dim != 64 && head_dim != 128)) return 0;
-  return attn_workspace(n_tokens, n_heads, head_dim, max_pos, dtype, backward != 0).total;
+  if (n_segments < 0) return 0;
+  return attn_workspace(n_tokens, n_heads, head_dim, n_segments, max_pos, dtype, backward != 0).total;
 }
 
 mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
@@ -205,7 +208,7 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return MF_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MF_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return MF_ERR_INVALID_ARG;
-  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, pos ? max_pos : 0, dtype, false);
+  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, n_segments, pos ? max_pos : 0, dtype, false);
   if (workspace_bytes < w.total) return MF_ERR_WORKSPACE;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
 
@@ -250,6 +253,13 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   a.tab = tab;
   a.max_pos = max_pos;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  a.order = reinterpret_cast<int*>(ws + w.sched_off);
+  a.pt = a.order + n_segments;
+  e = tr.run("attn_sched", [&] {
+    return mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kFwdTile, const_cast<int*>(a.order),
+                            const_cast<int*>(a.pt), s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("attn_fwd", [&] { return mf::launch_attn_fwd(a, q, kr, vb, o, lse, s); });
   return from_hip(e);
 }
@@ -271,7 +281,7 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return MF_ERR_INVALID_ARG;
-  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, pos ? max_pos : 0, dtype, true);
+  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, n_segments, pos ? max_pos : 0, dtype, true);
   if (workspace_bytes < w.total) return MF_ERR_WORKSPACE;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
 
@@ -329,6 +339,13 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   a.tab = tab;
   a.max_pos = max_pos;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  a.order = reinterpret_cast<int*>(ws + w.sched_off);
+  a.pt = a.order + n_segments;
+  e = tr.run("attn_sched", [&] {
+    return mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kDqTile, const_cast<int*>(a.order),
+                            const_cast<int*>(a.pt), s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("attn_bwd_delta", [&] { return mf::launch_attn_bwd_delta(a, o, dout, delta, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("attn_bwd_dkdv",

@@ -19,13 +19,6 @@ constexpr int kQB = 32;   // queries per dkdv LDS tile
 constexpr int kQT = 128;  // queries per dq workgroup (32 per wave)
 constexpr int kKT = 64;   // keys per dq LDS tile
 
-__device__ __forceinline__ void seg_bounds(const int* cu, int seg, int n_tokens, int& s0, int& s1) {
-  s0 = cu[seg];
-  s1 = cu[seg + 1];
-  s0 = min(max(s0, 0), n_tokens);
-  s1 = min(max(s1, s0), n_tokens);
-}
-
 // Rotate 4 consecutive elements (two pairs) starting at d0 (multiple of 4).
 template <int D>
 __device__ __forceinline__ void rotate4(float (&x)[4], int d0, int prow, int pcol, const float2* __restrict__ tab,

@@ -112,6 +112,44 @@ __device__ __forceinline__ bf16x8 lds_col_frag(const lds_char* tile, int rbase, 
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// One unit of attention work: a tile of one (segment, head).
+struct WorkItem {
+  int seg, head, tile;
+};
+
+// Decodes block b of an attention launch against the schedule written by
+// the scheduling kernel (order[r]: segment of rank r, longest first; pt[r]:
+// exclusive prefix of tile counts in rank order).  XCD x = b % 8 owns heads
+// x, x + 8, ...; its i-th block (i = b / 8) walks ranks, then its heads, then
+// tiles.  Returns false for the blocks past the end of their XCD's list.
+__device__ __forceinline__ bool decode_item(int b, int heads, int n_seg, const int* __restrict__ order,
+                                            const int* __restrict__ pt, WorkItem& w) {
+  const int x = b & 7;
+  const int i = b >> 3;
+  const int nx = (heads - x + 7) >> 3;
+  if (nx <= 0) return false;
+  const int total = pt[n_seg];
+  if (static_cast<long long>(i) >= static_cast<long long>(nx) * total) return false;
+  int lo = 0, hi = n_seg;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (static_cast<long long>(pt[mid]) * nx <= i) lo = mid; else hi = mid;
+  }
+  const int tiles = pt[lo + 1] - pt[lo];
+  const int j = i - pt[lo] * nx;
+  w.seg = order[lo];
+  w.head = x + 8 * (j / tiles);
+  w.tile = j % tiles;
+  return true;
+}
+
+__device__ __forceinline__ void seg_bounds(const int* __restrict__ cu, int seg, int n_tokens, int& s0, int& s1) {
+  s0 = cu[seg];
+  s1 = cu[seg + 1];
+  s0 = min(max(s0, 0), n_tokens);
+  s1 = min(max(s1, s0), n_tokens);
+}
+
 // Load 8 consecutive elements of a bf16 or f32 row as float.
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&x)[8]);

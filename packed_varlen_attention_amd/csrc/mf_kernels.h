@@ -24,6 +24,16 @@ hipError_t launch_rope_apply(const void* src, int src_dtype, void* dst, int dst_
                              const float2* tab, int max_pos, int n_tokens, int heads, int head_dim,
                              bool rotate, bool inverse, hipStream_t stream);
 
+// Longest-first schedule of (segment, tile) work; see sched.hip.
+hipError_t launch_sched(const int* cu_seqlens, int n_segments, int n_tokens, int tile, int* order, int* pt,
+                        hipStream_t stream);
+// Blocks to launch for a schedule with the given tile size (an upper bound).
+long long sched_grid(int n_tokens, int n_segments, int heads, int tile);
+
+constexpr int kFwdTile = 128;   // query rows per forward workgroup
+constexpr int kDqTile = 128;    // query rows per dq workgroup
+constexpr int kDkdvTile = 128;  // keys per dkdv workgroup
+
 struct AttnArgs {
   const int* cu_seqlens;
   int n_segments;
@@ -36,6 +46,8 @@ struct AttnArgs {
   const float2* tab;
   int max_pos;
   float scale;
+  const int* order;  // schedule: segments longest first
+  const int* pt;     // schedule: tile prefix in that order
 };
 
 // q: caller's (rotated in-kernel), kr/vb: bf16 [N][H][D] (kr already rotated).

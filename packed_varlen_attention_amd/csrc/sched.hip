@@ -1,0 +1,107 @@
+// Work schedule for the attention kernels: longest segment first, and every
+// tile of one (segment, head) on the same XCD.
+//
+// sched_kernel (one workgroup) sorts the segments by length, longest first
+// (ties by index; up to kMaxSortSegments, beyond that the given order), and
+// writes order[r] = segment of rank r and the exclusive prefix pt[r] of the
+// tile counts ceil(L / tile) in that order (pt[n] = total tiles).
+//
+// The attention kernels launch 8 * ceil(H/8) * bound blocks and decode block
+// b with decode_item(): XCD x = b % 8 (the dispatcher hands consecutive block
+// ids to the 8 XCDs in turn) owns heads x, x+8, ...; its i-th block (i = b/8)
+// walks ranks in order, heads of the rank, then tiles, so the concurrently
+// running blocks of one XCD share one (segment, head)'s K and V in that XCD's
+// L2.  Blocks past the end of their XCD's list exit.
+#include "mf_device.h"
+#include "mf_kernels.h"
+
+namespace mf {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kMaxSortSegments = 1024;
+
+__global__ __launch_bounds__(kThreads) void sched_kernel(const int* __restrict__ cu, int n_seg, int n_tokens,
+                                                         int tile, int* __restrict__ order, int* __restrict__ pt) {
+  __shared__ int sLen[kMaxSortSegments];
+  __shared__ int sWave[kThreads / 64];
+  __shared__ int sCarry;
+  const bool sort = n_seg <= kMaxSortSegments;
+  auto seg_len = [&](int s) {
+    int a = cu[s], b = cu[s + 1];
+    a = min(max(a, 0), n_tokens);
+    b = min(max(b, a), n_tokens);
+    return b - a;
+  };
+  if (sort) {
+    for (int s = threadIdx.x; s < n_seg; s += kThreads) sLen[s] = seg_len(s);
+    __syncthreads();
+    for (int s = threadIdx.x; s < n_seg; s += kThreads) {
+      const int l = sLen[s];
+      int rank = 0;
+      for (int t = 0; t < n_seg; ++t) {
+        const int lt = sLen[t];
+        rank += (lt > l) || (lt == l && t < s);
+      }
+      order[rank] = s;
+    }
+  } else {
+    for (int s = threadIdx.x; s < n_seg; s += kThreads) order[s] = s;
+  }
+  __syncthreads();  // order[] (global) is read back by other threads below
+  if (threadIdx.x == 0) sCarry = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int base = 0; base < n_seg; base += kThreads) {
+    const int r = base + threadIdx.x;
+    int t = 0;
+    if (r < n_seg) {
+      const int s = order[r];
+      const int l = sort ? sLen[s] : seg_len(s);
+      t = (l + tile - 1) / tile;
+    }
+    int x = t;  // inclusive scan
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) sWave[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int w = lane < kThreads / 64 ? sWave[lane] : 0;
+#pragma unroll
+      for (int d = 1; d < kThreads / 64; d <<= 1) {
+        const int y = __shfl_up(w, d, 64);
+        if (lane >= d) w += y;
+      }
+      if (lane < kThreads / 64) sWave[lane] = w;
+    }
+    __syncthreads();
+    const int incl = x + (wave > 0 ? sWave[wave - 1] : 0) + sCarry;
+    if (r < n_seg) pt[r] = incl - t;
+    __syncthreads();
+    if (threadIdx.x == kThreads - 1) sCarry = incl;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) pt[n_seg] = sCarry;
+}
+
+}  // namespace
+
+hipError_t launch_sched(const int* cu_seqlens, int n_segments, int n_tokens, int tile, int* order, int* pt,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kThreads), 0, stream, cu_seqlens, n_segments, n_tokens, tile, order,
+                     pt);
+  return hipGetLastError();
+}
+
+long long sched_grid(int n_tokens, int n_segments, int heads, int tile) {
+  const long long per_xcd_heads = (heads + 7) / 8;
+  const long long tiles_bound = (static_cast<long long>(n_tokens) + tile - 1) / tile + n_segments;
+  return 8LL * per_xcd_heads * tiles_bound;
+}
+
+}  // namespace mf

@@ -53,12 +53,14 @@ def assert_close(got, ref, max_abs: float, mean_abs: float, label: str) -> None:
     assert mn <= mean_abs, f"{label}: mean-abs {mn} > {mean_abs}"
 
 
-def assert_close_scaled(got, ref, label: str, rel_rms_max: float = 8e-3) -> None:
+def assert_close_scaled(got, ref, label: str, rel_rms_max: float = 8e-3, qscale: float = 1.0) -> None:
     """Bar for inputs scaled away from N(0, 1) (the peaky gates): the fixed
     2e-2 max-abs bar holds for outputs up to |4|, so it grows with max|ref|
-    beyond that; the relative RMS error must stay at the bf16 level."""
+    beyond that, and with the Q scale, which multiplies the logits and so the
+    logit error the bf16 rounding of rotated Q and K leaves; the relative RMS
+    error must stay at the bf16 level."""
     ref = np.asarray(ref, dtype=np.float64)
-    scale = max(1.0, float(np.abs(ref).max()) / 4.0) if ref.size else 1.0
+    scale = qscale * (max(1.0, float(np.abs(ref).max()) / 4.0) if ref.size else 1.0)
     mx, mn = errors(got, ref)
     rel = float(np.sqrt(np.mean((np.asarray(got) - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
     print(f"  {label}: max_abs={mx:.3e} (bar {2e-2 * scale:.3e}) rel_rms={rel:.3e} max|ref|={np.abs(ref).max():.3e}",

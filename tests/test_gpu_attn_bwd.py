@@ -59,9 +59,9 @@ def test_without_rope_and_peaky():
     c = Case(SMALL[:6], 1 << 20, 2, 128, "bf16", seed=32, qscale=4.0, with_dout=True)
     dq, dk, dv = _run(c, use_pos=False)
     rq, rk, rv = oracle.attn_bwd(c.q, c.k, c.v, c.do, c.cu, None, THETA)
-    assert_close_scaled(host_f64(dq), rq, "dQ no-rope q*4")
-    assert_close_scaled(host_f64(dk), rk, "dK no-rope q*4")
-    assert_close_scaled(host_f64(dv), rv, "dV no-rope q*4")
+    assert_close_scaled(host_f64(dq), rq, "dQ no-rope q*4", qscale=4.0)
+    assert_close_scaled(host_f64(dk), rk, "dK no-rope q*4", qscale=4.0)
+    assert_close_scaled(host_f64(dv), rv, "dV no-rope q*4", qscale=4.0)
 
 
 def test_deterministic_and_segment_local():
