@@ -1,7 +1,7 @@
 // Public C ABI (include/mf.h): host-side argument checks, workspace layout and
 // kernel launches.  Nothing here synchronises; every error is detected
 // before the first launch of a call.
-#include "../../include/mf.h"
+#include "mf.h"
 
 #include <math.h>
 #include <stdint.h>

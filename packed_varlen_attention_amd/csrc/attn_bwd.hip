@@ -14,10 +14,11 @@ namespace mf {
 
 namespace {
 
-constexpr int kKB = 128;  // keys per dkdv workgroup (32 per wave)
-constexpr int kQB = 32;   // queries per dkdv LDS tile
-constexpr int kQT = 128;  // queries per dq workgroup (32 per wave)
-constexpr int kKT = 64;   // keys per dq LDS tile
+constexpr int kKB = kDkdvTile;  // keys per dkdv workgroup (32 per wave)
+constexpr int kQB = 32;         // queries per dkdv LDS tile
+constexpr int kQT = kDqTile;    // queries per dq workgroup (32 per wave)
+constexpr int kKT = 64;         // keys per dq LDS tile
+static_assert(kKB == kQT, "dkdv and dq share one schedule");
 
 // Rotate 4 consecutive elements (two pairs) starting at d0 (multiple of 4).
 template <int D>
@@ -65,26 +66,28 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, con
 }
 
 template <int D, typename TOut>
-__global__ __launch_bounds__(256) void dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void dkdv_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     const uint16_t* __restrict__ dob, const float* __restrict__ lse, const float* __restrict__ delta,
-    TOut* __restrict__ dk, TOut* __restrict__ dv, const int* __restrict__ cu, int n_tokens, int heads,
-    const int2* __restrict__ pos, const float2* __restrict__ tab, int max_pos, float scale, float scale_log2) {
+    TOut* __restrict__ dk, TOut* __restrict__ dv, const int* __restrict__ cu, const int* __restrict__ order,
+    const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int2* __restrict__ pos,
+    const float2* __restrict__ tab, int max_pos, float scale, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
+  constexpr int CH = D / 8;
   constexpr int kTileBytes = kQB * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
-  __shared__ float sL[kQB];
-  __shared__ float sD[kQB];
-  lds_char* sQ = (lds_char*)(smem);
-  lds_char* sO = sQ + kTileBytes;
+  constexpr int kLoads = kQB * CH / 256;  // chunks per thread per tensor per tile
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // [buf][Q, dO]
+  __shared__ float sL[2][kQB];
+  __shared__ float sD[2][kQB];
 
-  const int seg = blockIdx.z;
-  const int head = blockIdx.y;
+  WorkItem it;
+  if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
+  const int head = it.head;
   int s0, s1;
-  seg_bounds(cu, seg, n_tokens, s0, s1);
+  seg_bounds(cu, it.seg, n_tokens, s0, s1);
   const int L = s1 - s0;
-  const int kbase = blockIdx.x * kKB;
+  const int kbase = it.tile * kKB;
   if (kbase >= L) return;
 
   const int lane = threadIdx.x & 63;
@@ -92,21 +95,52 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   const int hh = lane >> 5;
   const int key = kbase + wave * 32 + (lane & 31);
   const bool kok = key < L;
-  const long long krow = (static_cast<long long>(s0) + key) * heads + head;
+  const long long krow = (static_cast<long long>(s0) + min(key, L - 1)) * heads + head;
 
   // K and V fragments (B operands of S = Q Kr^T and dP = dO V^T).
   bf16x8 kf[NKK], vf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const int e0 = 16 * kk + 8 * hh;
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (kok) {
-      a = *reinterpret_cast<const u32x4*>(kr + krow * D + e0);
-      b = *reinterpret_cast<const u32x4*>(vb + krow * D + e0);
-    }
-    kf[kk] = __builtin_bit_cast(bf16x8, a);
-    vf[kk] = __builtin_bit_cast(bf16x8, b);
+    kf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + krow * D + e0));
+    vf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vb + krow * D + e0));
   }
+
+  u32x4 qreg[kLoads], oreg[kLoads];
+  float lreg = 0.f, dreg = 0.f;
+  auto gload = [&](int q0) {
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int ci = threadIdx.x + 256 * r;
+      const int qq = min(q0 + ci / CH, L - 1);
+      const size_t g = (static_cast<size_t>(s0 + qq) * heads + head) * D + (ci % CH) * 8;
+      qreg[r] = *reinterpret_cast<const u32x4*>(qr + g);
+      oreg[r] = *reinterpret_cast<const u32x4*>(dob + g);
+    }
+    if (threadIdx.x < kQB) {
+      const int qq = q0 + threadIdx.x;
+      const bool ok = qq < L;
+      const size_t g = static_cast<size_t>(head) * n_tokens + s0 + min(qq, L - 1);
+      lreg = ok ? lse[g] * kLog2e : INFINITY;  // rows past the end get P = 0
+      dreg = ok ? delta[g] : 0.f;
+    }
+  };
+  lds_char* const sbase = (lds_char*)(smem);
+  auto lstore = [&](int buf) {
+    lds_char* sQ = sbase + buf * 2 * kTileBytes;
+    lds_char* sO = sQ + kTileBytes;
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int ci = threadIdx.x + 256 * r;
+      const int off = Tile<D>::off(ci / CH, ci % CH);
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sQ + off) = qreg[r];
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sO + off) = oreg[r];
+    }
+    if (threadIdx.x < kQB) {
+      sL[buf][threadIdx.x] = lreg;
+      sD[buf][threadIdx.x] = dreg;
+    }
+  };
 
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -117,28 +151,16 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       dvacc[db][i] = 0.f;
     }
 
-  for (int q0 = 0; q0 < L; q0 += kQB) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < kQB * (D / 8); c += 256) {
-      const int row = c / (D / 8);
-      const int ch = c % (D / 8);
-      const int qq = q0 + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (qq < L) {
-        const size_t g = (static_cast<size_t>(s0 + qq) * heads + head) * D + ch * 8;
-        a = *reinterpret_cast<const u32x4*>(qr + g);
-        b = *reinterpret_cast<const u32x4*>(dob + g);
-      }
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sQ + Tile<D>::off(row, ch)) = a;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sO + Tile<D>::off(row, ch)) = b;
-    }
-    if (threadIdx.x < kQB) {
-      const int qq = q0 + threadIdx.x;
-      const bool ok = qq < L;
-      sL[threadIdx.x] = ok ? lse[static_cast<size_t>(head) * n_tokens + s0 + qq] * kLog2e : INFINITY;
-      sD[threadIdx.x] = ok ? delta[static_cast<size_t>(head) * n_tokens + s0 + qq] : 0.f;
-    }
-    __syncthreads();
+  const int ntiles = (L + kQB - 1) / kQB;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const bool more = j + 1 < ntiles;
+    if (more) gload((j + 1) * kQB);
+    const int buf = j & 1;
+    const lds_char* sQ = sbase + buf * 2 * kTileBytes;
+    const lds_char* sO = sQ + kTileBytes;
 
     f32x16 sacc, dpacc;
 #pragma unroll
@@ -155,8 +177,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int qq = acc_row(i, hh);
-      const float p = fast_exp2(sacc[i] * scale_log2 - sL[qq]);
-      const float ds = p * (dpacc[i] - sD[qq]);
+      const float p = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, -sL[buf][qq]));
+      const float ds = p * (dpacc[i] - sD[buf][qq]);
       pb[i >> 3][i & 7] = static_cast<__bf16>(p);
       dsb[i >> 3][i & 7] = static_cast<__bf16>(ds);
     }
@@ -167,6 +189,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
         dvacc[db] = mfma32(lds_col_frag<D>(sO, 16 * c, 32 * db, lane), pb[c], dvacc[db]);
         dkacc[db] = mfma32(lds_col_frag<D>(sQ, 16 * c, 32 * db, lane), dsb[c], dkacc[db]);
       }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
   }
 
   if (kok) {
@@ -188,24 +212,26 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
 }
 
 template <int D, typename TOut>
-__global__ __launch_bounds__(256) void dq_kernel(
+__global__ __launch_bounds__(256, 2) void dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     const uint16_t* __restrict__ dob, const float* __restrict__ lse, const float* __restrict__ delta,
-    TOut* __restrict__ dq, const int* __restrict__ cu, int n_tokens, int heads, const int2* __restrict__ pos,
-    const float2* __restrict__ tab, int max_pos, float scale, float scale_log2) {
+    TOut* __restrict__ dq, const int* __restrict__ cu, const int* __restrict__ order, const int* __restrict__ pt,
+    int n_seg, int n_tokens, int heads, const int2* __restrict__ pos, const float2* __restrict__ tab, int max_pos,
+    float scale, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
+  constexpr int CH = D / 8;
   constexpr int kTileBytes = kKT * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
-  lds_char* sK = (lds_char*)(smem);
-  lds_char* sV = sK + kTileBytes;
+  constexpr int kLoads = kKT * CH / 256;
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // [buf][K, V]
 
-  const int seg = blockIdx.z;
-  const int head = blockIdx.y;
+  WorkItem it;
+  if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
+  const int head = it.head;
   int s0, s1;
-  seg_bounds(cu, seg, n_tokens, s0, s1);
+  seg_bounds(cu, it.seg, n_tokens, s0, s1);
   const int L = s1 - s0;
-  const int qbase = blockIdx.x * kQT;
+  const int qbase = it.tile * kQT;
   if (qbase >= L) return;
 
   const int lane = threadIdx.x & 63;
@@ -213,22 +239,41 @@ __global__ __launch_bounds__(256) void dq_kernel(
   const int hh = lane >> 5;
   const int qi = qbase + wave * 32 + (lane & 31);
   const bool qok = qi < L;
-  const long long qrow = (static_cast<long long>(s0) + qi) * heads + head;
+  const long long qrow = (static_cast<long long>(s0) + min(qi, L - 1)) * heads + head;
 
   bf16x8 qf[NKK], df[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const int e0 = 16 * kk + 8 * hh;
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (qok) {
-      a = *reinterpret_cast<const u32x4*>(qr + qrow * D + e0);
-      b = *reinterpret_cast<const u32x4*>(dob + qrow * D + e0);
-    }
-    qf[kk] = __builtin_bit_cast(bf16x8, a);
-    df[kk] = __builtin_bit_cast(bf16x8, b);
+    qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + qrow * D + e0));
+    df[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dob + qrow * D + e0));
   }
   const float lse2 = qok ? lse[static_cast<size_t>(head) * n_tokens + s0 + qi] * kLog2e : INFINITY;
   const float dl = qok ? delta[static_cast<size_t>(head) * n_tokens + s0 + qi] : 0.f;
+
+  u32x4 kreg[kLoads], vreg[kLoads];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int ci = threadIdx.x + 256 * r;
+      const int kq = min(k0 + ci / CH, L - 1);
+      const size_t g = (static_cast<size_t>(s0 + kq) * heads + head) * D + (ci % CH) * 8;
+      kreg[r] = *reinterpret_cast<const u32x4*>(kr + g);
+      vreg[r] = *reinterpret_cast<const u32x4*>(vb + g);
+    }
+  };
+  lds_char* const sbase = (lds_char*)(smem);
+  auto lstore = [&](int buf) {
+    lds_char* sK = sbase + buf * 2 * kTileBytes;
+    lds_char* sV = sK + kTileBytes;
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int ci = threadIdx.x + 256 * r;
+      const int off = Tile<D>::off(ci / CH, ci % CH);
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sK + off) = kreg[r];
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sV + off) = vreg[r];
+    }
+  };
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -236,22 +281,16 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  for (int k0 = 0; k0 < L; k0 += kKT) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < kKT * (D / 8); c += 256) {
-      const int row = c / (D / 8);
-      const int ch = c % (D / 8);
-      const int kq = k0 + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (kq < L) {
-        const size_t g = (static_cast<size_t>(s0 + kq) * heads + head) * D + ch * 8;
-        a = *reinterpret_cast<const u32x4*>(kr + g);
-        b = *reinterpret_cast<const u32x4*>(vb + g);
-      }
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sK + Tile<D>::off(row, ch)) = a;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sV + Tile<D>::off(row, ch)) = b;
-    }
-    __syncthreads();
+  const int ntiles = (L + kKT - 1) / kKT;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = j * kKT;
+    const bool more = j + 1 < ntiles;
+    if (more) gload(k0 + kKT);
+    const lds_char* sK = sbase + (j & 1) * 2 * kTileBytes;
+    const lds_char* sV = sK + kTileBytes;
 
     bf16x8 dsb[kKT / 16];
 #pragma unroll
@@ -267,10 +306,11 @@ __global__ __launch_bounds__(256) void dq_kernel(
         sacc = mfma32(lds_row_frag<D>(sK, kb * 32, kk, lane), qf[kk], sacc);
         dpacc = mfma32(lds_row_frag<D>(sV, kb * 32, kk, lane), df[kk], dpacc);
       }
+      const bool tail = k0 + kb * 32 + 32 > L;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kq = k0 + kb * 32 + acc_row(i, hh);
-        const float p = kq < L ? fast_exp2(sacc[i] * scale_log2 - lse2) : 0.f;
+        float p = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, -lse2));
+        if (tail && k0 + kb * 32 + acc_row(i, hh) >= L) p = 0.f;
         dsb[2 * kb + (i >> 3)][i & 7] = static_cast<__bf16>(p * (dpacc[i] - dl));
       }
     }
@@ -279,6 +319,8 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         dqacc[db] = mfma32(lds_col_frag<D>(sK, 16 * c, 32 * db, lane), dsb[c], dqacc[db]);
+    if (more) lstore((j + 1) & 1);
+    __syncthreads();
   }
 
   if (qok) {
@@ -310,23 +352,27 @@ hipError_t launch_delta_t(const AttnArgs& a, const void* o, const void* dout, fl
 template <int D, typename TOut>
 hipError_t launch_dkdv_t(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,
                          const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
-  const dim3 grid((a.max_seqlen + kKB - 1) / kKB, a.n_heads, a.n_segments);
-  hipLaunchKernelGGL((dkdv_kernel<D, TOut>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(qr),
-                     static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
-                     static_cast<const uint16_t*>(dob), lse, delta, static_cast<TOut*>(dk), static_cast<TOut*>(dv),
-                     a.cu_seqlens, a.n_tokens, a.n_heads, reinterpret_cast<const int2*>(a.pos), a.tab, a.max_pos,
-                     a.scale, a.scale * kLog2e);
+  const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kKB);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((dkdv_kernel<D, TOut>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
+                     static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob), lse, delta,
+                     static_cast<TOut*>(dk), static_cast<TOut*>(dv), a.cu_seqlens, a.order, a.pt, a.n_segments,
+                     a.n_tokens, a.n_heads, reinterpret_cast<const int2*>(a.pos), a.tab, a.max_pos, a.scale,
+                     a.scale * kLog2e);
   return hipGetLastError();
 }
 
 template <int D, typename TOut>
 hipError_t launch_dq_t(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,
                        const float* lse, const float* delta, void* dq, hipStream_t stream) {
-  const dim3 grid((a.max_seqlen + kQT - 1) / kQT, a.n_heads, a.n_segments);
-  hipLaunchKernelGGL((dq_kernel<D, TOut>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(qr),
-                     static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
-                     static_cast<const uint16_t*>(dob), lse, delta, static_cast<TOut*>(dq), a.cu_seqlens, a.n_tokens,
-                     a.n_heads, reinterpret_cast<const int2*>(a.pos), a.tab, a.max_pos, a.scale, a.scale * kLog2e);
+  const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kQT);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((dq_kernel<D, TOut>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
+                     static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob), lse, delta,
+                     static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
+                     reinterpret_cast<const int2*>(a.pos), a.tab, a.max_pos, a.scale, a.scale * kLog2e);
   return hipGetLastError();
 }
 
