@@ -4,13 +4,14 @@
 // concatenated text and image tokens; samples packed into one stream never
 // attend to each other).
 //
-// One workgroup = 4 waves = 128 query rows of one (segment, head), taken from
-// the longest-first, XCD-grouped schedule; each wave owns 32 query rows.  Two
-// workgroups share a CU (<= 256 registers per lane, 64 KB LDS each), so each
-// SIMD interleaves two waves' matrix and vector work.  The loop walks the
-// segment's keys in tiles of 64:
-//   the next K/V tile is loaded to registers while this one is computed, and
-//   written to the other half of a double-buffered LDS (one barrier per tile);
+// One workgroup = 8 waves = 256 query rows of one (segment, head), taken from
+// the longest-first, XCD-grouped schedule; each wave owns 32 query rows and
+// all eight share each K/V tile.  With <= 256 registers per lane each SIMD
+// runs two waves, interleaving their matrix and vector work.  The loop walks
+// the segment's keys in tiles of 64, software-pipelined:
+//   K and V tiles are copied global -> LDS directly (no registers), double-
+//   buffered, with K one tile ahead of V, so the scores of tile j+1 are
+//   computed while the softmax and P V of tile j run; one barrier per tile;
 //   S^T = K Q^T      32x32x16 bf16 MFMA, Q in registers (rotated at load);
 //   online softmax   per query column, lane-local; the output is rescaled only
 //                    when the running max grows by more than 2^8 (exact: the
@@ -19,6 +20,8 @@
 // Computing S^T rather than S puts each query's scores, running max and sum
 // and output accumulator in the same lane, so no shuffles are needed except
 // one max exchange between the two lane halves per tile.
+#include <type_traits>
+
 #include "mf_device.h"
 #include "mf_kernels.h"
 
@@ -41,7 +44,7 @@ __device__ __forceinline__ void load_q8(const T* p, bool ok, float (&x)[8]) {
 }
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     const TIn* __restrict__ q, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     TIn* __restrict__ o, float* __restrict__ lse, const int* __restrict__ cu, const int* __restrict__ order,
     const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int2* __restrict__ pos,
@@ -49,9 +52,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;                   // 16-byte chunks per row
-  constexpr int kTileBytes = kKT * D * 2;
-  constexpr int kLoads = kKT * CH / 256;      // chunks per thread per tensor per tile
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // [buf][K, V]
+  constexpr int kRowBytes = D * 2;
+  constexpr int kTileBytes = kKT * kRowBytes;
+  constexpr int kRowsPerInst = 1024 / kRowBytes;  // rows one wave-wide 16-byte load covers
+  constexpr int kInstPerWave = kKT / kRowsPerInst / 8;
+  // LDS: K tiles [2] then V tiles [2]
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
 
   WorkItem it;
   if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   if (qbase >= L) return;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5;
   const int qi = qbase + wave * 32 + (lane & 31);
   const bool qok = qi < L;
@@ -85,30 +91,69 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     }
   }
 
-  // K/V staging: thread -> (row, chunk) pairs of a tile; rows past the end of
-  // the segment re-read its last row (their scores are masked).
-  u32x4 kreg[kLoads], vreg[kLoads];
-  auto gload = [&](int k0) {
+  // ---- global -> LDS tile copies (rows past the segment end re-read its
+  // last row; their scores are masked).  Per lane and load: a constant row /
+  // chunk offset inside the tile plus a block-uniform tile base.
+  const size_t hD = static_cast<size_t>(heads) * D;
+  const uint16_t* kseg = kr + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
+  const uint16_t* vseg = vb + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
+  int ld_row[kInstPerWave], ld_off[kInstPerWave];
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-      const int ci = threadIdx.x + 256 * r;
-      const int key = min(k0 + ci / CH, L - 1);
-      const size_t g = (static_cast<size_t>(s0 + key) * heads + head) * D + (ci % CH) * 8;
-      kreg[r] = *reinterpret_cast<const u32x4*>(kr + g);
-      vreg[r] = *reinterpret_cast<const u32x4*>(vb + g);
+  for (int r = 0; r < kInstPerWave; ++r) {
+    const int inst = wave * kInstPerWave + r;
+    ld_row[r] = inst * kRowsPerInst + lane / CH;
+    ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
+  }
+  lds_char* const sK0 = (lds_char*)(smem);
+  lds_char* const sV0 = sK0 + 2 * kTileBytes;
+  auto load_rows = [&](const uint16_t* seg, int k0, lds_char* dst) {
+    const bool tail = k0 + kKT > L;
+#pragma unroll
+    for (int r = 0; r < kInstPerWave; ++r) {
+      const int row = tail ? min(k0 + ld_row[r], L - 1) : k0 + ld_row[r];
+      const uint16_t* src = seg + static_cast<size_t>(row) * hD + ld_off[r];
+      __builtin_amdgcn_global_load_lds(src, dst + (wave * kInstPerWave + r) * 1024, 16, 0, 0);
     }
   };
-  lds_char* const sbase = (lds_char*)(smem);
-  auto lstore = [&](int buf) {
-    lds_char* sK = sbase + buf * 2 * kTileBytes;
-    lds_char* sV = sK + kTileBytes;
+
+  // ---- LDS fragment offsets (bytes), fixed per lane; tile bases add on top.
+  int roff[NKK];  // A-operand rows: row perm32(lane % 32), chunk 2kk + h
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-      const int ci = threadIdx.x + 256 * r;
-      const int off = Tile<D>::off(ci / CH, ci % CH);
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sK + off) = kreg[r];
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sV + off) = vreg[r];
-    }
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = Tile<D>::off(perm32(lane & 31), 2 * kk + hh);
+  int coff[NDB][2];  // transpose reads: rows 8h + (lane/4)%4 (+4), columns of block db
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int col = 32 * db + 16 * (g & 1) + 4 * (l16 & 3);
+    const int row0 = 8 * hh + (l16 >> 2);
+    coff[db][0] = Tile<D>::off(row0, col >> 3) + ((col >> 2) & 1) * 8;
+    coff[db][1] = Tile<D>::off(row0 + 4, col >> 3) + ((col >> 2) & 1) * 8;
+  }
+  auto s_tile = [&](const lds_char* sK, f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            sK + roff[kk] + kb * 32 * kRowBytes);
+        acc[kb] = mfma32(a, qf[kk], acc[kb]);
+      }
+  };
+  auto col_frag = [&](const lds_char* sV, int c, int db) {
+    const lds_char* p0 = sV + coff[db][0] + 16 * c * kRowBytes;
+    const lds_char* p1 = sV + coff[db][1] + 16 * c * kRowBytes;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p0)));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p1)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, r);
   };
 
   float m_run = -INFINITY;  // running max, log2 units, same in both lane halves
@@ -119,37 +164,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
+  // Pipeline: K runs one tile ahead of V, so the scores of tile j+1 are
+  // computed while the softmax of tile j runs.  Tile t of K lives in K
+  // buffer t % 2, tile t of V in V buffer t % 2.
   const int ntiles = (L + kKT - 1) / kKT;
-  gload(0);
-  lstore(0);
+  f32x16 scur[2], snext[2];
+  load_rows(kseg, 0, sK0);
+  load_rows(vseg, 0, sV0);
+  if (ntiles > 1) load_rows(kseg, kKT, sK0 + kTileBytes);
+  wait_vmem();
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * kKT;
-    const bool more = j + 1 < ntiles;
-    if (more) gload(k0 + kKT);
-    const lds_char* sK = sbase + (j & 1) * 2 * kTileBytes;
-    const lds_char* sV = sK + kTileBytes;
+  s_tile(sK0, scur);
+  __syncthreads();  // every wave is done with K tile 0 before tile 2 reuses its buffer
 
-    f32x16 sacc[kKT / 32];
+  // One pipeline step: softmax + P V of tile j, scores of tile j + 1.  Only
+  // the last tile masks keys; the rescale branch is rare.  The instruction
+  // groups below keep LDS reads several MFMAs ahead of their use and spread
+  // the softmax's vector work between the matrix instructions.
+  auto step = [&](int j, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    const int k0 = j * kKT;
+    const int b = j & 1;
+    if (j + 2 < ntiles) load_rows(kseg, k0 + 2 * kKT, sK0 + b * kTileBytes);
+    if (j + 1 < ntiles) load_rows(vseg, k0 + kKT, sV0 + (b ^ 1) * kTileBytes);
+    if constexpr (kTail) {
 #pragma unroll
-    for (int kb = 0; kb < kKT / 32; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) sacc[kb] = mfma32(lds_row_frag<D>(sK, kb * 32, kk, lane), qf[kk], sacc[kb]);
-    }
-    if (k0 + kKT > L) {
-#pragma unroll
-      for (int kb = 0; kb < kKT / 32; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (k0 + kb * 32 + acc_row(i, hh) >= L) sacc[kb][i] = -INFINITY;
+          if (k0 + kb * 32 + acc_row(i, hh) >= L) scur[kb][i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < kKT / 32; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, scur[kb][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mt = mx * scale_log2;
     if (__any(mt > m_run + kRescaleSlack)) {
@@ -162,24 +211,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       m_run = m_new;
     }
+    // Straight-line region: exp/sum/convert of tile j, S of tile j+1, P V of tile j.
     bf16x8 pf[kKT / 16];
 #pragma unroll
-    for (int kb = 0; kb < kKT / 32; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[kb][i], scale_log2, -m_run));
-        l_run += p;
-        pf[2 * kb + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(scur[kb][i], scale_log2, -m_run));
+        const float p1 = fast_exp2(__builtin_fmaf(scur[kb][i + 1], scale_log2, -m_run));
+        l_run += p0 + p1;
+        pf[2 * kb + (i >> 3)][i & 7] = static_cast<__bf16>(p0);
+        pf[2 * kb + (i >> 3)][(i & 7) + 1] = static_cast<__bf16>(p1);
       }
+    // Scores of tile j + 1 (for the last tile they read a stale buffer and
+    // are discarded).
+    s_tile(sK0 + (b ^ 1) * kTileBytes, snext);
+    const lds_char* sV = sV0 + b * kTileBytes;
 #pragma unroll
     for (int c = 0; c < kKT / 16; ++c)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        oacc[db] = mfma32(lds_col_frag<D>(sV, 16 * c, 32 * db, lane), pf[c], oacc[db]);
-
-    if (more) lstore((j + 1) & 1);
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(col_frag(sV, c, db), pf[c], oacc[db]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) scur[kb] = snext[kb];
+    wait_vmem();
     __syncthreads();
-  }
+  };
+  for (int j = 0; j + 1 < ntiles; ++j) step(j, std::false_type{});
+  step(ntiles - 1, std::true_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qok) {
@@ -203,7 +261,7 @@ hipError_t launch_fwd_t(const AttnArgs& a, const void* q, const void* kr, const 
                         hipStream_t stream) {
   const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kQT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
                      static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
                      static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
                      reinterpret_cast<const int2*>(a.pos), a.tab, a.max_pos, a.scale * kLog2e);

@@ -112,6 +112,34 @@ __device__ __forceinline__ bf16x8 lds_col_frag(const lds_char* tile, int rbase, 
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Asynchronous copy of one [rows][D] bf16 tile from global memory straight
+// into a swizzled LDS tile (global_load_lds_dwordx4: lane i of a wave lands
+// its 16 bytes at the wave's LDS base + 16 i).  The wave covers 1 KB per
+// instruction; the swizzle is applied by choosing which global chunk each
+// lane fetches.  `rows` must be a multiple of 4 * (1024 / (D * 2)); the caller
+// waits on vmcnt and then a barrier before the tile is read.
+// row_addr(r) gives the global address of tile row r (already clamped).
+template <int D, int kRows, int kWaves, typename RowAddr>
+__device__ __forceinline__ void tile_load_async(lds_char* tile, int wave, int lane, RowAddr row_addr) {
+  constexpr int kRowsPerInst = 1024 / (D * 2);
+  constexpr int kInst = kRows / kRowsPerInst;
+  static_assert(kInst % kWaves == 0, "tile rows must split evenly over the waves");
+  constexpr int kPerWave = kInst / kWaves;
+  constexpr int CH = D / 8;
+#pragma unroll
+  for (int r = 0; r < kPerWave; ++r) {
+    const int inst = wave * kPerWave + r;
+    const int row = inst * kRowsPerInst + lane / CH;
+    const int chunk = (lane % CH) ^ Tile<D>::swz(row);
+    const uint16_t* src = row_addr(row) + chunk * 8;
+    __builtin_amdgcn_global_load_lds(src, tile + inst * 1024, 16, 0, 0);
+  }
+}
+
+// Wait until this wave's outstanding global loads (including loads into LDS)
+// have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // One unit of attention work: a tile of one (segment, head).
 struct WorkItem {
   int seg, head, tile;
