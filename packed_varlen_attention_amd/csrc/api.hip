@@ -70,7 +70,7 @@ AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim
   w.qr = backward ? tensor_bf16 : 0;
   w.vb = dtype == MF_F32 ? tensor_bf16 : 0;
   w.dob = (backward && dtype == MF_F32) ? tensor_bf16 : 0;
-  w.delta = backward ? static_cast<size_t>(n_tokens) * n_heads * sizeof(float) : 0;
+  w.delta = backward ? 2 * static_cast<size_t>(n_tokens) * n_heads * sizeof(float) : 0;  // delta, lse2
   size_t off = 0;
   w.tab_off = off;
   off += align_up(w.tab);
@@ -292,6 +292,7 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   const void* kr = k;
   const void* qr = q;
   float* delta = reinterpret_cast<float*>(ws + w.delta_off);
+  float* lse2 = delta + static_cast<size_t>(n_tokens) * n_heads;
   const void* vb = v;
   const void* dob = dout;
   hipError_t e = hipSuccess;
@@ -346,12 +347,12 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
                             const_cast<int*>(a.pt), s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
-  e = tr.run("attn_bwd_delta", [&] { return mf::launch_attn_bwd_delta(a, o, dout, delta, s); });
+  e = tr.run("attn_bwd_delta", [&] { return mf::launch_attn_bwd_delta(a, o, dout, lse, delta, lse2, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("attn_bwd_dkdv",
-             [&] { return mf::launch_attn_bwd_dkdv(a, qr, kr, vb, dob, lse, delta, dk, dv, s); });
+             [&] { return mf::launch_attn_bwd_dkdv(a, qr, kr, vb, dob, lse2, delta, dk, dv, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
-  e = tr.run("attn_bwd_dq", [&] { return mf::launch_attn_bwd_dq(a, qr, kr, vb, dob, lse, delta, dq, s); });
+  e = tr.run("attn_bwd_dq", [&] { return mf::launch_attn_bwd_dq(a, qr, kr, vb, dob, lse2, delta, dq, s); });
   return from_hip(e);
 }
 

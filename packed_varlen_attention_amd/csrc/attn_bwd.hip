@@ -7,6 +7,8 @@
 // where dS = P * (dO V^T - Delta); dQ and dK are rotated back by the inverse
 // rotation in the epilogues.  Each output element is written by exactly one
 // lane and summed in a fixed order: results are deterministic (no atomics).
+#include <type_traits>
+
 #include "mf_device.h"
 #include "mf_kernels.h"
 
@@ -42,7 +44,8 @@ __device__ __forceinline__ void rotate4(float (&x)[4], int d0, int prow, int pco
 
 template <int D, typename T>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                    float* __restrict__ delta, int n_tokens, int heads) {
+                                                    const float* __restrict__ lse, float* __restrict__ delta,
+                                                    float* __restrict__ lse2, int n_tokens, int heads) {
   constexpr int kLanesPerRow = D / 8;
   const long long rows = static_cast<long long>(n_tokens) * heads;
   const long long gid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -61,25 +64,28 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, con
   if (row < rows && sub == 0) {
     const long long t = row / heads;
     const int h = static_cast<int>(row % heads);
-    delta[static_cast<size_t>(h) * n_tokens + t] = acc;
+    const size_t i = static_cast<size_t>(h) * n_tokens + t;
+    delta[i] = acc;
+    lse2[i] = lse[i] * kLog2e;
   }
 }
 
 template <int D, typename TOut>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
-    const uint16_t* __restrict__ dob, const float* __restrict__ lse, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dob, const float* __restrict__ lse2, const float* __restrict__ delta,
     TOut* __restrict__ dk, TOut* __restrict__ dv, const int* __restrict__ cu, const int* __restrict__ order,
     const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int2* __restrict__ pos,
     const float2* __restrict__ tab, int max_pos, float scale, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;
-  constexpr int kTileBytes = kQB * D * 2;
-  constexpr int kLoads = kQB * CH / 256;  // chunks per thread per tensor per tile
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // [buf][Q, dO]
-  __shared__ float sL[2][kQB];
-  __shared__ float sD[2][kQB];
+  constexpr int kRowBytes = D * 2;
+  constexpr int kTileBytes = kQB * kRowBytes;
+  constexpr int kRowsPerInst = 1024 / kRowBytes;
+  constexpr int kInstPerWave = kQB / kRowsPerInst / 4;
+  // LDS: Q tiles [2], dO tiles [2], then per buffer 32 log2-LSE + 32 Delta
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes + 2 * 2 * kQB * 4];
 
   WorkItem it;
   if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   if (kbase >= L) return;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5;
   const int key = kbase + wave * 32 + (lane & 31);
   const bool kok = key < L;
@@ -106,40 +112,63 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     vf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vb + krow * D + e0));
   }
 
-  u32x4 qreg[kLoads], oreg[kLoads];
-  float lreg = 0.f, dreg = 0.f;
-  auto gload = [&](int q0) {
+  // ---- global -> LDS copies of the Q / dO tiles and their row statistics.
+  const size_t hD = static_cast<size_t>(heads) * D;
+  const uint16_t* qseg = qr + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
+  const uint16_t* oseg = dob + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
+  const float* stat_src = (lane < 32 ? lse2 : delta) + static_cast<size_t>(head) * n_tokens + s0;
+  int ld_row[kInstPerWave], ld_off[kInstPerWave];
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-      const int ci = threadIdx.x + 256 * r;
-      const int qq = min(q0 + ci / CH, L - 1);
-      const size_t g = (static_cast<size_t>(s0 + qq) * heads + head) * D + (ci % CH) * 8;
-      qreg[r] = *reinterpret_cast<const u32x4*>(qr + g);
-      oreg[r] = *reinterpret_cast<const u32x4*>(dob + g);
+  for (int r = 0; r < kInstPerWave; ++r) {
+    const int inst = wave * kInstPerWave + r;
+    ld_row[r] = inst * kRowsPerInst + lane / CH;
+    ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
+  }
+  lds_char* const sQ0 = (lds_char*)(smem);
+  lds_char* const sO0 = sQ0 + 2 * kTileBytes;
+  lds_char* const sS0 = sQ0 + 4 * kTileBytes;  // [buf][lse2 x 32, delta x 32]
+  auto load_tile = [&](int q0, int buf) {
+    const bool tail = q0 + kQB > L;
+#pragma unroll
+    for (int r = 0; r < kInstPerWave; ++r) {
+      const int row = tail ? min(q0 + ld_row[r], L - 1) : q0 + ld_row[r];
+      const size_t off = static_cast<size_t>(row) * hD + ld_off[r];
+      const int dst = buf * kTileBytes + (wave * kInstPerWave + r) * 1024;
+      __builtin_amdgcn_global_load_lds(qseg + off, sQ0 + dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(oseg + off, sO0 + dst, 16, 0, 0);
     }
-    if (threadIdx.x < kQB) {
-      const int qq = q0 + threadIdx.x;
-      const bool ok = qq < L;
-      const size_t g = static_cast<size_t>(head) * n_tokens + s0 + min(qq, L - 1);
-      lreg = ok ? lse[g] * kLog2e : INFINITY;  // rows past the end get P = 0
-      dreg = ok ? delta[g] : 0.f;
+    if (wave == 0) {
+      const int row = min(q0 + (lane & 31), L - 1);
+      __builtin_amdgcn_global_load_lds(stat_src + row, sS0 + buf * 2 * kQB * 4, 4, 0, 0);
     }
   };
-  lds_char* const sbase = (lds_char*)(smem);
-  auto lstore = [&](int buf) {
-    lds_char* sQ = sbase + buf * 2 * kTileBytes;
-    lds_char* sO = sQ + kTileBytes;
+
+  int roff[NKK];
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-      const int ci = threadIdx.x + 256 * r;
-      const int off = Tile<D>::off(ci / CH, ci % CH);
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sQ + off) = qreg[r];
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sO + off) = oreg[r];
-    }
-    if (threadIdx.x < kQB) {
-      sL[buf][threadIdx.x] = lreg;
-      sD[buf][threadIdx.x] = dreg;
-    }
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = Tile<D>::off(perm32(lane & 31), 2 * kk + hh);
+  int coff[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int col = 32 * db + 16 * (g & 1) + 4 * (l16 & 3);
+    const int row0 = 8 * hh + (l16 >> 2);
+    coff[db][0] = Tile<D>::off(row0, col >> 3) + ((col >> 2) & 1) * 8;
+    coff[db][1] = Tile<D>::off(row0 + 4, col >> 3) + ((col >> 2) & 1) * 8;
+  }
+  auto row_frag = [&](const lds_char* t, int kk) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(t + roff[kk]);
+  };
+  auto col_frag = [&](const lds_char* t, int c, int db) {
+    const lds_char* p0 = t + coff[db][0] + 16 * c * kRowBytes;
+    const lds_char* p1 = t + coff[db][1] + 16 * c * kRowBytes;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p0)));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p1)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, r);
   };
 
   f32x16 dkacc[NDB], dvacc[NDB];
@@ -152,46 +181,59 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     }
 
   const int ntiles = (L + kQB - 1) / kQB;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const bool more = j + 1 < ntiles;
-    if (more) gload((j + 1) * kQB);
-    const int buf = j & 1;
-    const lds_char* sQ = sbase + buf * 2 * kTileBytes;
-    const lds_char* sO = sQ + kTileBytes;
+  auto step = [&](int j, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    const int q0 = j * kQB;
+    const int b = j & 1;
+    if (j + 1 < ntiles) load_tile(q0 + kQB, b ^ 1);
+    const lds_char* sQ = sQ0 + b * kTileBytes;
+    const lds_char* sO = sO0 + b * kTileBytes;
+    const __attribute__((address_space(3))) float* st =
+        reinterpret_cast<const __attribute__((address_space(3))) float*>(sS0 + b * 2 * kQB * 4);
 
-    f32x16 sacc, dpacc;
+    // S = Q Kr^T; P = exp2(S * scale * log2e - lse2) (rows past the end: 0)
+    f32x16 acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sacc[i] = 0.f;
-      dpacc[i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      sacc = mfma32(lds_row_frag<D>(sQ, 0, kk, lane), kf[kk], sacc);
-      dpacc = mfma32(lds_row_frag<D>(sO, 0, kk, lane), vf[kk], dpacc);
-    }
-    bf16x8 pb[2], dsb[2];
+    for (int kk = 0; kk < NKK; ++kk) acc = mfma32(row_frag(sQ, kk), kf[kk], acc);
+    float p[16];
+    bf16x8 pb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int qq = acc_row(i, hh);
-      const float p = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, -sL[buf][qq]));
-      const float ds = p * (dpacc[i] - sD[buf][qq]);
-      pb[i >> 3][i & 7] = static_cast<__bf16>(p);
-      dsb[i >> 3][i & 7] = static_cast<__bf16>(ds);
+      p[i] = fast_exp2(__builtin_fmaf(acc[i], scale_log2, -st[qq]));
+      if constexpr (kTail) {
+        if (q0 + qq >= L) p[i] = 0.f;
+      }
+      pb[i >> 3][i & 7] = static_cast<__bf16>(p[i]);
     }
+    // dV^T += dO^T P
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dvacc[db] = mfma32(lds_col_frag<D>(sO, 16 * c, 32 * db, lane), pb[c], dvacc[db]);
-        dkacc[db] = mfma32(lds_col_frag<D>(sQ, 16 * c, 32 * db, lane), dsb[c], dkacc[db]);
-      }
-    if (more) lstore(buf ^ 1);
+      for (int db = 0; db < NDB; ++db) dvacc[db] = mfma32(col_frag(sO, c, db), pb[c], dvacc[db]);
+    // dP = dO V^T; dS = P (dP - Delta)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) acc = mfma32(row_frag(sO, kk), vf[kk], acc);
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dsb[i >> 3][i & 7] = static_cast<__bf16>(p[i] * (acc[i] - st[kQB + acc_row(i, hh)]));
+    // dK^T += Q^T dS
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dkacc[db] = mfma32(col_frag(sQ, c, db), dsb[c], dkacc[db]);
+    wait_vmem();
     __syncthreads();
-  }
+  };
+  load_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j + 1 < ntiles; ++j) step(j, std::false_type{});
+  step(ntiles - 1, std::true_type{});
 
   if (kok) {
     int2 kp = make_int2(0, 0);
@@ -214,16 +256,18 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
 template <int D, typename TOut>
 __global__ __launch_bounds__(256, 2) void dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
-    const uint16_t* __restrict__ dob, const float* __restrict__ lse, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dob, const float* __restrict__ lse2, const float* __restrict__ delta,
     TOut* __restrict__ dq, const int* __restrict__ cu, const int* __restrict__ order, const int* __restrict__ pt,
     int n_seg, int n_tokens, int heads, const int2* __restrict__ pos, const float2* __restrict__ tab, int max_pos,
     float scale, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;
-  constexpr int kTileBytes = kKT * D * 2;
-  constexpr int kLoads = kKT * CH / 256;
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // [buf][K, V]
+  constexpr int kRowBytes = D * 2;
+  constexpr int kTileBytes = kKT * kRowBytes;
+  constexpr int kRowsPerInst = 1024 / kRowBytes;
+  constexpr int kInstPerWave = kKT / kRowsPerInst / 4;
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // K tiles [2], V tiles [2]
 
   WorkItem it;
   if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
@@ -235,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
   if (qbase >= L) return;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5;
   const int qi = qbase + wave * 32 + (lane & 31);
   const bool qok = qi < L;
@@ -248,31 +292,56 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + qrow * D + e0));
     df[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dob + qrow * D + e0));
   }
-  const float lse2 = qok ? lse[static_cast<size_t>(head) * n_tokens + s0 + qi] * kLog2e : INFINITY;
-  const float dl = qok ? delta[static_cast<size_t>(head) * n_tokens + s0 + qi] : 0.f;
+  const size_t si = static_cast<size_t>(head) * n_tokens + s0 + min(qi, L - 1);
+  const float l2 = lse2[si];
+  const float dl = delta[si];
 
-  u32x4 kreg[kLoads], vreg[kLoads];
-  auto gload = [&](int k0) {
+  const size_t hD = static_cast<size_t>(heads) * D;
+  const uint16_t* kseg = kr + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
+  const uint16_t* vseg = vb + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
+  int ld_row[kInstPerWave], ld_off[kInstPerWave];
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-      const int ci = threadIdx.x + 256 * r;
-      const int kq = min(k0 + ci / CH, L - 1);
-      const size_t g = (static_cast<size_t>(s0 + kq) * heads + head) * D + (ci % CH) * 8;
-      kreg[r] = *reinterpret_cast<const u32x4*>(kr + g);
-      vreg[r] = *reinterpret_cast<const u32x4*>(vb + g);
+  for (int r = 0; r < kInstPerWave; ++r) {
+    const int inst = wave * kInstPerWave + r;
+    ld_row[r] = inst * kRowsPerInst + lane / CH;
+    ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
+  }
+  lds_char* const sK0 = (lds_char*)(smem);
+  lds_char* const sV0 = sK0 + 2 * kTileBytes;
+  auto load_tile = [&](int k0, int buf) {
+    const bool tail = k0 + kKT > L;
+#pragma unroll
+    for (int r = 0; r < kInstPerWave; ++r) {
+      const int row = tail ? min(k0 + ld_row[r], L - 1) : k0 + ld_row[r];
+      const size_t off = static_cast<size_t>(row) * hD + ld_off[r];
+      const int dst = buf * kTileBytes + (wave * kInstPerWave + r) * 1024;
+      __builtin_amdgcn_global_load_lds(kseg + off, sK0 + dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vseg + off, sV0 + dst, 16, 0, 0);
     }
   };
-  lds_char* const sbase = (lds_char*)(smem);
-  auto lstore = [&](int buf) {
-    lds_char* sK = sbase + buf * 2 * kTileBytes;
-    lds_char* sV = sK + kTileBytes;
+  int roff[NKK];
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-      const int ci = threadIdx.x + 256 * r;
-      const int off = Tile<D>::off(ci / CH, ci % CH);
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sK + off) = kreg[r];
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sV + off) = vreg[r];
-    }
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = Tile<D>::off(perm32(lane & 31), 2 * kk + hh);
+  int coff[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int col = 32 * db + 16 * (g & 1) + 4 * (l16 & 3);
+    const int row0 = 8 * hh + (l16 >> 2);
+    coff[db][0] = Tile<D>::off(row0, col >> 3) + ((col >> 2) & 1) * 8;
+    coff[db][1] = Tile<D>::off(row0 + 4, col >> 3) + ((col >> 2) & 1) * 8;
+  }
+  auto col_frag = [&](const lds_char* t, int c, int db) {
+    const lds_char* p0 = t + coff[db][0] + 16 * c * kRowBytes;
+    const lds_char* p1 = t + coff[db][1] + 16 * c * kRowBytes;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p0)));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p1)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, r);
   };
 
   f32x16 dqacc[NDB];
@@ -282,16 +351,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
   const int ntiles = (L + kKT - 1) / kKT;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
+  auto step = [&](int j, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
     const int k0 = j * kKT;
-    const bool more = j + 1 < ntiles;
-    if (more) gload(k0 + kKT);
-    const lds_char* sK = sbase + (j & 1) * 2 * kTileBytes;
-    const lds_char* sV = sK + kTileBytes;
-
+    const int b = j & 1;
+    if (j + 1 < ntiles) load_tile(k0 + kKT, b ^ 1);
+    const lds_char* sK = sK0 + b * kTileBytes;
+    const lds_char* sV = sV0 + b * kTileBytes;
     bf16x8 dsb[kKT / 16];
 #pragma unroll
     for (int kb = 0; kb < kKT / 32; ++kb) {
@@ -303,25 +369,34 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
       }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sacc = mfma32(lds_row_frag<D>(sK, kb * 32, kk, lane), qf[kk], sacc);
-        dpacc = mfma32(lds_row_frag<D>(sV, kb * 32, kk, lane), df[kk], dpacc);
+        const bf16x8 ka = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            sK + roff[kk] + kb * 32 * kRowBytes);
+        const bf16x8 va = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            sV + roff[kk] + kb * 32 * kRowBytes);
+        sacc = mfma32(ka, qf[kk], sacc);
+        dpacc = mfma32(va, df[kk], dpacc);
       }
-      const bool tail = k0 + kb * 32 + 32 > L;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, -lse2));
-        if (tail && k0 + kb * 32 + acc_row(i, hh) >= L) p = 0.f;
+        float p = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, -l2));
+        if constexpr (kTail) {
+          if (k0 + kb * 32 + acc_row(i, hh) >= L) p = 0.f;
+        }
         dsb[2 * kb + (i >> 3)][i & 7] = static_cast<__bf16>(p * (dpacc[i] - dl));
       }
     }
 #pragma unroll
     for (int c = 0; c < kKT / 16; ++c)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dqacc[db] = mfma32(lds_col_frag<D>(sK, 16 * c, 32 * db, lane), dsb[c], dqacc[db]);
-    if (more) lstore((j + 1) & 1);
+      for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(col_frag(sK, c, db), dsb[c], dqacc[db]);
+    wait_vmem();
     __syncthreads();
-  }
+  };
+  load_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j + 1 < ntiles; ++j) step(j, std::false_type{});
+  step(ntiles - 1, std::true_type{});
 
   if (qok) {
     int2 qp = make_int2(0, 0);
@@ -340,12 +415,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 }
 
 template <int D, typename T>
-hipError_t launch_delta_t(const AttnArgs& a, const void* o, const void* dout, float* delta, hipStream_t stream) {
+hipError_t launch_delta_t(const AttnArgs& a, const void* o, const void* dout, const float* lse, float* delta,
+                          float* lse2, hipStream_t stream) {
   const long long threads = static_cast<long long>(a.n_tokens) * a.n_heads * (D / 8);
   if (threads == 0) return hipSuccess;
   const long long blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((delta_kernel<D, T>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                     static_cast<const T*>(o), static_cast<const T*>(dout), delta, a.n_tokens, a.n_heads);
+                     static_cast<const T*>(o), static_cast<const T*>(dout), lse, delta, lse2, a.n_tokens, a.n_heads);
   return hipGetLastError();
 }
 
@@ -378,13 +454,13 @@ hipError_t launch_dq_t(const AttnArgs& a, const void* qr, const void* kr, const 
 
 }  // namespace
 
-hipError_t launch_attn_bwd_delta(const AttnArgs& a, const void* o, const void* dout, float* delta,
-                                 hipStream_t stream) {
+hipError_t launch_attn_bwd_delta(const AttnArgs& a, const void* o, const void* dout, const float* lse, float* delta,
+                                 float* lse2, hipStream_t stream) {
   if (a.head_dim == 128)
-    return a.dtype == kDtypeBf16 ? launch_delta_t<128, uint16_t>(a, o, dout, delta, stream)
-                                 : launch_delta_t<128, float>(a, o, dout, delta, stream);
-  return a.dtype == kDtypeBf16 ? launch_delta_t<64, uint16_t>(a, o, dout, delta, stream)
-                               : launch_delta_t<64, float>(a, o, dout, delta, stream);
+    return a.dtype == kDtypeBf16 ? launch_delta_t<128, uint16_t>(a, o, dout, lse, delta, lse2, stream)
+                                 : launch_delta_t<128, float>(a, o, dout, lse, delta, lse2, stream);
+  return a.dtype == kDtypeBf16 ? launch_delta_t<64, uint16_t>(a, o, dout, lse, delta, lse2, stream)
+                               : launch_delta_t<64, float>(a, o, dout, lse, delta, lse2, stream);
 }
 
 hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,

@@ -54,10 +54,11 @@ struct AttnArgs {
 hipError_t launch_attn_fwd(const AttnArgs& a, const void* q, const void* kr, const void* vb, void* o,
                            float* lse, hipStream_t stream);
 
-hipError_t launch_attn_bwd_delta(const AttnArgs& a, const void* o, const void* dout, float* delta,
-                                 hipStream_t stream);
+// delta = rowsum(dout * o), lse2 = lse * log2(e), both [H][N].
+hipError_t launch_attn_bwd_delta(const AttnArgs& a, const void* o, const void* dout, const float* lse, float* delta,
+                                 float* lse2, hipStream_t stream);
 
-// qr/kr rotated bf16, vb/dob bf16; outputs in a.dtype.
+// qr/kr rotated bf16, vb/dob bf16, lse2 in log2 units; outputs in a.dtype.
 hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, const void* qr, const void* kr, const void* vb,
                                 const void* dob, const float* lse, const float* delta, void* dk, void* dv,
                                 hipStream_t stream);
