@@ -3,6 +3,7 @@
 // With P = softmax(scale * Qr Kr^T) recomputed from the forward's LSE:
 //   Delta = rowsum(dO * O)                       delta kernel (HBM-bound)
 //   dV = P^T dO,  dKr = scale * dS^T Qr          dkdv kernel, per 32 keys/wave
+//                                                (K in registers, V rows in LDS)
 //   dQr = scale * dS Kr                          dq kernel,   per 32 queries/wave
 // where dS = P * (dO V^T - Delta); dQ and dK are rotated back by the inverse
 // rotation in the epilogues.  Each output element is written by exactly one
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   constexpr int kRowsPerInst = 1024 / kRowBytes;
   constexpr int kInstPerWave = kQB / kRowsPerInst / 4;
   // LDS: Q tiles [2], dO tiles [2], then per buffer 32 log2-LSE + 32 Delta
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes + 2 * 2 * kQB * 4];
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes + 2 * 2 * kQB * 4 + kKB * kRowBytes];
 
   WorkItem it;
   if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
@@ -103,13 +104,13 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   const bool kok = key < L;
   const long long krow = (static_cast<long long>(s0) + min(key, L - 1)) * heads + head;
 
-  // K and V fragments (B operands of S = Q Kr^T and dP = dO V^T).
-  bf16x8 kf[NKK], vf[NKK];
+  // K fragments in registers (B operand of S = Q Kr^T); the workgroup's V
+  // rows live in LDS and feed dP = dO V^T.
+  bf16x8 kf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const int e0 = 16 * kk + 8 * hh;
     kf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + krow * D + e0));
-    vf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vb + krow * D + e0));
   }
 
   // ---- global -> LDS copies of the Q / dO tiles and their row statistics.
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   lds_char* const sQ0 = (lds_char*)(smem);
   lds_char* const sO0 = sQ0 + 2 * kTileBytes;
   lds_char* const sS0 = sQ0 + 4 * kTileBytes;  // [buf][lse2 x 32, delta x 32]
+  lds_char* const sVb = sS0 + 2 * 2 * kQB * 4;   // V rows of this workgroup's keys
   auto load_tile = [&](int q0, int buf) {
     const bool tail = q0 + kQB > L;
 #pragma unroll
@@ -217,7 +219,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) acc = mfma32(row_frag(sO, kk), vf[kk], acc);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int vr = wave * 32 + (lane & 31);
+      const bf16x8 vfr = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          sVb + Tile<D>::off(vr, 2 * kk + hh));
+      acc = mfma32(row_frag(sO, kk), vfr, acc);
+    }
     bf16x8 dsb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) dsb[i >> 3][i & 7] = static_cast<__bf16>(p[i] * (acc[i] - st[kQB + acc_row(i, hh)]));
@@ -229,6 +236,18 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     wait_vmem();
     __syncthreads();
   };
+  {
+    const uint16_t* vseg = vb + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
+    constexpr int kVInst = kKB / kRowsPerInst / 4;
+#pragma unroll
+    for (int r = 0; r < kVInst; ++r) {
+      const int inst = wave * kVInst + r;
+      const int row = inst * kRowsPerInst + lane / CH;
+      const int chunk = (lane % CH) ^ Tile<D>::swz(row);
+      const int vrow = min(kbase + row, L - 1);
+      __builtin_amdgcn_global_load_lds(vseg + static_cast<size_t>(vrow) * hD + chunk * 8, sVb + inst * 1024, 16, 0, 0);
+    }
+  }
   load_tile(0, 0);
   wait_vmem();
   __syncthreads();
