@@ -56,8 +56,13 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   constexpr int kTileBytes = kKT * kRowBytes;
   constexpr int kRowsPerInst = 1024 / kRowBytes;  // rows one wave-wide 16-byte load covers
   constexpr int kInstPerWave = kKT / kRowsPerInst / 8;
-  // LDS: K tiles [2] then V tiles [2]
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
+  // LDS: two K and two V tiles, as four separate objects so the compiler can
+  // tell the tile being read from the tiles being filled by in-flight copies
+  // (otherwise it waits for every copy before each transpose read).
+  __shared__ __attribute__((aligned(16))) char smemK0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemK1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemV0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemV1[kTileBytes];
 
   WorkItem it;
   if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
@@ -104,8 +109,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     ld_row[r] = inst * kRowsPerInst + lane / CH;
     ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
   }
-  lds_char* const sK0 = (lds_char*)(smem);
-  lds_char* const sV0 = sK0 + 2 * kTileBytes;
+  lds_char* const sKb[2] = {(lds_char*)(smemK0), (lds_char*)(smemK1)};
+  lds_char* const sVb[2] = {(lds_char*)(smemV0), (lds_char*)(smemV1)};
   auto load_rows = [&](const uint16_t* seg, int k0, lds_char* dst) {
     const bool tail = k0 + kKT > L;
 #pragma unroll
@@ -169,24 +174,24 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   // buffer t % 2, tile t of V in V buffer t % 2.
   const int ntiles = (L + kKT - 1) / kKT;
   f32x16 scur[2], snext[2];
-  load_rows(kseg, 0, sK0);
-  load_rows(vseg, 0, sV0);
-  if (ntiles > 1) load_rows(kseg, kKT, sK0 + kTileBytes);
+  load_rows(kseg, 0, sKb[0]);
+  load_rows(vseg, 0, sVb[0]);
+  if (ntiles > 1) load_rows(kseg, kKT, sKb[1]);
   wait_vmem();
   __syncthreads();
-  s_tile(sK0, scur);
+  s_tile(sKb[0], scur);
   __syncthreads();  // every wave is done with K tile 0 before tile 2 reuses its buffer
 
   // One pipeline step: softmax + P V of tile j, scores of tile j + 1.  Only
-  // the last tile masks keys; the rescale branch is rare.  The instruction
-  // groups below keep LDS reads several MFMAs ahead of their use and spread
-  // the softmax's vector work between the matrix instructions.
-  auto step = [&](int j, auto tail_tag) {
+  // the last tile masks keys; the rescale branch is rare.
+  // b (= j % 2) and the tail flag are compile-time, so every LDS address
+  // names its buffer statically.
+  auto step = [&](int j, auto buf_tag, auto tail_tag) {
     constexpr bool kTail = decltype(tail_tag)::value;
+    constexpr int b = decltype(buf_tag)::value;
     const int k0 = j * kKT;
-    const int b = j & 1;
-    if (j + 2 < ntiles) load_rows(kseg, k0 + 2 * kKT, sK0 + b * kTileBytes);
-    if (j + 1 < ntiles) load_rows(vseg, k0 + kKT, sV0 + (b ^ 1) * kTileBytes);
+    if (j + 2 < ntiles) load_rows(kseg, k0 + 2 * kKT, sKb[b]);
+    if (j + 1 < ntiles) load_rows(vseg, k0 + kKT, sVb[b ^ 1]);
     if constexpr (kTail) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -225,8 +230,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
       }
     // Scores of tile j + 1 (for the last tile they read a stale buffer and
     // are discarded).
-    s_tile(sK0 + (b ^ 1) * kTileBytes, snext);
-    const lds_char* sV = sV0 + b * kTileBytes;
+    s_tile(sKb[b ^ 1], snext);
+    const lds_char* sV = sVb[b];
 #pragma unroll
     for (int c = 0; c < kKT / 16; ++c)
 #pragma unroll
@@ -236,8 +241,19 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     wait_vmem();
     __syncthreads();
   };
-  for (int j = 0; j + 1 < ntiles; ++j) step(j, std::false_type{});
-  step(ntiles - 1, std::true_type{});
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int j = 0;
+  for (; j + 2 < ntiles; j += 2) {
+    step(j, B0{}, std::false_type{});
+    step(j + 1, B1{}, std::false_type{});
+  }
+  if (ntiles - j == 2) {
+    step(j, B0{}, std::false_type{});
+    step(j + 1, B1{}, std::true_type{});
+  } else {
+    step(j, B0{}, std::true_type{});
+  }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qok) {
