@@ -43,31 +43,65 @@ __device__ __forceinline__ void rotate4(float (&x)[4], int d0, int prow, int pco
   }
 }
 
+// Delta[h][t] = dot(dO[t][h], O[t][h]) and the log2-scaled LSE, for a tile of
+// kDeltaTokens tokens x kDeltaHeads heads per workgroup.  The rows of one token
+// are contiguous in O and dO, so the loads are coalesced 16-byte reads, four
+// rows in flight per lane; the dot products go through LDS and leave as
+// kDeltaTokens consecutive floats per head (the outputs are head-major).
+constexpr int kDeltaTokens = 32;
+constexpr int kDeltaHeads = 8;
+constexpr int kDeltaUnroll = 4;
+
 template <int D, typename T>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
                                                     const float* __restrict__ lse, float* __restrict__ delta,
                                                     float* __restrict__ lse2, int n_tokens, int heads) {
   constexpr int kLanesPerRow = D / 8;
-  const long long rows = static_cast<long long>(n_tokens) * heads;
-  const long long gid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const long long row = gid / kLanesPerRow;
-  const int sub = static_cast<int>(gid % kLanesPerRow);
-  float acc = 0.f;
-  if (row < rows) {
-    float a[8], b[8];
-    load8<T>(o + row * D + sub * 8, a);
-    load8<T>(dout + row * D + sub * 8, b);
+  constexpr int kRowsPerPass = 256 / kLanesPerRow;
+  constexpr int kRows = kDeltaTokens * kDeltaHeads;
+  static_assert(kRows % (kRowsPerPass * kDeltaUnroll) == 0, "whole unrolled passes");
+  __shared__ float sDot[kDeltaHeads][kDeltaTokens + 1];
+  const int t0 = blockIdx.x * kDeltaTokens;
+  const int h0 = blockIdx.y * kDeltaHeads;
+  const int hc = min(kDeltaHeads, heads - h0);
+  const int sub = threadIdx.x % kLanesPerRow;
+  for (int r0 = threadIdx.x / kLanesPerRow; r0 < kRows; r0 += kRowsPerPass * kDeltaUnroll) {
+    float a[kDeltaUnroll][8], b[kDeltaUnroll][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc += a[j] * b[j];
+    for (int u = 0; u < kDeltaUnroll; ++u) {
+      const int r = r0 + u * kRowsPerPass;
+      const int hl = r % kDeltaHeads;
+      const int t = t0 + r / kDeltaHeads;
+      if (hl < hc && t < n_tokens) {
+        const long long row = static_cast<long long>(t) * heads + h0 + hl;
+        load8<T>(o + row * D + sub * 8, a[u]);
+        load8<T>(dout + row * D + sub * 8, b[u]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[u][j] = b[u][j] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDeltaUnroll; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += a[u][j] * b[u][j];
+#pragma unroll
+      for (int m = kLanesPerRow / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+      const int r = r0 + u * kRowsPerPass;
+      if (sub == 0) sDot[r % kDeltaHeads][r / kDeltaHeads] = acc;
+    }
   }
-#pragma unroll
-  for (int m = kLanesPerRow / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && sub == 0) {
-    const long long t = row / heads;
-    const int h = static_cast<int>(row % heads);
-    const size_t i = static_cast<size_t>(h) * n_tokens + t;
-    delta[i] = acc;
-    lse2[i] = lse[i] * kLog2e;
+  __syncthreads();
+  for (int e = threadIdx.x; e < kRows; e += 256) {
+    const int hl = e / kDeltaTokens;
+    const int tl = e % kDeltaTokens;
+    const int t = t0 + tl;
+    if (hl < hc && t < n_tokens) {
+      const size_t i = static_cast<size_t>(h0 + hl) * n_tokens + t;
+      delta[i] = sDot[hl][tl];
+      lse2[i] = lse[i] * kLog2e;
+    }
   }
 }
 
@@ -436,10 +470,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 template <int D, typename T>
 hipError_t launch_delta_t(const AttnArgs& a, const void* o, const void* dout, const float* lse, float* delta,
                           float* lse2, hipStream_t stream) {
-  const long long threads = static_cast<long long>(a.n_tokens) * a.n_heads * (D / 8);
-  if (threads == 0) return hipSuccess;
-  const long long blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL((delta_kernel<D, T>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+  if (a.n_tokens == 0 || a.n_heads == 0) return hipSuccess;
+  const dim3 grid((a.n_tokens + kDeltaTokens - 1) / kDeltaTokens, (a.n_heads + kDeltaHeads - 1) / kDeltaHeads);
+  if (grid.y > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((delta_kernel<D, T>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(o), static_cast<const T*>(dout), lse, delta, lse2, a.n_tokens, a.n_heads);
   return hipGetLastError();
 }
