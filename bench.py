@@ -271,6 +271,19 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    # Clock-limited ceiling: sustained matrix-instruction rate on operands with
+    # the inputs' distribution, and the shader clock meanwhile (after timing).
+    probe_ops = torch.from_numpy(
+        workloads.normal(w.seed, 9, (mf.PROBE_VECTORS * 8,), "bf16").view(np.int16)).to(dev).view(torch.bfloat16)
+    probe_blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    mf.mfma_probe(probe_ops, probe_blocks, 20000)
+    probe = mf.mfma_probe(probe_ops, probe_blocks, 400000)
+    result["mfma_probe"] = {"tflops": round(probe["tflops"], 1), "sclk_mhz": round(probe["sclk_mhz"]),
+                            "ms": round(probe["ms"], 2),
+                            "operands": "seeded N(0,1) bf16; 32x32x16 bf16 MFMA, 2 waves per SIMD"}
+    if roof["unit"] == "TFLOP/s":
+        roof["peak_measured"] = round(probe["tflops"], 1)
+        roof["frac_measured"] = round(roof["achieved"] / probe["tflops"], 4)
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

@@ -219,6 +219,33 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
                              int32_t head_dim, float softmax_scale, void* workspace,
                              size_t workspace_bytes, void* stream, mf_trace* trace);
 
+/*
+ * mf_mfma_probe -- measurement helper, not a step of the path: the sustained
+ * rate of the 32x32x16 bf16 matrix instruction on the caller's operand values
+ * and the shader clock meanwhile.  Throughput figures of the attention
+ * kernels are quoted against the datasheet peak, which assumes the top
+ * clock; this call measures what the chip sustains under a full matrix load
+ * with realistic data, where power limits lower the clock.
+ *
+ * operands     device, 4096 vectors of 8 bf16 (64 KiB), 16-byte aligned, in;
+ *              wave lanes cycle through them as A and B fragments.
+ * n_blocks     workgroups of 256 threads (4 waves), 1 .. 2^20.
+ * iters        loop trips; each wave issues 4 * iters instructions of
+ *              32 * 32 * 16 * 2 = 32768 flops each, so the launch performs
+ *              n_blocks * 4 * 4 * iters * 32768 flops.
+ * sink         device float[n_blocks * 256], out: accumulator sums (keeps
+ *              the work observable; the values carry no meaning).
+ * clocks       device uint64[2 * n_blocks], out: per workgroup, shader-clock
+ *              ticks and wall-clock ticks between its first and last
+ *              instruction.
+ * wall_clock_khz  host int32*, out (may be NULL): the wall counter's rate,
+ *              written before the call returns.
+ * Returns MF_ERR_INVALID_ARG for a NULL or misaligned pointer or a size out
+ * of range, MF_ERR_HIP if the launch fails.
+ */
+mf_status mf_mfma_probe(const void* operands, int32_t n_blocks, int32_t iters, float* sink,
+                        uint64_t* clocks, int32_t* wall_clock_khz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ MF_F32 = 1
 EXPORTED = (
     "mf_status_string", "mf_abi_version", "mf_pack", "mf_rope2d_workspace_size",
     "mf_rope2d_apply", "mf_varlen_attn_workspace_size", "mf_varlen_attn_fwd",
-    "mf_varlen_attn_bwd",
+    "mf_varlen_attn_bwd", "mf_mfma_probe",
 )
 
 
@@ -117,6 +117,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mf_varlen_attn_bwd.restype = _i32
     lib.mf_varlen_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                        _vp, _dbl, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp, _vp]
+    lib.mf_mfma_probe.restype = _i32
+    lib.mf_mfma_probe.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp]
     _lib = lib
     return lib
 
@@ -228,3 +230,12 @@ def mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, n_segments
                                   int(workspace.numel() * workspace.element_size()), _stream(stream),
                                   _trace(trace))
     _check(st, "mf_varlen_attn_bwd")
+
+
+def mf_mfma_probe(operands: torch.Tensor, n_blocks: int, iters: int, sink: torch.Tensor, clocks: torch.Tensor,
+                  stream=None) -> int:
+    """Enqueue the matrix-instruction probe; returns the wall counter's rate in kHz."""
+    khz = ctypes.c_int32(0)
+    _check(lib().mf_mfma_probe(_ptr(operands), int(n_blocks), int(iters), _ptr(sink), _ptr(clocks),
+                               ctypes.byref(khz), _stream(stream)), "mf_mfma_probe")
+    return int(khz.value)

@@ -87,3 +87,31 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     B.mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nseg, max_seqlen, pos, theta, max_pos,
                          softmax_scale, workspace, stream, trace)
     return dq, dk, dv
+
+
+PROBE_VECTORS = 4096  # bf16x8 operand vectors mf_mfma_probe reads
+
+
+def mfma_probe(operands: torch.Tensor, n_blocks: int, iters: int) -> dict:
+    """Sustained bf16 matrix-instruction rate on ``operands`` and the shader clock.
+
+    ``operands`` is a bf16 device tensor of PROBE_VECTORS * 8 elements.  One
+    launch of ``n_blocks`` 256-thread workgroups, timed with events on the
+    current stream (synchronises).  Returns flops, milliseconds, TFLOP/s and
+    the mean shader clock in MHz over the workgroups.
+    """
+    if operands.dtype != torch.bfloat16 or operands.numel() != PROBE_VECTORS * 8:
+        raise ValueError(f"operands must be {PROBE_VECTORS * 8} bf16 values")
+    sink = torch.empty(n_blocks * 256, dtype=torch.float32, device=operands.device)
+    clocks = torch.empty(2 * n_blocks, dtype=torch.int64, device=operands.device)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    khz = B.mf_mfma_probe(operands, n_blocks, iters, sink, clocks)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    c = clocks.view(n_blocks, 2).cpu().double()
+    sclk_mhz = float(c[:, 0].sum() / c[:, 1].sum()) * khz / 1000.0
+    flops = float(n_blocks) * 4 * 4 * iters * 32768
+    return {"flops": flops, "ms": ms, "tflops": flops / ms / 1e9, "sclk_mhz": sclk_mhz}

@@ -128,3 +128,14 @@ def test_workspace_sizes(lib):
     assert fwd_bf16 % 256 == 0 and bwd_bf16 % 256 == 0
     assert lib.mf_varlen_attn_workspace_size(n, h, 96, 3, 640, 0, 0) == 0
     assert lib.mf_rope2d_workspace_size(128, 640) == table
+
+
+def test_probe_argument_errors(lib):
+    khz = ctypes.c_int32(0)
+    assert lib.mf_mfma_probe(None, 4, 10, FAKE, FAKE, ctypes.byref(khz), None) == -1
+    assert lib.mf_mfma_probe(FAKE, 0, 10, FAKE, FAKE, ctypes.byref(khz), None) == -1
+    assert lib.mf_mfma_probe(FAKE, 4, 0, FAKE, FAKE, ctypes.byref(khz), None) == -1
+    assert lib.mf_mfma_probe(FAKE, (1 << 20) + 1, 10, FAKE, FAKE, ctypes.byref(khz), None) == -1
+    assert lib.mf_mfma_probe(FAKE + 8, 4, 10, FAKE, FAKE, ctypes.byref(khz), None) == -1  # operands misaligned
+    assert lib.mf_mfma_probe(FAKE, 4, 10, FAKE, FAKE + 4, ctypes.byref(khz), None) == -1  # clocks misaligned
+    assert lib.mf_mfma_probe(FAKE, 4, 10, None, FAKE, ctypes.byref(khz), None) == -1
