@@ -56,13 +56,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   constexpr int kTileBytes = kKT * kRowBytes;
   constexpr int kRowsPerInst = 1024 / kRowBytes;  // rows one wave-wide 16-byte load covers
   constexpr int kInstPerWave = kKT / kRowsPerInst / 8;
-  // LDS: two K and two V tiles, as four separate objects so the compiler can
-  // tell the tile being read from the tiles being filled by in-flight copies
-  // (otherwise it waits for every copy before each transpose read).
+  // LDS: three K and three V tiles, as six separate objects so the compiler
+  // can tell the tile being read from the tiles being filled by in-flight
+  // copies (otherwise it waits for every copy before each transpose read).
   __shared__ __attribute__((aligned(16))) char smemK0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char smemK1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemK2[kTileBytes];
   __shared__ __attribute__((aligned(16))) char smemV0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char smemV1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemV2[kTileBytes];
 
   WorkItem it;
   if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
@@ -109,8 +111,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     ld_row[r] = inst * kRowsPerInst + lane / CH;
     ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
   }
-  lds_char* const sKb[2] = {(lds_char*)(smemK0), (lds_char*)(smemK1)};
-  lds_char* const sVb[2] = {(lds_char*)(smemV0), (lds_char*)(smemV1)};
+  lds_char* const sKb[3] = {(lds_char*)(smemK0), (lds_char*)(smemK1), (lds_char*)(smemK2)};
+  lds_char* const sVb[3] = {(lds_char*)(smemV0), (lds_char*)(smemV1), (lds_char*)(smemV2)};
   auto load_rows = [&](const uint16_t* seg, int k0, lds_char* dst) {
     const bool tail = k0 + kKT > L;
 #pragma unroll
@@ -170,9 +172,13 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
   // Pipeline: K runs one tile ahead of V, so the scores of tile j+1 are
-  // computed while the softmax of tile j runs.  Tile t of K lives in K
-  // buffer t % 2, tile t of V in V buffer t % 2.
+  // computed while the softmax of tile j runs, and the copies run two steps
+  // ahead of their use.  Tile t of K lives in K buffer t % 3, tile t of V in
+  // V buffer t % 3.  Step j issues the copies of K tile j+3 and V tile j+2
+  // and, at its end, waits only for the copies issued before it (K tile j+2,
+  // V tile j+1), leaving its own in flight across the next step.
   const int ntiles = (L + kKT - 1) / kKT;
+  const int last_k0 = (ntiles - 1) * kKT;
   f32x16 scur[2], snext[2];
   load_rows(kseg, 0, sKb[0]);
   load_rows(vseg, 0, sVb[0]);
@@ -180,18 +186,23 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   wait_vmem();
   __syncthreads();
   s_tile(sKb[0], scur);
-  __syncthreads();  // every wave is done with K tile 0 before tile 2 reuses its buffer
+  if (ntiles > 2) load_rows(kseg, 2 * kKT, sKb[2]);
+  if (ntiles > 1) load_rows(vseg, kKT, sVb[1]);
+  __syncthreads();  // every wave is done with K tile 0 before tile 3 reuses its buffer
 
   // One pipeline step: softmax + P V of tile j, scores of tile j + 1.  Only
   // the last tile masks keys; the rescale branch is rare.
-  // b (= j % 2) and the tail flag are compile-time, so every LDS address
+  // b (= j % 3) and the tail flag are compile-time, so every LDS address
   // names its buffer statically.
   auto step = [&](int j, auto buf_tag, auto tail_tag) {
     constexpr bool kTail = decltype(tail_tag)::value;
     constexpr int b = decltype(buf_tag)::value;
     const int k0 = j * kKT;
-    if (j + 2 < ntiles) load_rows(kseg, k0 + 2 * kKT, sKb[b]);
-    if (j + 1 < ntiles) load_rows(vseg, k0 + kKT, sVb[b ^ 1]);
+    // Every step issues both copies, so the wait below has a fixed count;
+    // past the end they re-read the last tile into buffers no later step
+    // reads.
+    load_rows(kseg, min(k0 + 3 * kKT, last_k0), sKb[b]);
+    load_rows(vseg, min(k0 + 2 * kKT, last_k0), sVb[(b + 2) % 3]);
     if constexpr (kTail) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -230,7 +241,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
       }
     // Scores of tile j + 1 (for the last tile they read a stale buffer and
     // are discarded).
-    s_tile(sKb[b ^ 1], snext);
+    s_tile(sKb[(b + 1) % 3], snext);
     const lds_char* sV = sVb[b];
 #pragma unroll
     for (int c = 0; c < kKT / 16; ++c)
@@ -238,22 +249,30 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(col_frag(sV, c, db), pf[c], oacc[db]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) scur[kb] = snext[kb];
-    wait_vmem();
-    __syncthreads();
+    // Wait for everything but this step's own copies (they complete in order).
+    wait_vmem_keep<2 * kInstPerWave>();
+    barrier_keep_loads();
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   int j = 0;
-  for (; j + 2 < ntiles; j += 2) {
+  for (; j + 3 < ntiles; j += 3) {
     step(j, B0{}, std::false_type{});
     step(j + 1, B1{}, std::false_type{});
+    step(j + 2, B2{}, std::false_type{});
   }
-  if (ntiles - j == 2) {
+  if (ntiles - j == 3) {
+    step(j, B0{}, std::false_type{});
+    step(j + 1, B1{}, std::false_type{});
+    step(j + 2, B2{}, std::true_type{});
+  } else if (ntiles - j == 2) {
     step(j, B0{}, std::false_type{});
     step(j + 1, B1{}, std::true_type{});
   } else {
     step(j, B0{}, std::true_type{});
   }
+  wait_vmem();  // the last step's copies land before the workgroup's LDS is released
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qok) {

@@ -140,6 +140,25 @@ __device__ __forceinline__ void tile_load_async(lds_char* tile, int wave, int la
 // have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's global loads are outstanding.  Loads
+// complete in issue order, so this waits for all but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 16, "vmcnt field holds 0..15 here");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier that leaves this wave's newest loads into LDS in flight.
+// __syncthreads() fences memory, and its fence waits for every outstanding
+// copy into LDS; here the caller has already waited (wait_vmem_keep) for the
+// copies other waves will read next.  This waits for the wave's own LDS
+// accesses, then synchronises; the memory clobber keeps the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // One unit of attention work: a tile of one (segment, head).
 struct WorkItem {
   int seg, head, tile;
