@@ -191,11 +191,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   __syncthreads();  // every wave is done with K tile 0 before tile 3 reuses its buffer
 
   // One pipeline step: softmax + P V of tile j, scores of tile j + 1.  Only
-  // the last tile masks keys; the rescale branch is rare.
-  // b (= j % 3) and the tail flag are compile-time, so every LDS address
-  // names its buffer statically.
-  auto step = [&](int j, auto buf_tag, auto tail_tag) {
-    constexpr bool kTail = decltype(tail_tag)::value;
+  // the last tile masks keys; that branch and the rescale branch are rare.
+  // b (= j % 3) is compile-time, so every LDS address names its buffer
+  // statically.
+  auto step = [&](int j, auto buf_tag) {
     constexpr int b = decltype(buf_tag)::value;
     const int k0 = j * kKT;
     // Every step issues both copies, so the wait below has a fixed count;
@@ -203,7 +202,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     // reads.
     load_rows(kseg, min(k0 + 3 * kKT, last_k0), sKb[b]);
     load_rows(vseg, min(k0 + 2 * kKT, last_k0), sVb[(b + 2) % 3]);
-    if constexpr (kTail) {
+    if (k0 + kKT > L) {  // only the segment's last tile holds keys past its end
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -257,20 +256,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   using B1 = std::integral_constant<int, 1>;
   using B2 = std::integral_constant<int, 2>;
   int j = 0;
-  for (; j + 3 < ntiles; j += 3) {
-    step(j, B0{}, std::false_type{});
-    step(j + 1, B1{}, std::false_type{});
-    step(j + 2, B2{}, std::false_type{});
+  for (; j + 3 <= ntiles; j += 3) {
+    step(j, B0{});
+    step(j + 1, B1{});
+    step(j + 2, B2{});
   }
-  if (ntiles - j == 3) {
-    step(j, B0{}, std::false_type{});
-    step(j + 1, B1{}, std::false_type{});
-    step(j + 2, B2{}, std::true_type{});
-  } else if (ntiles - j == 2) {
-    step(j, B0{}, std::false_type{});
-    step(j + 1, B1{}, std::true_type{});
-  } else {
-    step(j, B0{}, std::true_type{});
+  if (j < ntiles) {
+    step(j, B0{});
+    if (j + 1 < ntiles) step(j + 1, B1{});
   }
   wait_vmem();  // the last step's copies land before the workgroup's LDS is released
 
