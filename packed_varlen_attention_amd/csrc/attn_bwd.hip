@@ -217,8 +217,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     }
 
   const int ntiles = (L + kQB - 1) / kQB;
-  auto step = [&](int j, auto tail_tag) {
-    constexpr bool kTail = decltype(tail_tag)::value;
+  auto step = [&](int j) {
     const int q0 = j * kQB;
     const int b = j & 1;
     if (j + 1 < ntiles) load_tile(q0 + kQB, b ^ 1);
@@ -234,21 +233,16 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) acc = mfma32(row_frag(sQ, kk), kf[kk], acc);
     float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(acc[i], scale_log2, -st[acc_row(i, hh)]));
+    if (q0 + kQB > L) {  // only the segment's last tile holds rows past its end
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (q0 + acc_row(i, hh) >= L) p[i] = 0.f;
+    }
     bf16x8 pb[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qq = acc_row(i, hh);
-      p[i] = fast_exp2(__builtin_fmaf(acc[i], scale_log2, -st[qq]));
-      if constexpr (kTail) {
-        if (q0 + qq >= L) p[i] = 0.f;
-      }
-      pb[i >> 3][i & 7] = static_cast<__bf16>(p[i]);
-    }
-    // dV^T += dO^T P
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) dvacc[db] = mfma32(col_frag(sO, c, db), pb[c], dvacc[db]);
+    for (int i = 0; i < 16; ++i) pb[i >> 3][i & 7] = static_cast<__bf16>(p[i]);
     // dP = dO V^T; dS = P (dP - Delta)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
@@ -262,6 +256,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     bf16x8 dsb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) dsb[i >> 3][i & 7] = static_cast<__bf16>(p[i] * (acc[i] - st[kQB + acc_row(i, hh)]));
+    // dV^T += dO^T P.  The transpose reads come last in the step: the compiler
+    // waits for the next tile's copies before the first of them.
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dvacc[db] = mfma32(col_frag(sO, c, db), pb[c], dvacc[db]);
     // dK^T += Q^T dS
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -285,8 +285,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   load_tile(0, 0);
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j + 1 < ntiles; ++j) step(j, std::false_type{});
-  step(ntiles - 1, std::true_type{});
+  for (int j = 0; j < ntiles; ++j) step(j);
 
   if (kok) {
     int2 kp = make_int2(0, 0);
@@ -404,8 +403,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
   const int ntiles = (L + kKT - 1) / kKT;
-  auto step = [&](int j, auto tail_tag) {
-    constexpr bool kTail = decltype(tail_tag)::value;
+  auto step = [&](int j) {
     const int k0 = j * kKT;
     const int b = j & 1;
     if (j + 1 < ntiles) load_tile(k0 + kKT, b ^ 1);
@@ -429,14 +427,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
         sacc = mfma32(ka, qf[kk], sacc);
         dpacc = mfma32(va, df[kk], dpacc);
       }
+      float p[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, -l2));
-        if constexpr (kTail) {
-          if (k0 + kb * 32 + acc_row(i, hh) >= L) p = 0.f;
-        }
-        dsb[2 * kb + (i >> 3)][i & 7] = static_cast<__bf16>(p * (dpacc[i] - dl));
+      for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, -l2));
+      if (k0 + kKT > L) {  // only the segment's last tile holds keys past its end
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (k0 + kb * 32 + acc_row(i, hh) >= L) p[i] = 0.f;
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dsb[2 * kb + (i >> 3)][i & 7] = static_cast<__bf16>(p[i] * (dpacc[i] - dl));
     }
 #pragma unroll
     for (int c = 0; c < kKT / 16; ++c)
@@ -448,8 +448,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
   load_tile(0, 0);
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j + 1 < ntiles; ++j) step(j, std::false_type{});
-  step(ntiles - 1, std::true_type{});
+  for (int j = 0; j < ntiles; ++j) step(j);
 
   if (qok) {
     int2 qp = make_int2(0, 0);
