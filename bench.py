@@ -54,9 +54,12 @@ def parse_args():
 
 
 def source_digest(name: str) -> str:
-    path = os.path.join(ROOT, "packed_varlen_attention_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of a kernel's source file together with the device headers it includes."""
+    h = hashlib.sha256()
+    for part in (name, "mf_device.h", "mf_kernels.h"):
+        with open(os.path.join(ROOT, "packed_varlen_attention_amd", "csrc", part), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_bytes(name: str, n: int, h: int, d: int, n_samples: int) -> float:
@@ -64,8 +67,8 @@ def kernel_bytes(name: str, n: int, h: int, d: int, n_samples: int) -> float:
     t = n * h * d * 2
     if name in ("rope_q", "rope_k"):
         return 2.0 * t + 8.0 * n
-    if name == "attn_bwd_delta":
-        return 2.0 * t + 4.0 * n * h
+    if name == "attn_bwd_delta":  # read O, dO, LSE; write Delta and log2-scaled LSE
+        return 2.0 * t + 12.0 * n * h
     if name == "pack_fill":
         return 2.0 * n * ROW_BYTES + 8.0 * n
     if name == "pack_scan":
