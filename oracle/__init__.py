@@ -18,7 +18,11 @@ Sources (the Mage-Flow pages):
   variable-length attention kernels -- same sections;
 * packed classifier-free guidance: conditional and unconditional branches are
   independent segments of one pass -- paper section 3.2.1; hyper.ai summary,
-  "Experiment".
+  "Experiment";
+* editing: text, source-image and target-image tokens of one sample in one
+  segment, with a frame-aware 3D rotary embedding that tells source from
+  target -- paper section 3.2.2 "Conditioning and rectified-flow training"
+  (hyper.ai summary); paperlayer.ai summary, "Method".
 
 The pages fix no formula for the rotation, the position assignment, the
 softmax scale or the log-sum-exp.  The readings taken here are listed in each
@@ -27,6 +31,6 @@ module's docstring.
 Pins: every function is checked by ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force and library routines (see those files).
 """
-from .pack import pack, positions, gather  # noqa: F401
-from .rope import inv_freq, rope2d  # noqa: F401
+from .pack import pack, positions, gather, pack_edit, positions_edit, gather_edit  # noqa: F401
+from .rope import inv_freq, rope2d, rope3d, rope_axes, blocks3d  # noqa: F401
 from .attention import attn_fwd, attn_bwd, attn_fwd_rows  # noqa: F401

@@ -14,7 +14,8 @@ evaluates, one (segment, head) at a time, in float64.
 Readings taken where the pages are silent:
 * attention is non-causal inside a segment and absent across segments;
 * RoPE (``oracle.rope``) is applied to Q and K before the scores; V is not
-  rotated;
+  rotated.  Positions with two components (row, col) take the 2D rotation,
+  positions with three (row, col, frame) the frame-aware 3D rotation;
 * softmax scale defaults to 1/sqrt(head_dim);
 * LSE is the natural log of the row's sum of exp(scaled scores), laid out
   [H][N];
@@ -31,7 +32,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
 
-from .rope import rope2d
+from .rope import rope_axes
 
 
 def _segments(cu_seqlens: Sequence[int]):
@@ -44,7 +45,7 @@ def _rotated(x: np.ndarray, pos: Optional[np.ndarray], theta: float) -> np.ndarr
     x = np.asarray(x, dtype=np.float64)
     if pos is None:
         return x
-    return rope2d(x, pos, theta)
+    return rope_axes(x, pos, theta)
 
 
 def _scale(head_dim: int, scale: Optional[float]) -> float:
@@ -163,4 +164,4 @@ def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
                 dkr[a:b, h, :] += sc * (ds.T @ qq)
     if pos is None:
         return dqr, dkr, dv
-    return rope2d(dqr, pos, theta, inverse=True), rope2d(dkr, pos, theta, inverse=True), dv
+    return rope_axes(dqr, pos, theta, inverse=True), rope_axes(dkr, pos, theta, inverse=True), dv

@@ -110,3 +110,89 @@ def gather(text_rows: Sequence[np.ndarray], image_rows: Sequence[np.ndarray],
     if not parts:
         return np.zeros((0, 0), dtype=np.uint8)
     return np.concatenate(parts, axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Editing samples: [text | source image | target image]
+# ---------------------------------------------------------------------------
+#
+# For editing, the conditioning tokens are followed by the source image's
+# latents and then the noisy target latents (Mage-Flow paper section 3.2.2
+# "Conditioning and rectified-flow training", hyper.ai summary), and the
+# visual tokens carry (h, w, f) positions whose frame tells source from
+# target while the spatial positions correspond (same section).  Readings
+# taken where the pages are silent:
+# * one editing sample is one joint segment [text | source | target]; source
+#   and target share the sample's latent grid (an edit keeps the image size);
+# * positions (row, col, frame): text token u -> (u, u, u); source token
+#   (r, c) -> (T + r, T + c, T); target token (r, c) -> (T + r, T + c, T + 1),
+#   i.e. the 2D convention with the frame axis starting after the text too;
+# * the budget policy is the same longest order-preserving prefix.
+
+def _edit_lengths(samples: Sequence[Tuple[int, int, int]]) -> List[int]:
+    return [t + 2 * (l - t) for t, l in zip((int(s[0]) for s in samples), _lengths(samples))]
+
+
+def pack_edit(samples: Sequence[Tuple[int, int, int]], budget: int) -> Dict[str, object]:
+    """Pack the longest prefix of editing ``samples`` (text_len, grid_h, grid_w) that fits ``budget``.
+
+    Same fields as :func:`pack`, except
+      cu_pieces   int32 [3 n_packed + 1]: per sample its start, the end of its
+                  text and the end of its source image; then N;
+      max_pos     1 + largest position coordinate over all three axes.
+    """
+    lengths = _edit_lengths(samples)
+    n = 0
+    total = 0
+    for length in lengths:
+        if total + length > budget:
+            break
+        total += length
+        n += 1
+    cu = [0]
+    pieces = []
+    max_pos = 0
+    for i in range(n):
+        t, gh, gw = (int(v) for v in samples[i])
+        pieces += [cu[i], cu[i] + t, cu[i] + t + gh * gw]
+        cu.append(cu[i] + lengths[i])
+        if t > 0:
+            max_pos = max(max_pos, t)                        # text positions 0..t-1
+        if gh > 0 and gw > 0:
+            max_pos = max(max_pos, t + max(gh, gw), t + 2)   # rows/cols up to t+max-1, frames t, t+1
+    pieces.append(cu[n])
+    return {
+        "n_packed": n,
+        "n_tokens": cu[n],
+        "cu_seqlens": np.array(cu, dtype=np.int32),
+        "cu_pieces": np.array(pieces, dtype=np.int32),
+        "max_seqlen": max(lengths[:n], default=0),
+        "max_pos": max_pos,
+    }
+
+
+def positions_edit(samples: Sequence[Tuple[int, int, int]], n_packed: int) -> np.ndarray:
+    """Per-token (row, col, frame) of the first ``n_packed`` editing samples; int32 [N][3]."""
+    rows = []
+    for i in range(n_packed):
+        t, gh, gw = (int(v) for v in samples[i])
+        for u in range(t):
+            rows.append((u, u, u))
+        for f in (0, 1):  # source, then target
+            for r in range(gh):
+                for c in range(gw):
+                    rows.append((t + r, t + c, t + f))
+    return np.array(rows, dtype=np.int32).reshape(-1, 3)
+
+
+def gather_edit(text_rows: Sequence[np.ndarray], source_rows: Sequence[np.ndarray],
+                target_rows: Sequence[np.ndarray], n_packed: int) -> np.ndarray:
+    """Concatenate each packed sample's text, source-image and target-image rows, bit for bit."""
+    parts = []
+    for i in range(n_packed):
+        for a in (text_rows[i], source_rows[i], target_rows[i]):
+            a = np.asarray(a)
+            parts.append(a.reshape(-1, a.shape[-1]))
+    if not parts:
+        return np.zeros((0, 0), dtype=np.uint8)
+    return np.concatenate(parts, axis=0)
