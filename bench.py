@@ -44,8 +44,9 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mixed50k", choices=["mixed50k", "cfg1024", "stress"],
-                    help="bench line workload (mixed50k is the metric's; others for exploration)")
+    ap.add_argument("--workload", default="mixed50k", choices=["mixed50k", "cfg1024", "stress", "edit50k"],
+                    help="bench line workload (mixed50k is the metric's; others for exploration; edit50k runs "
+                         "the editing path with frame-aware 3D RoPE)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU timing")
     ap.add_argument("--cpu-threads", type=int, default=16, help="BLAS threads for the oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -62,15 +63,16 @@ def source_digest(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_bytes(name: str, n: int, h: int, d: int, n_samples: int) -> float:
-    """Algorithmic HBM bytes of the memory-bound kernels (per launch)."""
+def kernel_bytes(name: str, n: int, h: int, d: int, n_samples: int, pos_bytes: int = 8) -> float:
+    """Algorithmic HBM bytes of the memory-bound kernels (per launch); pos_bytes
+    is 8 for (row, col) positions, 12 for (row, col, frame)."""
     t = n * h * d * 2
     if name in ("rope_q", "rope_k"):
-        return 2.0 * t + 8.0 * n
+        return 2.0 * t + pos_bytes * n
     if name == "attn_bwd_delta":  # read O, dO, LSE; write Delta and log2-scaled LSE
         return 2.0 * t + 12.0 * n * h
     if name == "pack_fill":
-        return 2.0 * n * ROW_BYTES + 8.0 * n
+        return 2.0 * n * ROW_BYTES + pos_bytes * n
     if name == "pack_scan":
         return 12.0 * n_samples + 4.0 * (3 * n_samples + 2) + 16
     return 0.0
@@ -142,26 +144,32 @@ def main():
 
     torch.cuda.set_device(0)
     w = {"mixed50k": lambda: workloads.mixed50k(backward=True), "cfg1024": workloads.cfg1024,
-         "stress": workloads.stress}[args.workload]()
+         "stress": workloads.stress, "edit50k": workloads.edit50k}[args.workload]()
     samples = list(w.samples)
     H, D = w.n_heads, w.head_dim
     dev = torch.device("cuda", 0)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed)
 
-    # Per-sample hidden rows (text, then row-major image grid) to gather.
+    # Per-sample hidden rows (text, then row-major image grid; for editing,
+    # text, source grid, target grid) to gather.
     t_samples = torch.tensor(np.asarray(samples, dtype=np.int32)).to(dev)
-    bufs, tptr, iptr = [], [], []
+    bufs, ptrs = [], ([], [], [])
     for (t, gh, gw) in samples:
-        tb = torch.randn((max(t, 1), ROW_BYTES // 2), generator=gen, device=dev, dtype=torch.bfloat16)
-        ib = torch.randn((max(gh * gw, 1), ROW_BYTES // 2), generator=gen, device=dev, dtype=torch.bfloat16)
-        bufs += [tb, ib]
-        tptr.append(tb.data_ptr())
-        iptr.append(ib.data_ptr())
-    t_tptr = torch.tensor(tptr, dtype=torch.int64, device=dev)
-    t_iptr = torch.tensor(iptr, dtype=torch.int64, device=dev)
+        parts = [max(t, 1), max(gh * gw, 1)] + ([max(gh * gw, 1)] if w.editing else [])
+        for lst, rows in zip(ptrs, parts):
+            b = torch.randn((rows, ROW_BYTES // 2), generator=gen, device=dev, dtype=torch.bfloat16)
+            bufs.append(b)
+            lst.append(b.data_ptr())
+    row_ptrs = [torch.tensor(x, dtype=torch.int64, device=dev) for x in ptrs if x]
 
-    packres = mf.pack(t_samples, w.budget, t_tptr, t_iptr, ROW_BYTES)
+    def do_pack(out=None, trace=None):
+        if w.editing:
+            return mf.pack_edit(t_samples, w.budget, *row_ptrs, row_bytes=ROW_BYTES, out=out, trace=trace)
+        return mf.pack(t_samples, w.budget, *row_ptrs, ROW_BYTES, out=out, trace=trace)
+
+    packres = do_pack()
+    pos_bytes = 12 if w.editing else 8
     torch.cuda.synchronize()
     n_packed, N, max_seqlen, max_pos = (int(x) for x in packres.counts.cpu().tolist())
     cu_host = packres.cu_seqlens.cpu().numpy()[: n_packed + 1].astype(np.int64)
@@ -183,7 +191,7 @@ def main():
 
     def step(traces=None):
         tp, tf, tb = traces if traces else (None, None, None)
-        mf.pack(t_samples, w.budget, t_tptr, t_iptr, ROW_BYTES, out=packres, trace=tp)
+        do_pack(out=packres, trace=tp)
         mf.attn_fwd(tq, tk, tv, packres.cu_seqlens, max_seqlen, packres.pos, w.theta, max_pos, out=o, lse=lse,
                     workspace=ws_f, trace=tf, n_segments=n_packed)
         mf.attn_bwd(tq, tk, tv, o, lse, tdo, packres.cu_seqlens, max_seqlen, packres.pos, w.theta, max_pos,
@@ -226,7 +234,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "algorithmic_flops_per_launch": algo, "ms_per_launch": round(kern[dominant], 4)}
     else:
-        algo = kernel_bytes(base, N, H, D, len(samples))
+        algo = kernel_bytes(base, N, H, D, len(samples), pos_bytes)
         achieved = algo / (kern[dominant] * 1e-3) / 1e9
         roof = {"kernel": base, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -239,8 +247,8 @@ def main():
         entry = {"ms": round(ms, 4)}
         if b in KERNEL_FLOP_FACTOR:
             entry["tflops"] = round(KERNEL_FLOP_FACTOR[b] * sum_l2 * D * H / (ms * 1e-3) / 1e12, 1)
-        elif kernel_bytes(b, N, H, D, len(samples)) > 0:
-            entry["gbs"] = round(kernel_bytes(b, N, H, D, len(samples)) / (ms * 1e-3) / 1e9, 1)
+        elif kernel_bytes(b, N, H, D, len(samples), pos_bytes) > 0:
+            entry["gbs"] = round(kernel_bytes(b, N, H, D, len(samples), pos_bytes) / (ms * 1e-3) / 1e9, 1)
         per_kernel[name] = entry
 
     result = {
@@ -261,7 +269,9 @@ def main():
                                      "pack + fwd(LSE) + bwd",
                          "cfg1024": "1024^2 packed-CFG inference pack (4 prompts x cond/uncond): pack + fwd + bwd",
                          "stress": "long/ragged stress pack (2048^2 + two 4:1 panoramas + 64 thumbnails): "
-                                   "pack + fwd + bwd"}[args.workload],
+                                   "pack + fwd + bwd",
+                         "edit50k": "editing training pack [text | source | target], frame-aware 3D RoPE, "
+                                    "50,000-token budget, seed 6: pack + fwd(LSE) + bwd"}[args.workload],
             "n_tokens": N, "segments": n_packed, "heads": H, "head_dim": D, "max_seqlen": max_seqlen,
             "sum_L2": sum_l2, "gather_row_bytes": ROW_BYTES,
         },

@@ -71,7 +71,7 @@ typedef int32_t mf_status;
 #define MF_BF16 0
 #define MF_F32 1
 
-#define MF_ABI_VERSION 1
+#define MF_ABI_VERSION 2
 
 /* One sample descriptor: text tokens, then a grid_h x grid_w latent grid. */
 typedef struct mf_sample {
@@ -218,6 +218,79 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
                              int32_t max_pos, int32_t n_tokens, int32_t n_heads,
                              int32_t head_dim, float softmax_scale, void* workspace,
                              size_t workspace_bytes, void* stream, mf_trace* trace);
+
+/*
+ * Editing (frame-aware 3D RoPE).  For instruction-based editing, a sample's
+ * conditioning tokens are followed by the source image's latents and then
+ * the noisy target latents, and visual tokens carry (h, w, f) positions: the
+ * frame tells source from target while the spatial positions correspond
+ * (Mage-Flow paper section 3.2.2 "Conditioning and rectified-flow training",
+ * hyper.ai summary; paperlayer.ai summary, "Method").  The pages do not say
+ * how the head dimension is shared among the axes.  Readings taken here:
+ *   - one editing sample is one segment [text | source | target]; source and
+ *     target have the sample's grid_h x grid_w grid;
+ *   - positions (row, col, frame): text token u -> (u, u, u); source token
+ *     (r, c) -> (T + r, T + c, T); target token (r, c) -> (T + r, T + c, T + 1);
+ *   - rotation blocks: dims [0, 3D/8) turn by the row, [3D/8, 3D/4) by the
+ *     column, [3D/4, D) by the frame; inside a block of d dims the pair
+ *     (2j, 2j+1) turns by p * theta^(-2j/d).
+ * Positions are [n][3] int32 (4-byte aligned) in these calls.
+ */
+
+/*
+ * mf_pack_edit -- mf_pack for editing samples.  A sample's length is
+ * text_len + 2 * grid_h * grid_w; the budget policy, cu_seqlens, counts,
+ * errors and row gather are those of mf_pack, with:
+ * cu_pieces    [3 * n_samples + 1] out, or NULL: per sample its start, the
+ *              start of its source tokens and the start of its target
+ *              tokens; entries past 3 * n_packed hold n_tokens.
+ * pos          [token_budget][3] out: (row, col, frame) of packed token t.
+ * counts[3]    1 + the largest coordinate over all three axes.
+ * text_rows, source_rows, target_rows
+ *              [n_samples] device arrays of device pointers, or all NULL;
+ *              source_rows[i] and target_rows[i] hold grid_h * grid_w rows
+ *              each, row-major.
+ */
+mf_status mf_pack_edit(const mf_sample* samples, int32_t n_samples, int32_t token_budget,
+                       int32_t* cu_seqlens, int32_t* cu_pieces, int32_t* pos, int32_t* counts,
+                       const void* const* text_rows, const void* const* source_rows,
+                       const void* const* target_rows, int64_t row_bytes, void* packed,
+                       void* stream, mf_trace* trace);
+
+/* Bytes of workspace mf_rope3d_apply needs: the cos/sin table. */
+size_t mf_rope3d_workspace_size(int32_t head_dim, int32_t max_pos);
+
+/*
+ * mf_rope3d_apply -- mf_rope2d_apply with the frame-aware 3D rotation:
+ * pos is [n_tokens][3] (row, col, frame), every coordinate in [0, max_pos);
+ * workspace >= mf_rope3d_workspace_size(head_dim, max_pos) bytes.
+ */
+mf_status mf_rope3d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens,
+                          int32_t n_heads, int32_t head_dim, double theta, int32_t max_pos,
+                          int32_t inverse, void* workspace, size_t workspace_bytes,
+                          void* stream, mf_trace* trace);
+
+/*
+ * mf_varlen_attn3d_fwd, mf_varlen_attn3d_bwd -- mf_varlen_attn_fwd and
+ * mf_varlen_attn_bwd with the frame-aware 3D rotation: pos is
+ * [n_tokens][3] (row, col, frame) and must not be NULL.  Every other
+ * argument, the workspace size (mf_varlen_attn_workspace_size) and the
+ * error behaviour are those of the 2D calls.
+ */
+mf_status mf_varlen_attn3d_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
+                               int32_t max_seqlen, const int32_t* pos, double theta,
+                               int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                               int32_t head_dim, float softmax_scale, void* workspace,
+                               size_t workspace_bytes, void* stream, mf_trace* trace);
+
+mf_status mf_varlen_attn3d_bwd(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
+                               int32_t max_seqlen, const int32_t* pos, double theta,
+                               int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                               int32_t head_dim, float softmax_scale, void* workspace,
+                               size_t workspace_bytes, void* stream, mf_trace* trace);
 
 /*
  * mf_mfma_probe -- measurement helper, not a step of the path: the sustained

@@ -7,10 +7,13 @@ package loads the library and fails loudly if it has not been built.
 """
 from ._binding import (  # noqa: F401
     EXPORTED, LIB_PATH, MF_TRACE_MAX, KernelTrace, Trace, MF_BF16, MF_F32, MF_ERR_HIP, MF_ERR_INVALID_ARG, MF_ERR_UNSUPPORTED,
-    MF_ERR_WORKSPACE, MF_OK, MFError, abi_version, dtype_code, load_library, mf_mfma_probe, mf_pack,
+    MF_ERR_WORKSPACE, MF_OK, MFError, abi_version, dtype_code, load_library, mf_mfma_probe, mf_pack, mf_pack_edit,
+    mf_rope3d_apply, mf_rope3d_workspace_size,
     mf_rope2d_apply, mf_rope2d_workspace_size, mf_varlen_attn_bwd, mf_varlen_attn_fwd,
     mf_varlen_attn_workspace_size, status_string,
 )
-from .api import PROBE_VECTORS, PackResult, attn_bwd, attn_fwd, mfma_probe, pack, rope2d_apply  # noqa: F401
+from .api import (  # noqa: F401
+    PROBE_VECTORS, PackResult, attn_bwd, attn_fwd, mfma_probe, pack, pack_edit, rope2d_apply, rope3d_apply,
+)
 
 load_library()

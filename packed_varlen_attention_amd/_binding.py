@@ -28,7 +28,8 @@ MF_F32 = 1
 EXPORTED = (
     "mf_status_string", "mf_abi_version", "mf_pack", "mf_rope2d_workspace_size",
     "mf_rope2d_apply", "mf_varlen_attn_workspace_size", "mf_varlen_attn_fwd",
-    "mf_varlen_attn_bwd", "mf_mfma_probe",
+    "mf_varlen_attn_bwd", "mf_mfma_probe", "mf_pack_edit", "mf_rope3d_workspace_size", "mf_rope3d_apply",
+    "mf_varlen_attn3d_fwd", "mf_varlen_attn3d_bwd",
 )
 
 
@@ -119,6 +120,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        _vp, _dbl, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp, _vp]
     lib.mf_mfma_probe.restype = _i32
     lib.mf_mfma_probe.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp]
+    lib.mf_pack_edit.restype = _i32
+    lib.mf_pack_edit.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]
+    lib.mf_rope3d_workspace_size.restype = _sz
+    lib.mf_rope3d_workspace_size.argtypes = [_i32, _i32]
+    lib.mf_rope3d_apply.restype = _i32
+    lib.mf_rope3d_apply.argtypes = lib.mf_rope2d_apply.argtypes
+    lib.mf_varlen_attn3d_fwd.restype = _i32
+    lib.mf_varlen_attn3d_fwd.argtypes = lib.mf_varlen_attn_fwd.argtypes
+    lib.mf_varlen_attn3d_bwd.restype = _i32
+    lib.mf_varlen_attn3d_bwd.argtypes = lib.mf_varlen_attn_bwd.argtypes
     _lib = lib
     return lib
 
@@ -186,6 +197,20 @@ def mf_pack(samples: torch.Tensor, token_budget: int, cu_seqlens: torch.Tensor,
     _check(st, "mf_pack")
 
 
+def mf_pack_edit(samples: torch.Tensor, token_budget: int, cu_seqlens: torch.Tensor,
+                 cu_pieces: Optional[torch.Tensor], pos: torch.Tensor, counts: torch.Tensor,
+                 text_rows: Optional[torch.Tensor] = None, source_rows: Optional[torch.Tensor] = None,
+                 target_rows: Optional[torch.Tensor] = None, row_bytes: int = 0,
+                 packed: Optional[torch.Tensor] = None, stream=None, trace=None) -> None:
+    """Editing samples [text | source | target]; pos is int32 [budget, 3]."""
+    if samples.dtype != torch.int32 or samples.dim() != 2 or samples.shape[1] != 3:
+        raise ValueError("samples must be an int32 [S, 3] tensor")
+    st = lib().mf_pack_edit(_ptr(samples), int(samples.shape[0]), int(token_budget), _ptr(cu_seqlens),
+                            _ptr(cu_pieces), _ptr(pos), _ptr(counts), _ptr(text_rows), _ptr(source_rows),
+                            _ptr(target_rows), int(row_bytes), _ptr(packed), _stream(stream), _trace(trace))
+    _check(st, "mf_pack_edit")
+
+
 def mf_rope2d_workspace_size(head_dim: int, max_pos: int) -> int:
     return int(lib().mf_rope2d_workspace_size(int(head_dim), int(max_pos)))
 
@@ -200,6 +225,20 @@ def mf_rope2d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: i
     _check(st, "mf_rope2d_apply")
 
 
+def mf_rope3d_workspace_size(head_dim: int, max_pos: int) -> int:
+    return int(lib().mf_rope3d_workspace_size(int(head_dim), int(max_pos)))
+
+
+def mf_rope3d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: int,
+                    inverse: bool, workspace: torch.Tensor, stream=None, trace=None) -> None:
+    n, h, d = x.shape
+    st = lib().mf_rope3d_apply(_ptr(x), dtype_code(x), _ptr(pos), int(n), int(h), int(d), float(theta),
+                               int(max_pos), int(bool(inverse)), _ptr(workspace),
+                               int(workspace.numel() * workspace.element_size()), _stream(stream),
+                               _trace(trace))
+    _check(st, "mf_rope3d_apply")
+
+
 def mf_varlen_attn_workspace_size(n_tokens: int, n_heads: int, head_dim: int, n_segments: int,
                                   max_pos: int, dtype: int, backward: bool) -> int:
     return int(lib().mf_varlen_attn_workspace_size(int(n_tokens), int(n_heads), int(head_dim),
@@ -207,29 +246,42 @@ def mf_varlen_attn_workspace_size(n_tokens: int, n_heads: int, head_dim: int, n_
                                                    int(bool(backward))))
 
 
+def _entry(pos, which: str):
+    """The 2D call for [n, 2] (or no) positions, the frame-aware 3D call for [n, 3]."""
+    if pos is not None and pos.dim() == 2 and pos.shape[1] == 3:
+        name = f"mf_varlen_attn3d_{which}"
+    elif pos is None or (pos.dim() == 2 and pos.shape[1] == 2):
+        name = f"mf_varlen_attn_{which}"
+    else:
+        raise ValueError("pos must be an int32 [n, 2] or [n, 3] tensor")
+    return getattr(lib(), name), name
+
+
 def mf_varlen_attn_fwd(q, k, v, o, lse, cu_seqlens, n_segments: int, max_seqlen: int, pos,
                        theta: float, max_pos: int, softmax_scale: float, workspace, stream=None,
                        trace=None) -> None:
     n, h, d = q.shape
-    st = lib().mf_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dtype_code(q),
+    call, name = _entry(pos, "fwd")
+    st = call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dtype_code(q),
                                   _ptr(cu_seqlens), int(n_segments), int(max_seqlen), _ptr(pos),
                                   float(theta), int(max_pos), int(n), int(h), int(d), float(softmax_scale),
                                   _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                   _stream(stream), _trace(trace))
-    _check(st, "mf_varlen_attn_fwd")
+    _check(st, name)
 
 
 def mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, n_segments: int, max_seqlen: int,
                        pos, theta: float, max_pos: int, softmax_scale: float, workspace,
                        stream=None, trace=None) -> None:
     n, h, d = q.shape
-    st = lib().mf_varlen_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+    call, name = _entry(pos, "bwd")
+    st = call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                   _ptr(dk), _ptr(dv), dtype_code(q), _ptr(cu_seqlens), int(n_segments),
                                   int(max_seqlen), _ptr(pos), float(theta), int(max_pos), int(n), int(h),
                                   int(d), float(softmax_scale), _ptr(workspace),
                                   int(workspace.numel() * workspace.element_size()), _stream(stream),
                                   _trace(trace))
-    _check(st, "mf_varlen_attn_bwd")
+    _check(st, name)
 
 
 def mf_mfma_probe(operands: torch.Tensor, n_blocks: int, iters: int, sink: torch.Tensor, clocks: torch.Tensor,

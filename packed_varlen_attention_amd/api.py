@@ -16,8 +16,8 @@ from . import _binding as B
 @dataclass
 class PackResult:
     cu_seqlens: torch.Tensor  # int32 [S + 1]
-    cu_pieces: torch.Tensor   # int32 [2 S + 1]
-    pos: torch.Tensor         # int32 [token_budget, 2]
+    cu_pieces: torch.Tensor   # int32 [2 S + 1] ([3 S + 1] for editing packs)
+    pos: torch.Tensor         # int32 [token_budget, 2] ([token_budget, 3] for editing packs)
     counts: torch.Tensor      # int32 [4]: n_packed, n_tokens, max_seqlen, max_pos
     packed: Optional[torch.Tensor]  # uint8 [token_budget, row_bytes] or None
 
@@ -38,6 +38,34 @@ def pack(samples: torch.Tensor, token_budget: int, text_rows: Optional[torch.Ten
     B.mf_pack(samples, token_budget, out.cu_seqlens, out.cu_pieces, out.pos, out.counts, text_rows, image_rows,
               row_bytes, out.packed, stream, trace)
     return out
+
+
+def pack_edit(samples: torch.Tensor, token_budget: int, text_rows: Optional[torch.Tensor] = None,
+              source_rows: Optional[torch.Tensor] = None, target_rows: Optional[torch.Tensor] = None,
+              row_bytes: int = 0, stream=None, trace=None, out: Optional[PackResult] = None) -> PackResult:
+    """Editing pack [text | source | target]: cu_pieces [3 S + 1], pos [budget, 3]."""
+    if out is None:
+        dev = samples.device
+        s = int(samples.shape[0])
+        packed = None
+        if text_rows is not None:
+            packed = torch.empty((max(int(token_budget), 1), int(row_bytes)), dtype=torch.uint8, device=dev)
+        out = PackResult(torch.empty(s + 1, dtype=torch.int32, device=dev),
+                         torch.empty(3 * s + 1, dtype=torch.int32, device=dev),
+                         torch.empty((max(int(token_budget), 1), 3), dtype=torch.int32, device=dev),
+                         torch.empty(4, dtype=torch.int32, device=dev), packed)
+    B.mf_pack_edit(samples, token_budget, out.cu_seqlens, out.cu_pieces, out.pos, out.counts, text_rows,
+                   source_rows, target_rows, row_bytes, out.packed, stream, trace)
+    return out
+
+
+def rope3d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: int, inverse: bool = False,
+                 workspace: Optional[torch.Tensor] = None, stream=None, trace=None) -> torch.Tensor:
+    if workspace is None:
+        workspace = torch.empty(max(B.mf_rope3d_workspace_size(x.shape[2], max_pos), 1), dtype=torch.uint8,
+                                device=x.device)
+    B.mf_rope3d_apply(x, pos, theta, max_pos, inverse, workspace, stream, trace)
+    return x
 
 
 def rope2d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: int, inverse: bool = False,

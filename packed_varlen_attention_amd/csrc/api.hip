@@ -65,7 +65,8 @@ AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim
   AttnWorkspace w;
   w.sched = (2 * static_cast<size_t>(n_segments > 0 ? n_segments : 0) + 1) * sizeof(int32_t);
   const size_t tensor_bf16 = static_cast<size_t>(n_tokens) * n_heads * head_dim * 2;
-  w.tab = static_cast<size_t>(max_pos > 0 ? max_pos : 0) * (head_dim / 4) * sizeof(float2);
+  // rotary table, sized for the wider (3-axis) layout so one size serves both
+  w.tab = static_cast<size_t>(max_pos > 0 ? max_pos : 0) * mf::rope_table_width(head_dim, 3) * sizeof(float2);
   w.kr = tensor_bf16;  // rotated (or converted) K
   w.qr = backward ? tensor_bf16 : 0;
   w.vb = dtype == MF_F32 ? tensor_bf16 : 0;
@@ -91,8 +92,8 @@ AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim
 }
 
 mf_status check_attn_common(int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
-                            const int32_t* pos, double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads,
-                            int32_t head_dim, float softmax_scale) {
+                            const int32_t* pos, int nax, double theta, int32_t max_pos, int32_t n_tokens,
+                            int32_t n_heads, int32_t head_dim, float softmax_scale) {
   if (dtype != MF_BF16 && dtype != MF_F32) return MF_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return MF_ERR_UNSUPPORTED;
   if (cu_seqlens == nullptr) return MF_ERR_INVALID_ARG;
@@ -102,7 +103,8 @@ mf_status check_attn_common(int32_t dtype, const int32_t* cu_seqlens, int32_t n_
   if (!(softmax_scale >= 0.0f) || isinf(softmax_scale)) return MF_ERR_INVALID_ARG;
   if (pos != nullptr) {
     if (max_pos < 1 || !(theta > 0.0) || isinf(theta)) return MF_ERR_INVALID_ARG;
-    if ((reinterpret_cast<uintptr_t>(pos) & 7u) != 0) return MF_ERR_INVALID_ARG;
+    const uintptr_t align = nax == 3 ? 3u : 7u;  // [n][3] int32 or [n][2] int32 (read as int2)
+    if ((reinterpret_cast<uintptr_t>(pos) & align) != 0) return MF_ERR_INVALID_ARG;
   }
   return MF_OK;
 }
@@ -130,62 +132,119 @@ const char* mf_status_string(mf_status status) {
 
 int32_t mf_abi_version(void) { return MF_ABI_VERSION; }
 
-mf_status mf_pack(const mf_sample* samples, int32_t n_samples, int32_t token_budget, int32_t* cu_seqlens,
-                  int32_t* cu_pieces, int32_t* pos, int32_t* counts, const void* const* text_rows,
-                  const void* const* image_rows, int64_t row_bytes, void* packed, void* stream, mf_trace* trace) {
+}  // extern "C"
+
+namespace {
+
+mf_status pack_impl(int frames, const mf_sample* samples, int32_t n_samples, int32_t token_budget,
+                    int32_t* cu_seqlens, int32_t* cu_pieces, int32_t* pos, int32_t* counts,
+                    const void* const* text_rows, const void* const* image_rows, const void* const* target_rows,
+                    int64_t row_bytes, void* packed, void* stream, mf_trace* trace) {
   if (n_samples < 0 || token_budget < 0) return MF_ERR_INVALID_ARG;
-  if (n_samples > (0x7fffffff - 1) / 2) return MF_ERR_INVALID_ARG;
+  if (n_samples > (0x7fffffff - 1) / (frames + 1)) return MF_ERR_INVALID_ARG;
   if (cu_seqlens == nullptr || counts == nullptr) return MF_ERR_INVALID_ARG;
   if (n_samples > 0 && samples == nullptr) return MF_ERR_INVALID_ARG;
   if (token_budget > 0 && pos == nullptr) return MF_ERR_INVALID_ARG;
-  if (pos != nullptr && (reinterpret_cast<uintptr_t>(pos) & 7u) != 0) return MF_ERR_INVALID_ARG;
+  const uintptr_t pos_align = frames == 2 ? 3u : 7u;
+  if (pos != nullptr && (reinterpret_cast<uintptr_t>(pos) & pos_align) != 0) return MF_ERR_INVALID_ARG;
   if (packed != nullptr) {
     if (row_bytes <= 0 || text_rows == nullptr || image_rows == nullptr) return MF_ERR_INVALID_ARG;
-  } else if (text_rows != nullptr || image_rows != nullptr) {
+    if (frames == 2 && target_rows == nullptr) return MF_ERR_INVALID_ARG;
+  } else if (text_rows != nullptr || image_rows != nullptr || target_rows != nullptr) {
     return MF_ERR_INVALID_ARG;
   }
   if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Tracer tr(trace, s);
   hipError_t e = tr.run("pack_scan", [&] {
-    return mf::launch_pack_scan(samples, n_samples, token_budget, cu_seqlens, cu_pieces, counts, s);
+    return mf::launch_pack_scan(samples, n_samples, token_budget, frames, cu_seqlens, cu_pieces, counts, s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
   if (token_budget == 0 || n_samples == 0) return MF_OK;
   e = tr.run("pack_fill", [&] {
-    return mf::launch_pack_fill(samples, token_budget, cu_seqlens, counts, pos, text_rows, image_rows,
-                                packed ? row_bytes : 0, packed, s);
+    return mf::launch_pack_fill(samples, token_budget, frames, cu_seqlens, counts, pos, text_rows, image_rows,
+                                target_rows, packed ? row_bytes : 0, packed, s);
   });
   return from_hip(e);
 }
 
-size_t mf_rope2d_workspace_size(int32_t head_dim, int32_t max_pos) {
-  if (head_dim <= 0 || max_pos <= 0) return 0;
-  return align_up(static_cast<size_t>(max_pos) * (head_dim / 4) * sizeof(float2));
+}  // namespace
+
+extern "C" {
+
+mf_status mf_pack(const mf_sample* samples, int32_t n_samples, int32_t token_budget, int32_t* cu_seqlens,
+                  int32_t* cu_pieces, int32_t* pos, int32_t* counts, const void* const* text_rows,
+                  const void* const* image_rows, int64_t row_bytes, void* packed, void* stream, mf_trace* trace) {
+  return pack_impl(1, samples, n_samples, token_budget, cu_seqlens, cu_pieces, pos, counts, text_rows, image_rows,
+                   nullptr, row_bytes, packed, stream, trace);
 }
 
-mf_status mf_rope2d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens, int32_t n_heads,
-                          int32_t head_dim, double theta, int32_t max_pos, int32_t inverse, void* workspace,
-                          size_t workspace_bytes, void* stream, mf_trace* trace) {
+mf_status mf_pack_edit(const mf_sample* samples, int32_t n_samples, int32_t token_budget, int32_t* cu_seqlens,
+                       int32_t* cu_pieces, int32_t* pos, int32_t* counts, const void* const* text_rows,
+                       const void* const* source_rows, const void* const* target_rows, int64_t row_bytes,
+                       void* packed, void* stream, mf_trace* trace) {
+  return pack_impl(2, samples, n_samples, token_budget, cu_seqlens, cu_pieces, pos, counts, text_rows, source_rows,
+                   target_rows, row_bytes, packed, stream, trace);
+}
+
+size_t mf_rope2d_workspace_size(int32_t head_dim, int32_t max_pos) {
+  if (head_dim <= 0 || max_pos <= 0) return 0;
+  return align_up(static_cast<size_t>(max_pos) * mf::rope_table_width(head_dim, 2) * sizeof(float2));
+}
+
+size_t mf_rope3d_workspace_size(int32_t head_dim, int32_t max_pos) {
+  if (head_dim <= 0 || max_pos <= 0) return 0;
+  return align_up(static_cast<size_t>(max_pos) * mf::rope_table_width(head_dim, 3) * sizeof(float2));
+}
+
+}  // extern "C"
+
+namespace {
+
+mf_status rope_impl(int nax, void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens, int32_t n_heads,
+                    int32_t head_dim, double theta, int32_t max_pos, int32_t inverse, void* workspace,
+                    size_t workspace_bytes, void* stream, mf_trace* trace) {
   if (dtype != MF_BF16 && dtype != MF_F32) return MF_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return MF_ERR_UNSUPPORTED;
   if (n_tokens < 0 || n_heads < 1 || max_pos < 1 || !(theta > 0.0) || isinf(theta)) return MF_ERR_INVALID_ARG;
   if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
   if (n_tokens == 0) return MF_OK;
   if (x == nullptr || pos == nullptr || workspace == nullptr) return MF_ERR_INVALID_ARG;
-  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(pos) & 7u) != 0 || !aligned16(workspace))
+  const uintptr_t pos_align = nax == 3 ? 3u : 7u;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(pos) & pos_align) != 0 || !aligned16(workspace))
     return MF_ERR_INVALID_ARG;
-  if (workspace_bytes < mf_rope2d_workspace_size(head_dim, max_pos)) return MF_ERR_WORKSPACE;
+  const size_t need = nax == 3 ? mf_rope3d_workspace_size(head_dim, max_pos)
+                               : mf_rope2d_workspace_size(head_dim, max_pos);
+  if (workspace_bytes < need) return MF_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Tracer tr(trace, s);
   float2* tab = static_cast<float2*>(workspace);
-  hipError_t e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, theta, s); });
+  hipError_t e =
+      tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, nax, theta, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("rope_apply", [&] {
-    return mf::launch_rope_apply(x, dtype, x, dtype, pos, tab, max_pos, n_tokens, n_heads, head_dim, true,
+    return mf::launch_rope_apply(x, dtype, x, dtype, pos, nax, tab, max_pos, n_tokens, n_heads, head_dim, true,
                                  inverse != 0, s);
   });
   return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+mf_status mf_rope2d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens, int32_t n_heads,
+                          int32_t head_dim, double theta, int32_t max_pos, int32_t inverse, void* workspace,
+                          size_t workspace_bytes, void* stream, mf_trace* trace) {
+  return rope_impl(2, x, dtype, pos, n_tokens, n_heads, head_dim, theta, max_pos, inverse, workspace,
+                   workspace_bytes, stream, trace);
+}
+
+mf_status mf_rope3d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_tokens, int32_t n_heads,
+                          int32_t head_dim, double theta, int32_t max_pos, int32_t inverse, void* workspace,
+                          size_t workspace_bytes, void* stream, mf_trace* trace) {
+  return rope_impl(3, x, dtype, pos, n_tokens, n_heads, head_dim, theta, max_pos, inverse, workspace,
+                   workspace_bytes, stream, trace);
 }
 
 size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
@@ -195,12 +254,16 @@ size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t 
   return attn_workspace(n_tokens, n_heads, head_dim, n_segments, max_pos, dtype, backward != 0).total;
 }
 
-mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
-                             const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
-                             double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
-                             mf_trace* trace) {
-  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
+}  // extern "C"
+
+namespace {
+
+mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                        const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
+                        double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                        float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
+                        mf_trace* trace) {
+  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, nax, theta, max_pos, n_tokens,
                                    n_heads, head_dim, softmax_scale);
   if (st != MF_OK) return st;
   if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
@@ -220,7 +283,7 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   const void* vb = v;
   hipError_t e = hipSuccess;
   if (pos != nullptr) {
-    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, theta, s); });
+    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, nax, theta, s); });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
   // K rotated once into bf16 (also converts float32 input); Q is rotated
@@ -228,7 +291,7 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   if (pos != nullptr || dtype == MF_F32) {
     kr = ws + w.kr_off;
     e = tr.run("rope_k", [&] {
-      return mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads,
+      return mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, nax, tab, max_pos, n_tokens, n_heads,
                                    head_dim, pos != nullptr, false, s);
     });
     if (e != hipSuccess) return MF_ERR_HIP;
@@ -236,7 +299,7 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   if (dtype == MF_F32) {
     vb = ws + w.vb_off;
     e = tr.run("convert_v", [&] {
-      return mf::launch_rope_apply(v, dtype, ws + w.vb_off, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads,
+      return mf::launch_rope_apply(v, dtype, ws + w.vb_off, MF_BF16, nullptr, 2, nullptr, 0, n_tokens, n_heads,
                                    head_dim, false, false, s);
     });
     if (e != hipSuccess) return MF_ERR_HIP;
@@ -250,6 +313,7 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   a.head_dim = head_dim;
   a.dtype = dtype;
   a.pos = pos;
+  a.nax = nax;
   a.tab = tab;
   a.max_pos = max_pos;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
@@ -264,13 +328,13 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
   return from_hip(e);
 }
 
-mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                             const void* dout, void* dq, void* dk, void* dv, int32_t dtype, const int32_t* cu_seqlens,
-                             int32_t n_segments, int32_t max_seqlen, const int32_t* pos, double theta,
-                             int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
-                             mf_trace* trace) {
-  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
+mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int32_t dtype, const int32_t* cu_seqlens,
+                        int32_t n_segments, int32_t max_seqlen, const int32_t* pos, double theta,
+                        int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                        float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
+                        mf_trace* trace) {
+  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, nax, theta, max_pos, n_tokens,
                                    n_heads, head_dim, softmax_scale);
   if (st != MF_OK) return st;
   if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
@@ -297,19 +361,19 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   const void* dob = dout;
   hipError_t e = hipSuccess;
   if (pos != nullptr) {
-    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, theta, s); });
+    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, nax, theta, s); });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
   if (pos != nullptr || dtype == MF_F32) {
     qr = ws + w.qr_off;
     kr = ws + w.kr_off;
     e = tr.run("rope_q", [&] {
-      return mf::launch_rope_apply(q, dtype, ws + w.qr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads,
+      return mf::launch_rope_apply(q, dtype, ws + w.qr_off, MF_BF16, pos, nax, tab, max_pos, n_tokens, n_heads,
                                    head_dim, pos != nullptr, false, s);
     });
     if (e != hipSuccess) return MF_ERR_HIP;
     e = tr.run("rope_k", [&] {
-      return mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, tab, max_pos, n_tokens, n_heads,
+      return mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, nax, tab, max_pos, n_tokens, n_heads,
                                    head_dim, pos != nullptr, false, s);
     });
     if (e != hipSuccess) return MF_ERR_HIP;
@@ -318,12 +382,12 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
     vb = ws + w.vb_off;
     dob = ws + w.dob_off;
     e = tr.run("convert_v", [&] {
-      return mf::launch_rope_apply(v, dtype, ws + w.vb_off, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads,
+      return mf::launch_rope_apply(v, dtype, ws + w.vb_off, MF_BF16, nullptr, 2, nullptr, 0, n_tokens, n_heads,
                                    head_dim, false, false, s);
     });
     if (e != hipSuccess) return MF_ERR_HIP;
     e = tr.run("convert_do", [&] {
-      return mf::launch_rope_apply(dout, dtype, ws + w.dob_off, MF_BF16, nullptr, nullptr, 0, n_tokens, n_heads,
+      return mf::launch_rope_apply(dout, dtype, ws + w.dob_off, MF_BF16, nullptr, 2, nullptr, 0, n_tokens, n_heads,
                                    head_dim, false, false, s);
     });
     if (e != hipSuccess) return MF_ERR_HIP;
@@ -337,6 +401,7 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   a.head_dim = head_dim;
   a.dtype = dtype;
   a.pos = pos;
+  a.nax = nax;
   a.tab = tab;
   a.max_pos = max_pos;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
@@ -354,6 +419,52 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
   if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("attn_bwd_dq", [&] { return mf::launch_attn_bwd_dq(a, qr, kr, vb, dob, lse2, delta, dq, s); });
   return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                             const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
+                             double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
+                             mf_trace* trace) {
+  return attn_fwd_impl(2, q, k, v, o, lse, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
+                       n_heads, head_dim, softmax_scale, workspace, workspace_bytes, stream, trace);
+}
+
+mf_status mf_varlen_attn3d_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                               const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                               const int32_t* pos, double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                               int32_t head_dim, float softmax_scale, void* workspace, size_t workspace_bytes,
+                               void* stream, mf_trace* trace) {
+  if (pos == nullptr) return MF_ERR_INVALID_ARG;
+  return attn_fwd_impl(3, q, k, v, o, lse, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
+                       n_heads, head_dim, softmax_scale, workspace, workspace_bytes, stream, trace);
+}
+
+mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, int32_t dtype, const int32_t* cu_seqlens,
+                             int32_t n_segments, int32_t max_seqlen, const int32_t* pos, double theta,
+                             int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
+                             mf_trace* trace) {
+  return attn_bwd_impl(2, q, k, v, o, lse, dout, dq, dk, dv, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta,
+                       max_pos, n_tokens, n_heads, head_dim, softmax_scale, workspace, workspace_bytes, stream,
+                       trace);
+}
+
+mf_status mf_varlen_attn3d_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, int32_t dtype,
+                               const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                               const int32_t* pos, double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                               int32_t head_dim, float softmax_scale, void* workspace, size_t workspace_bytes,
+                               void* stream, mf_trace* trace) {
+  if (pos == nullptr) return MF_ERR_INVALID_ARG;
+  return attn_bwd_impl(3, q, k, v, o, lse, dout, dq, dk, dv, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta,
+                       max_pos, n_tokens, n_heads, head_dim, softmax_scale, workspace, workspace_bytes, stream,
+                       trace);
 }
 
 }  // extern "C"

@@ -23,26 +23,6 @@ constexpr int kQT = kDqTile;    // queries per dq workgroup (32 per wave)
 constexpr int kKT = 64;         // keys per dq LDS tile
 static_assert(kKB == kQT, "dkdv and dq share one schedule");
 
-// Rotate 4 consecutive elements (two pairs) starting at d0 (multiple of 4).
-template <int D>
-__device__ __forceinline__ void rotate4(float (&x)[4], int d0, int prow, int pcol, const float2* __restrict__ tab,
-                                        int max_pos, float sign) {
-  const int half = d0 / (D / 2);
-  int p = half ? pcol : prow;
-  p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
-  const int j0 = (d0 % (D / 2)) / 2;
-  const float2* t = tab + static_cast<size_t>(p) * (D / 4) + j0;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float2 cs = t[j];
-    const float s = sign * cs.y;
-    const float a = x[2 * j];
-    const float b = x[2 * j + 1];
-    x[2 * j] = a * cs.x - b * s;
-    x[2 * j + 1] = a * s + b * cs.x;
-  }
-}
-
 // Delta[h][t] = dot(dO[t][h], O[t][h]) and the log2-scaled LSE, for a tile of
 // kDeltaTokens tokens x kDeltaHeads heads per workgroup.  The rows of one token
 // are contiguous in O and dO, so the loads are coalesced 16-byte reads, four
@@ -110,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     const uint16_t* __restrict__ dob, const float* __restrict__ lse2, const float* __restrict__ delta,
     TOut* __restrict__ dk, TOut* __restrict__ dv, const int* __restrict__ cu, const int* __restrict__ order,
-    const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int2* __restrict__ pos,
+    const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax,
     const float2* __restrict__ tab, int max_pos, float scale, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -288,8 +268,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   for (int j = 0; j < ntiles; ++j) step(j);
 
   if (kok) {
-    int2 kp = make_int2(0, 0);
-    if (pos != nullptr) kp = pos[s0 + key];
+    Pos3 kp = {0, 0, 0};
+    if (pos != nullptr) kp = load_pos(pos, s0 + key, nax);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -297,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
         const int d0 = 32 * db + 8 * g4 + 4 * hh;
         float x[4] = {dkacc[db][4 * g4] * scale, dkacc[db][4 * g4 + 1] * scale, dkacc[db][4 * g4 + 2] * scale,
                       dkacc[db][4 * g4 + 3] * scale};
-        if (pos != nullptr) rotate4<D>(x, d0, kp.x, kp.y, tab, max_pos, -1.0f);
+        if (pos != nullptr) rotate_n<D, 4>(x, d0, kp, tab, max_pos, -1.0f, nax);
         store4<TOut>(dk + krow * D + d0, x[0], x[1], x[2], x[3]);
         store4<TOut>(dv + krow * D + d0, dvacc[db][4 * g4], dvacc[db][4 * g4 + 1], dvacc[db][4 * g4 + 2],
                      dvacc[db][4 * g4 + 3]);
@@ -310,8 +290,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     const uint16_t* __restrict__ dob, const float* __restrict__ lse2, const float* __restrict__ delta,
     TOut* __restrict__ dq, const int* __restrict__ cu, const int* __restrict__ order, const int* __restrict__ pt,
-    int n_seg, int n_tokens, int heads, const int2* __restrict__ pos, const float2* __restrict__ tab, int max_pos,
-    float scale, float scale_log2) {
+    int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax, const float2* __restrict__ tab,
+    int max_pos, float scale, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;
@@ -451,8 +431,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
   for (int j = 0; j < ntiles; ++j) step(j);
 
   if (qok) {
-    int2 qp = make_int2(0, 0);
-    if (pos != nullptr) qp = pos[s0 + qi];
+    Pos3 qp = {0, 0, 0};
+    if (pos != nullptr) qp = load_pos(pos, s0 + qi, nax);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -460,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
         const int d0 = 32 * db + 8 * g4 + 4 * hh;
         float x[4] = {dqacc[db][4 * g4] * scale, dqacc[db][4 * g4 + 1] * scale, dqacc[db][4 * g4 + 2] * scale,
                       dqacc[db][4 * g4 + 3] * scale};
-        if (pos != nullptr) rotate4<D>(x, d0, qp.x, qp.y, tab, max_pos, -1.0f);
+        if (pos != nullptr) rotate_n<D, 4>(x, d0, qp, tab, max_pos, -1.0f, nax);
         store4<TOut>(dq + qrow * D + d0, x[0], x[1], x[2], x[3]);
       }
   }
@@ -486,7 +466,7 @@ hipError_t launch_dkdv_t(const AttnArgs& a, const void* qr, const void* kr, cons
                      static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
                      static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob), lse, delta,
                      static_cast<TOut*>(dk), static_cast<TOut*>(dv), a.cu_seqlens, a.order, a.pt, a.n_segments,
-                     a.n_tokens, a.n_heads, reinterpret_cast<const int2*>(a.pos), a.tab, a.max_pos, a.scale,
+                     a.n_tokens, a.n_heads, a.pos, a.nax, a.tab, a.max_pos, a.scale,
                      a.scale * kLog2e);
   return hipGetLastError();
 }
@@ -500,7 +480,7 @@ hipError_t launch_dq_t(const AttnArgs& a, const void* qr, const void* kr, const 
                      static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
                      static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob), lse, delta,
                      static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     reinterpret_cast<const int2*>(a.pos), a.tab, a.max_pos, a.scale, a.scale * kLog2e);
+                     a.pos, a.nax, a.tab, a.max_pos, a.scale, a.scale * kLog2e);
   return hipGetLastError();
 }
 

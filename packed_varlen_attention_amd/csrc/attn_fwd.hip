@@ -47,7 +47,7 @@ template <int D, typename TIn>
 __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     const TIn* __restrict__ q, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     TIn* __restrict__ o, float* __restrict__ lse, const int* __restrict__ cu, const int* __restrict__ order,
-    const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int2* __restrict__ pos,
+    const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax,
     const float2* __restrict__ tab, int max_pos, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -85,14 +85,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   // Q fragments (B operand of S^T = K Q^T): Q[q][16kk + 8h .. +8], rotated.
   bf16x8 qf[NKK];
   {
-    int2 qp = make_int2(0, 0);
-    if (pos != nullptr && qok) qp = pos[s0 + qi];
+    Pos3 qp = {0, 0, 0};
+    if (pos != nullptr && qok) qp = load_pos(pos, s0 + qi, nax);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int e0 = 16 * kk + 8 * hh;
       float x[8];
       load_q8<TIn>(q + qrow * D + e0, qok, x);
-      if (pos != nullptr) rotate8<D>(x, e0, qp.x, qp.y, tab, max_pos, 1.0f);
+      if (pos != nullptr) rotate_n<D, 8>(x, e0, qp, tab, max_pos, 1.0f, nax);
 #pragma unroll
       for (int j = 0; j < 8; ++j) qf[kk][j] = static_cast<__bf16>(x[j]);
     }
@@ -292,7 +292,7 @@ hipError_t launch_fwd_t(const AttnArgs& a, const void* q, const void* kr, const 
   hipLaunchKernelGGL((attn_fwd_kernel<D, TIn>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
                      static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
                      static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     reinterpret_cast<const int2*>(a.pos), a.tab, a.max_pos, a.scale * kLog2e);
+                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -263,20 +263,68 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
-// Rotate 8 consecutive elements x[0..7] of one head row starting at element
-// e0 (a multiple of 8) by the axial 2D rotation of position (row, col).
-// tab holds float2 (cos, sin) of p * theta^(-2j/(D/2)), [max_pos][D/4].
-// sign = +1 forward, -1 inverse.
+// Position of one token on up to three axes: row, column, frame.
+struct Pos3 {
+  int r, c, f;
+};
+
+// Positions are [n][nax] int32: nax = 2 (row, col) for the axial 2D
+// rotation, nax = 3 (row, col, frame) for the frame-aware 3D rotation.
+__device__ __forceinline__ Pos3 load_pos(const int* __restrict__ pos, long long t, int nax) {
+  Pos3 p;
+  if (nax == 3) {
+    p.r = pos[3 * t];
+    p.c = pos[3 * t + 1];
+    p.f = pos[3 * t + 2];
+  } else {
+    const int2 q = reinterpret_cast<const int2*>(pos)[t];
+    p.r = q.x;
+    p.c = q.y;
+    p.f = 0;
+  }
+  return p;
+}
+
+// Rotary layout.  2D: dims [0, D/2) turn by the row and [D/2, D) by the
+// column; the table row of a position holds D/4 (cos, sin) pairs, pair j of
+// each half at p * theta^(-2j/(D/2)).  3D: blocks [0, 3D/8) row, [3D/8, 3D/4)
+// column, [3D/4, D) frame; the table row holds the 3D/16 pairs of a row or
+// column block (p * theta^(-2j/(3D/8))) followed by the D/8 pairs of the
+// frame block (p * theta^(-2j/(D/4))).  Every block is a multiple of 8 dims,
+// so one 8- or 4-element group never straddles two blocks.
 template <int D>
-__device__ __forceinline__ void rotate8(float (&x)[8], int e0, int prow, int pcol,
-                                        const float2* __restrict__ tab, int max_pos, float sign) {
-  const int half = e0 / (D / 2);
-  int p = half ? pcol : prow;
-  p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
-  const int j0 = (e0 % (D / 2)) / 2;
-  const float2* t = tab + static_cast<size_t>(p) * (D / 4) + j0;
+__host__ __device__ constexpr int rope_tab_width(int nax) {
+  return nax == 3 ? 3 * D / 16 + D / 8 : D / 4;
+}
+
+// Table entry of the first pair of the group starting at element e0, and the
+// position along that group's axis.
+template <int D>
+__device__ __forceinline__ const float2* rope_entry(int e0, const Pos3& p, const float2* __restrict__ tab,
+                                                   int max_pos, int nax) {
+  int axis, j0;
+  if (nax == 3) {
+    constexpr int kB = 3 * D / 8;
+    axis = e0 < kB ? 0 : (e0 < 2 * kB ? 1 : 2);
+    j0 = axis == 2 ? kB / 2 + (e0 - 2 * kB) / 2 : (e0 - axis * kB) / 2;
+  } else {
+    axis = e0 / (D / 2);
+    j0 = (e0 % (D / 2)) / 2;
+  }
+  int q = axis == 0 ? p.r : (axis == 1 ? p.c : p.f);
+  q = q < 0 ? 0 : (q >= max_pos ? max_pos - 1 : q);
+  return tab + static_cast<size_t>(q) * rope_tab_width<D>(nax) + j0;
+}
+
+// Rotate N consecutive elements x[0..N-1] (N = 4 or 8, two or four pairs) of
+// one head row starting at element e0 (a multiple of N) by the rotation of
+// position p.  sign = +1 forward, -1 inverse.
+template <int D, int N>
+__device__ __forceinline__ void rotate_n(float (&x)[N], int e0, const Pos3& p, const float2* __restrict__ tab,
+                                         int max_pos, float sign, int nax) {
+  const float2* t = rope_entry<D>(e0, p, tab, max_pos, nax);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < N / 2; ++j) {
     const float2 cs = t[j];
     const float c = cs.x;
     const float s = sign * cs.y;

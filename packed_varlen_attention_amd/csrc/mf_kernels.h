@@ -10,17 +10,23 @@ namespace mf {
 constexpr int kDtypeBf16 = 0;
 constexpr int kDtypeF32 = 1;
 
-hipError_t launch_pack_scan(const void* samples, int n, int budget, int* cu_seqlens, int* cu_pieces,
+// frames = 1: samples are [text | image], positions (row, col);
+// frames = 2: editing samples [text | source | target], positions (row, col, frame).
+hipError_t launch_pack_scan(const void* samples, int n, int budget, int frames, int* cu_seqlens, int* cu_pieces,
                             int* counts, hipStream_t stream);
 
-hipError_t launch_pack_fill(const void* samples, int budget, const int* cu_seqlens, const int* counts, int* pos,
-                            const void* const* text_rows, const void* const* image_rows, long long row_bytes,
-                            void* packed, hipStream_t stream);
+hipError_t launch_pack_fill(const void* samples, int budget, int frames, const int* cu_seqlens, const int* counts,
+                            int* pos, const void* const* text_rows, const void* const* image_rows,
+                            const void* const* target_rows, long long row_bytes, void* packed, hipStream_t stream);
 
-hipError_t launch_rope_table(float2* tab, int max_pos, int head_dim, double theta, hipStream_t stream);
+// (cos, sin) pairs per position of the rotary table: D/4 (2 axes) or 5D/16 (3 axes).
+int rope_table_width(int head_dim, int nax);
 
-// dst = rotate(src) (or a plain copy/convert when rotate is false).
-hipError_t launch_rope_apply(const void* src, int src_dtype, void* dst, int dst_dtype, const int* pos,
+hipError_t launch_rope_table(float2* tab, int max_pos, int head_dim, int nax, double theta, hipStream_t stream);
+
+// dst = rotate(src) (or a plain copy/convert when rotate is false); pos is
+// [n_tokens][nax] int32.
+hipError_t launch_rope_apply(const void* src, int src_dtype, void* dst, int dst_dtype, const int* pos, int nax,
                              const float2* tab, int max_pos, int n_tokens, int heads, int head_dim,
                              bool rotate, bool inverse, hipStream_t stream);
 
@@ -42,7 +48,8 @@ struct AttnArgs {
   int n_heads;
   int head_dim;
   int dtype;  // of q/k/v/o/dout/dq/dk/dv
-  const int* pos;  // nullptr: no rotation
+  const int* pos;  // [n_tokens][nax]; nullptr: no rotation
+  int nax;         // 2: axial 2D rotation, 3: frame-aware 3D rotation
   const float2* tab;
   int max_pos;
   float scale;

@@ -3,12 +3,19 @@
 // sequences packed under a fixed token budget, each image keeping its native
 // latent grid; rcap.io post, `pack(..., budget=50_000)`).
 //
-// Two kernels:
+// Editing samples (Mage-Flow paper section 3.2.2, "Conditioning and
+// rectified-flow training": conditioning, then source-image latents, then
+// noisy target latents; visual tokens at (h, w, f)) pack the same way with
+// two frames per sample: [text | source | target].
+//
+// Two kernels, for frames = 1 ([text | image], positions (row, col)) or
+// frames = 2 ([text | source | target], positions (row, col, frame)):
 //   pack_scan  one workgroup: validates the descriptors, scans the sample
-//              lengths, cuts the longest prefix that fits the budget and
-//              writes cu_seqlens, cu_pieces and counts;
+//              lengths T + frames * grid_h * grid_w, cuts the longest prefix
+//              that fits the budget and writes cu_seqlens, cu_pieces and
+//              counts;
 //   pack_fill  one wave per packed token (grid-stride): finds the token's
-//              segment by binary search in cu_seqlens, writes its (row, col)
+//              segment by binary search in cu_seqlens, writes its position
 //              and, when asked, copies its source row into the packed buffer.
 #include "mf_device.h"
 #include "mf_kernels.h"
@@ -51,8 +58,9 @@ __device__ long long block_incl_scan(long long x, long long* s_wave) {
 }
 
 __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(
-    const Sample* __restrict__ samples, int n, int budget, int* __restrict__ cu_seqlens,
+    const Sample* __restrict__ samples, int n, int budget, int frames, int* __restrict__ cu_seqlens,
     int* __restrict__ cu_pieces, int* __restrict__ counts) {
+  const int per = frames + 1;  // cu_pieces entries per sample
   __shared__ long long s_wave[kScanWaves];
   __shared__ int s_err;
   __shared__ int s_npacked;
@@ -72,14 +80,14 @@ __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(
   for (int i = threadIdx.x; i < n; i += kScanThreads) {
     const Sample s = samples[i];
     const long long len = static_cast<long long>(s.text_len) +
-                          static_cast<long long>(s.grid_h) * static_cast<long long>(s.grid_w);
+                          frames * static_cast<long long>(s.grid_h) * static_cast<long long>(s.grid_w);
     if (s.text_len < 0 || s.grid_h < 0 || s.grid_w < 0 || len > 0x7fffffffLL) s_err = 1;
   }
   __syncthreads();
   if (s_err) {
     for (int i = threadIdx.x; i <= n; i += kScanThreads) cu_seqlens[i] = 0;
     if (cu_pieces)
-      for (int i = threadIdx.x; i <= 2 * n; i += kScanThreads) cu_pieces[i] = 0;
+      for (int i = threadIdx.x; i <= per * n; i += kScanThreads) cu_pieces[i] = 0;
     if (threadIdx.x == 0) {
       counts[0] = -1;
       counts[1] = 0;
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(
     Sample s = {0, 0, 0};
     if (i < n) {
       s = samples[i];
-      len = static_cast<long long>(s.text_len) + static_cast<long long>(s.grid_h) * s.grid_w;
+      len = static_cast<long long>(s.text_len) + frames * static_cast<long long>(s.grid_h) * s.grid_w;
     }
     const long long incl = carry + block_incl_scan(len, s_wave);
     const bool packed = i < n && incl <= budget;
@@ -110,7 +118,10 @@ __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(
       atomicMax(&s_maxlen, static_cast<int>(len));
       int mp = 0;
       if (s.text_len > 0) mp = s.text_len;
-      if (s.grid_h > 0 && s.grid_w > 0) mp = max(mp, s.text_len + max(s.grid_h, s.grid_w));
+      if (s.grid_h > 0 && s.grid_w > 0) {
+        mp = max(mp, s.text_len + max(s.grid_h, s.grid_w));  // rows and columns up to T + max - 1
+        if (frames == 2) mp = max(mp, s.text_len + 2);       // frames T (source) and T + 1 (target)
+      }
       atomicMax(&s_maxpos, mp);
     }
     // The last thread's inclusive value is the running total.
@@ -140,10 +151,13 @@ __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(
     cu_seqlens[i] = v;
     if (cu_pieces) {
       if (i < n) {
-        cu_pieces[2 * i] = v;
-        cu_pieces[2 * i + 1] = i < npk ? v + samples[i].text_len : ntok;
+        const bool in = i < npk;
+        const Sample si = samples[i];
+        cu_pieces[per * i] = v;
+        cu_pieces[per * i + 1] = in ? v + si.text_len : ntok;
+        if (frames == 2) cu_pieces[per * i + 2] = in ? v + si.text_len + si.grid_h * si.grid_w : ntok;
       } else {
-        cu_pieces[2 * n] = ntok;
+        cu_pieces[per * n] = ntok;
       }
     }
   }
@@ -156,9 +170,10 @@ __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(
 }
 
 __global__ __launch_bounds__(256) void pack_fill_kernel(
-    const Sample* __restrict__ samples, const int* __restrict__ cu_seqlens,
-    const int* __restrict__ counts, int2* __restrict__ pos, const char* const* __restrict__ text_rows,
-    const char* const* __restrict__ image_rows, long long row_bytes, char* __restrict__ packed) {
+    const Sample* __restrict__ samples, const int* __restrict__ cu_seqlens, const int* __restrict__ counts,
+    int frames, int* __restrict__ pos, const char* const* __restrict__ text_rows,
+    const char* const* __restrict__ image_rows, const char* const* __restrict__ target_rows, long long row_bytes,
+    char* __restrict__ packed) {
   const int npk = counts[0];
   const int ntok = counts[1];
   if (npk <= 0) return;
@@ -176,21 +191,32 @@ __global__ __launch_bounds__(256) void pack_fill_kernel(
     const Sample s = samples[lo];
     const int u = static_cast<int>(t) - cu_seqlens[lo];
     const bool text = u < s.text_len;
-    const int v = u - s.text_len;
+    // Image tokens: frame f (0 source, 1 target), index v inside the grid.
+    int v = u - s.text_len;
+    int f = 0;
+    if (!text && frames == 2) {
+      const int img = s.grid_h * s.grid_w;
+      f = v >= img;
+      v -= f * img;
+    }
     if (lane == 0) {
-      int2 p;
-      if (text) {
-        p.x = u;
-        p.y = u;
-      } else {
-        p.x = s.text_len + v / s.grid_w;
-        p.y = s.text_len + v % s.grid_w;
+      int r = u, c = u, fr = u;
+      if (!text) {
+        r = s.text_len + v / s.grid_w;
+        c = s.text_len + v % s.grid_w;
+        fr = s.text_len + f;
       }
-      pos[t] = p;
+      if (frames == 2) {
+        pos[3 * t] = r;
+        pos[3 * t + 1] = c;
+        pos[3 * t + 2] = fr;
+      } else {
+        reinterpret_cast<int2*>(pos)[t] = make_int2(r, c);
+      }
     }
     if (packed) {
       const char* src = text ? text_rows[lo] + static_cast<long long>(u) * row_bytes
-                             : image_rows[lo] + static_cast<long long>(v) * row_bytes;
+                             : (f ? target_rows[lo] : image_rows[lo]) + static_cast<long long>(v) * row_bytes;
       char* dst = packed + t * row_bytes;
       if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) |
             static_cast<uintptr_t>(row_bytes)) & 15) == 0) {
@@ -206,26 +232,26 @@ __global__ __launch_bounds__(256) void pack_fill_kernel(
 
 }  // namespace
 
-hipError_t launch_pack_scan(const void* samples, int n, int budget, int* cu_seqlens, int* cu_pieces,
+hipError_t launch_pack_scan(const void* samples, int n, int budget, int frames, int* cu_seqlens, int* cu_pieces,
                             int* counts, hipStream_t stream) {
   hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                     static_cast<const Sample*>(samples), n, budget, cu_seqlens, cu_pieces, counts);
+                     static_cast<const Sample*>(samples), n, budget, frames, cu_seqlens, cu_pieces, counts);
   return hipGetLastError();
 }
 
-hipError_t launch_pack_fill(const void* samples, int budget, const int* cu_seqlens, const int* counts, int* pos,
-                            const void* const* text_rows, const void* const* image_rows, long long row_bytes,
-                            void* packed, hipStream_t stream) {
+hipError_t launch_pack_fill(const void* samples, int budget, int frames, const int* cu_seqlens, const int* counts,
+                            int* pos, const void* const* text_rows, const void* const* image_rows,
+                            const void* const* target_rows, long long row_bytes, void* packed, hipStream_t stream) {
   // Enough waves to stream the rows at full bandwidth; each loops over tokens.
   long long waves = budget;
   const long long max_waves = 256LL * 8 * 4;  // 8 resident blocks of 4 waves on 256 CUs
   if (waves > max_waves) waves = max_waves;
   const int blocks = static_cast<int>((waves + 3) / 4);
   hipLaunchKernelGGL(pack_fill_kernel, dim3(blocks), dim3(256), 0, stream,
-                     static_cast<const Sample*>(samples), cu_seqlens, counts,
-                     reinterpret_cast<int2*>(pos), reinterpret_cast<const char* const*>(text_rows),
-                     reinterpret_cast<const char* const*>(image_rows), row_bytes,
-                     static_cast<char*>(packed));
+                     static_cast<const Sample*>(samples), cu_seqlens, counts, frames, pos,
+                     reinterpret_cast<const char* const*>(text_rows),
+                     reinterpret_cast<const char* const*>(image_rows),
+                     reinterpret_cast<const char* const*>(target_rows), row_bytes, static_cast<char*>(packed));
   return hipGetLastError();
 }
 

@@ -73,14 +73,15 @@ def assert_close_scaled(got, ref, label: str, rel_rms_max: float = 8e-3, qscale:
 class Case:
     """A packed workload with inputs on host (as exact float32 values) and GPU."""
 
-    def __init__(self, samples, budget, heads, head_dim, dtype, seed, qscale=1.0, with_dout=False):
+    def __init__(self, samples, budget, heads, head_dim, dtype, seed, qscale=1.0, with_dout=False, editing=False):
         self.samples = [tuple(int(v) for v in s) for s in samples]
         self.budget = budget
-        p = oracle.pack(self.samples, budget)
+        self.editing = editing
+        p = (oracle.pack_edit if editing else oracle.pack)(self.samples, budget)
         self.pack = p
         self.n = p["n_tokens"]
         self.cu = p["cu_seqlens"]
-        self.pos = oracle.positions(self.samples, p["n_packed"])
+        self.pos = (oracle.positions_edit if editing else oracle.positions)(self.samples, p["n_packed"])
         self.max_seqlen = p["max_seqlen"]
         self.max_pos = max(p["max_pos"], 1)
         self.heads, self.d, self.dtype = heads, head_dim, dtype
@@ -99,8 +100,9 @@ class Case:
         self.tk = dev(k, dtype)
         self.tv = dev(v, dtype)
         self.tcu = torch.from_numpy(self.cu.astype(np.int32)).cuda()
-        self.tpos = torch.from_numpy(self.pos.astype(np.int32).reshape(-1, 2)).cuda() if self.n else \
-            torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+        nax = 3 if editing else 2
+        self.tpos = torch.from_numpy(self.pos.astype(np.int32).reshape(-1, nax)).cuda() if self.n else \
+            torch.zeros((1, nax), dtype=torch.int32, device="cuda")
         if with_dout:
             self.tdo = dev(self.do_bits, dtype)
 
@@ -109,4 +111,4 @@ class Case:
 
     def describe(self) -> str:
         return (f"N={self.n} segments={len(self.cu) - 1} H={self.heads} D={self.d} {self.dtype} "
-                f"max_seqlen={self.max_seqlen}")
+                f"max_seqlen={self.max_seqlen}" + (" editing" if self.editing else ""))

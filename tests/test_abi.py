@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     import packed_varlen_attention_amd as m
-    assert m.abi_version() == 1
+    assert m.abi_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert len(m.status_string(code)) > 0
     assert m.status_string(7) == "unknown status"
@@ -139,3 +139,37 @@ def test_probe_argument_errors(lib):
     assert lib.mf_mfma_probe(FAKE + 8, 4, 10, FAKE, FAKE, ctypes.byref(khz), None) == -1  # operands misaligned
     assert lib.mf_mfma_probe(FAKE, 4, 10, FAKE, FAKE + 4, ctypes.byref(khz), None) == -1  # clocks misaligned
     assert lib.mf_mfma_probe(FAKE, 4, 10, None, FAKE, ctypes.byref(khz), None) == -1
+
+
+def test_editing_argument_errors(lib):
+    # mf_pack_edit: positions are [n][3] int32 (4-byte aligned); target rows required when gathering
+    assert lib.mf_pack_edit(FAKE, -1, 10, FAKE, None, FAKE, FAKE, None, None, None, 0, None, None, None) == -1
+    assert lib.mf_pack_edit(FAKE, 2, 10, FAKE, None, FAKE + 2, FAKE, None, None, None, 0, None, None, None) == -1
+    assert lib.mf_pack_edit(FAKE, 2, 10, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 16, FAKE, None, None) == -1
+    assert lib.mf_pack_edit(FAKE, 2, 10, FAKE, None, FAKE, FAKE, None, None, FAKE, 0, None, None, None) == -1
+    # 3D rope: same checks as 2D, a 4-byte aligned [n][3] pos, the wider table
+    assert lib.mf_rope3d_apply(FAKE, 0, FAKE, 8, 1, 48, 1e4, 16, 0, FAKE, 1 << 20, None, None) == -2
+    assert lib.mf_rope3d_apply(FAKE, 0, FAKE, 8, 1, 64, 1e4, 16, 0, FAKE,
+                               lib.mf_rope3d_workspace_size(64, 16) - 1, None, None) == -3
+    assert lib.mf_rope3d_apply(FAKE, 0, FAKE + 2, 8, 1, 64, 1e4, 16, 0, FAKE, 1 << 20, None, None) == -1
+    # 3D attention: positions are mandatory and 4-byte aligned
+    def fwd3(**kw):
+        a = dict(pos=FAKE, d=128)
+        a.update(kw)
+        return lib.mf_varlen_attn3d_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 8, a["pos"], 1e4, 16, 8, 1,
+                                        a["d"], 0.0, FAKE, 1 << 30, None, None)
+    assert fwd3(pos=None) == -1
+    assert fwd3(pos=FAKE + 2) == -1
+    assert fwd3(d=96) == -2
+    assert lib.mf_varlen_attn3d_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 8, None,
+                                    1e4, 16, 8, 1, 64, 0.0, FAKE, 1 << 30, None, None) == -1
+
+
+def test_editing_workspace_sizes(lib):
+    # 3D table: 3D/16 row/column pairs + D/8 frame pairs per position
+    assert lib.mf_rope3d_workspace_size(128, 640) == 640 * 40 * 8
+    assert lib.mf_rope3d_workspace_size(64, 10) == (10 * 20 * 8 + 255) // 256 * 256
+    # the attention workspace holds the wider table for either call
+    n, h = 1000, 4
+    table3 = 640 * 40 * 8
+    assert lib.mf_varlen_attn_workspace_size(n, h, 128, 3, 640, 0, 0) >= table3 + n * h * 128 * 2

@@ -61,6 +61,7 @@ class Workload:
     theta: float = 10000.0
     backward: bool = False
     notes: str = ""
+    editing: bool = False  # samples are [text | source | target] (two frames of one grid)
 
 
 # ----------------------------------------------------------------------------
@@ -131,6 +132,26 @@ def mixed50k(seed: int = 3, n_candidates: int = 64, backward: bool = False) -> W
     return Workload("mixed50k_bwd" if backward else "mixed50k", tuple(samples),
                     budget=50_000, n_heads=24, head_dim=128, dtype="bf16",
                     seed=seed, backward=backward)
+
+
+def edit50k(seed: int = 6, n_candidates: int = 32) -> Workload:
+    """Editing training pack under a 50 000-token budget.
+
+    Each candidate is an instruction (text uniform in [32, 512]) with a
+    source image and its edited target on the same latent grid, height and
+    width drawn independently from 512..2048 step 64 as in mixed50k; a
+    sample holds text + 2 * grid tokens.  The packer keeps the longest prefix
+    that fits.
+    """
+    rng = np.random.default_rng([seed, STREAM_SHAPES])
+    samples: List[Sample] = []
+    for _ in range(n_candidates):
+        h = IMAGE_SIDES[int(rng.integers(0, len(IMAGE_SIDES)))]
+        w = IMAGE_SIDES[int(rng.integers(0, len(IMAGE_SIDES)))]
+        t = int(rng.integers(32, 513))
+        samples.append((t, h // 16, w // 16))
+    return Workload("edit50k", tuple(samples), budget=50_000, n_heads=24, head_dim=128, dtype="bf16",
+                    seed=seed, editing=True)
 
 
 def stress() -> Workload:
