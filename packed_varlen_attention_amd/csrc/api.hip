@@ -63,7 +63,8 @@ struct AttnWorkspace {
 AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
                              int32_t max_pos, int32_t dtype, bool backward) {
   AttnWorkspace w;
-  w.sched = (2 * static_cast<size_t>(n_segments > 0 ? n_segments : 0) + 1) * sizeof(int32_t);
+  // schedules (order, tile prefix): one for the forward; dkdv's and dq's for the backward
+  w.sched = (backward ? 2 : 1) * (2 * static_cast<size_t>(n_segments > 0 ? n_segments : 0) + 1) * sizeof(int32_t);
   const size_t tensor_bf16 = static_cast<size_t>(n_tokens) * n_heads * head_dim * 2;
   // rotary table, sized for the wider (3-axis) layout so one size serves both
   w.tab = static_cast<size_t>(max_pos > 0 ? max_pos : 0) * mf::rope_table_width(head_dim, 3) * sizeof(float2);
@@ -407,9 +408,16 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
   a.order = reinterpret_cast<int*>(ws + w.sched_off);
   a.pt = a.order + n_segments;
+  // dkdv walks key tiles of kDkdvTile, dq query tiles of kDqTile: one schedule each.
+  mf::AttnArgs aq = a;
+  aq.order = a.pt + n_segments + 1;
+  aq.pt = aq.order + n_segments;
   e = tr.run("attn_sched", [&] {
-    return mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kDqTile, const_cast<int*>(a.order),
-                            const_cast<int*>(a.pt), s);
+    hipError_t r = mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kDkdvTile, const_cast<int*>(a.order),
+                                    const_cast<int*>(a.pt), s);
+    if (r != hipSuccess) return r;
+    return mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kDqTile, const_cast<int*>(aq.order),
+                            const_cast<int*>(aq.pt), s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("attn_bwd_delta", [&] { return mf::launch_attn_bwd_delta(a, o, dout, lse, delta, lse2, s); });
@@ -417,7 +425,7 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
   e = tr.run("attn_bwd_dkdv",
              [&] { return mf::launch_attn_bwd_dkdv(a, qr, kr, vb, dob, lse2, delta, dk, dv, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
-  e = tr.run("attn_bwd_dq", [&] { return mf::launch_attn_bwd_dq(a, qr, kr, vb, dob, lse2, delta, dq, s); });
+  e = tr.run("attn_bwd_dq", [&] { return mf::launch_attn_bwd_dq(aq, qr, kr, vb, dob, lse2, delta, dq, s); });
   return from_hip(e);
 }
 

@@ -5,6 +5,7 @@
 //   dV = P^T dO,  dKr = scale * dS^T Qr          dkdv kernel, per 32 keys/wave
 //                                                (K in registers, V rows in LDS)
 //   dQr = scale * dS Kr                          dq kernel,   per 32 queries/wave
+//                                                (8 waves, K/V tiles three-buffered)
 // where dS = P * (dO V^T - Delta); dQ and dK are rotated back by the inverse
 // rotation in the epilogues.  Each output element is written by exactly one
 // lane and summed in a fixed order: results are deterministic (no atomics).
@@ -20,8 +21,8 @@ namespace {
 constexpr int kKB = kDkdvTile;  // keys per dkdv workgroup (32 per wave)
 constexpr int kQB = 32;         // queries per dkdv LDS tile
 constexpr int kQT = kDqTile;    // queries per dq workgroup (32 per wave)
+constexpr int kDqWaves = kQT / 32;
 constexpr int kKT = 64;         // keys per dq LDS tile
-static_assert(kKB == kQT, "dkdv and dq share one schedule");
 
 // Delta[h][t] = dot(dO[t][h], O[t][h]) and the log2-scaled LSE, for a tile of
 // kDeltaTokens tokens x kDeltaHeads heads per workgroup.  The rows of one token
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
 }
 
 template <int D, typename TOut>
-__global__ __launch_bounds__(256, 2) void dq_kernel(
+__global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     const uint16_t* __restrict__ dob, const float* __restrict__ lse2, const float* __restrict__ delta,
     TOut* __restrict__ dq, const int* __restrict__ cu, const int* __restrict__ order, const int* __restrict__ pt,
@@ -298,8 +299,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kKT * kRowBytes;
   constexpr int kRowsPerInst = 1024 / kRowBytes;
-  constexpr int kInstPerWave = kKT / kRowsPerInst / 4;
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // K tiles [2], V tiles [2]
+  constexpr int kInstPerWave = kKT / kRowsPerInst / kDqWaves;
+  static_assert(kInstPerWave >= 1, "every wave issues whole tile copies");
+  // LDS: three K and three V tiles, six separate objects so the compiler can
+  // tell the tile being read from the tiles being filled by in-flight copies.
+  __shared__ __attribute__((aligned(16))) char smemK0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemK1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemK2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemV0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemV1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemV2[kTileBytes];
 
   WorkItem it;
   if (!decode_item(blockIdx.x, heads, n_seg, order, pt, it)) return;
@@ -338,17 +347,17 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     ld_row[r] = inst * kRowsPerInst + lane / CH;
     ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
   }
-  lds_char* const sK0 = (lds_char*)(smem);
-  lds_char* const sV0 = sK0 + 2 * kTileBytes;
-  auto load_tile = [&](int k0, int buf) {
+  lds_char* const sKb[3] = {(lds_char*)(smemK0), (lds_char*)(smemK1), (lds_char*)(smemK2)};
+  lds_char* const sVb[3] = {(lds_char*)(smemV0), (lds_char*)(smemV1), (lds_char*)(smemV2)};
+  auto load_tile = [&](int k0, lds_char* dK, lds_char* dV) {
     const bool tail = k0 + kKT > L;
 #pragma unroll
     for (int r = 0; r < kInstPerWave; ++r) {
       const int row = tail ? min(k0 + ld_row[r], L - 1) : k0 + ld_row[r];
       const size_t off = static_cast<size_t>(row) * hD + ld_off[r];
-      const int dst = buf * kTileBytes + (wave * kInstPerWave + r) * 1024;
-      __builtin_amdgcn_global_load_lds(kseg + off, sK0 + dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vseg + off, sV0 + dst, 16, 0, 0);
+      const int dst = (wave * kInstPerWave + r) * 1024;
+      __builtin_amdgcn_global_load_lds(kseg + off, dK + dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vseg + off, dV + dst, 16, 0, 0);
     }
   };
   int roff[NKK];
@@ -382,13 +391,18 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
+  // Tile t lives in buffer t % 3.  Step j issues the copies of tile j + 2
+  // (past the end: the last tile again, into a buffer no later step reads),
+  // so every step issues the same number of copies, and at its end waits
+  // only for those issued before it; b = j % 3 is compile-time.
   const int ntiles = (L + kKT - 1) / kKT;
-  auto step = [&](int j) {
+  const int last_k0 = (ntiles - 1) * kKT;
+  auto step = [&](int j, auto buf_tag) {
+    constexpr int b = decltype(buf_tag)::value;
     const int k0 = j * kKT;
-    const int b = j & 1;
-    if (j + 1 < ntiles) load_tile(k0 + kKT, b ^ 1);
-    const lds_char* sK = sK0 + b * kTileBytes;
-    const lds_char* sV = sV0 + b * kTileBytes;
+    load_tile(min(k0 + 2 * kKT, last_k0), sKb[(b + 2) % 3], sVb[(b + 2) % 3]);
+    const lds_char* sK = sKb[b];
+    const lds_char* sV = sVb[b];
     bf16x8 dsb[kKT / 16];
 #pragma unroll
     for (int kb = 0; kb < kKT / 32; ++kb) {
@@ -422,13 +436,27 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     for (int c = 0; c < kKT / 16; ++c)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(col_frag(sK, c, db), dsb[c], dqacc[db]);
-    wait_vmem();
-    __syncthreads();
+    wait_vmem_keep<2 * kInstPerWave>();
+    barrier_keep_loads();
   };
-  load_tile(0, 0);
+  load_tile(0, sKb[0], sVb[0]);
+  if (ntiles > 1) load_tile(kKT, sKb[1], sVb[1]);
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) step(j);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  int j = 0;
+  for (; j + 3 <= ntiles; j += 3) {
+    step(j, B0{});
+    step(j + 1, B1{});
+    step(j + 2, B2{});
+  }
+  if (j < ntiles) {
+    step(j, B0{});
+    if (j + 1 < ntiles) step(j + 1, B1{});
+  }
+  wait_vmem();  // the last steps' copies land before the workgroup's LDS is released
 
   if (qok) {
     Pos3 qp = {0, 0, 0};
@@ -476,7 +504,7 @@ hipError_t launch_dq_t(const AttnArgs& a, const void* qr, const void* kr, const 
                        const float* lse, const float* delta, void* dq, hipStream_t stream) {
   const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kQT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((dq_kernel<D, TOut>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((dq_kernel<D, TOut>), dim3(static_cast<unsigned>(blocks)), dim3(kDqWaves * 64), 0, stream,
                      static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
                      static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob), lse, delta,
                      static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,

@@ -37,7 +37,7 @@ hipError_t launch_sched(const int* cu_seqlens, int n_segments, int n_tokens, int
 long long sched_grid(int n_tokens, int n_segments, int heads, int tile);
 
 constexpr int kFwdTile = 256;   // query rows per forward workgroup (8 waves)
-constexpr int kDqTile = 128;    // query rows per dq workgroup
+constexpr int kDqTile = 256;    // query rows per dq workgroup (8 waves)
 constexpr int kDkdvTile = 128;  // keys per dkdv workgroup
 
 struct AttnArgs {
