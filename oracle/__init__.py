@@ -22,7 +22,9 @@ Sources (the Mage-Flow pages):
 * editing: text, source-image and target-image tokens of one sample in one
   segment, with a frame-aware 3D rotary embedding that tells source from
   target -- paper section 3.2.2 "Conditioning and rectified-flow training"
-  (hyper.ai summary); paperlayer.ai summary, "Method".
+  (hyper.ai summary); paperlayer.ai summary, "Method";
+* the rectified flow-matching objective on the packed latents and the packed
+  CFG combine -- ``oracle.flow``.
 
 The pages fix no formula for the rotation, the position assignment, the
 softmax scale or the log-sum-exp.  The readings taken here are listed in each
@@ -34,3 +36,4 @@ forms, invariants, brute force and library routines (see those files).
 from .pack import pack, positions, gather, pack_edit, positions_edit, gather_edit  # noqa: F401
 from .rope import inv_freq, rope2d, rope3d, rope_axes, blocks3d  # noqa: F401
 from .attention import attn_fwd, attn_bwd, attn_fwd_rows  # noqa: F401
+from . import flow  # noqa: F401
