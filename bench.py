@@ -49,6 +49,10 @@ def parse_args():
                          "the editing path with frame-aware 3D RoPE)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU timing")
     ap.add_argument("--cpu-threads", type=int, default=16, help="BLAS threads for the oracle baseline")
+    ap.add_argument("--flow", action="store_true",
+                    help="after timing, also time the rectified-flow noising / loss passes on the pack's latents "
+                         "(128 channels, bf16) and the CFG combine on the 1024^2 packed-CFG pack; reported under "
+                         "'flow', not part of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -127,6 +131,64 @@ def cpu_baseline(w, samples, q, k, v, do, threads: int, min_seconds: float = 10.
         "sample": f"fp64 numpy oracle, forward+backward of {heads} of {w.n_heads} heads over all "
                   f"{p['n_packed']} segments ({p['n_tokens']} tokens), {secs:.1f} s",
     }
+
+
+def flow_timing(mf, workloads, w, samples, packres, n_tokens: int, dev, reps: int = 20) -> dict:
+    """Mean per-launch time and algorithmic GB/s of the rectified-flow and CFG passes."""
+    import numpy as np
+    import torch
+
+    c = 128  # latent channels
+    frames = 2 if w.editing else 1
+    s = len(samples)
+
+    def bf16(stream):
+        x = workloads.normal(w.seed, stream, (n_tokens, c), "bf16")
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    z, eps, v = bf16(20), bf16(21), bf16(22)
+    t = torch.rand(s, generator=torch.Generator(device=dev).manual_seed(w.seed), device=dev)
+    cp = packres.cu_pieces
+    noised = int(sum(b - a for a, b in zip(
+        cp.cpu().numpy()[frames::frames + 1][:s].tolist(), cp.cpu().numpy()[frames + 1::frames + 1][:s].tolist())))
+    row = c * 2
+    out = {}
+
+    def timed(name, fn, nbytes):
+        tr = mf.KernelTrace(4)
+        fn(None)
+        torch.cuda.synchronize()
+        total = 0.0
+        for _ in range(reps):
+            fn(tr)
+            torch.cuda.synchronize()
+            total += sum(ms for _, ms in tr.results())
+        ms = total / reps
+        out[name] = {"ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes}
+
+    zt = torch.empty_like(z)
+    grad = torch.empty_like(v)
+    ws = torch.empty(mf._binding.mf_rf_loss_workspace_size(n_tokens), dtype=torch.uint8, device=dev)
+    # noise: read z (all rows), eps (noised rows), write z_t (all rows)
+    timed("rf_noise", lambda tr: mf.rf_noise(z, eps, t, cp, s, frames, out=zt, trace=tr),
+          (2 * n_tokens + noised) * row)
+    # loss: read v, z, eps (noised rows), write grad (all rows) and one float per row
+    timed("rf_loss", lambda tr: mf.rf_loss(v, z, eps, cp, s, frames, 1.0, workspace=ws, trace=tr),
+          3 * noised * row + n_tokens * row + 8 * n_tokens)
+    g = workloads.cfg1024()
+    gs = torch.tensor(np.asarray(g.samples, dtype=np.int32)).to(dev)
+    gp = mf.pack(gs, g.budget)
+    torch.cuda.synchronize()
+    gn = int(gp.counts[1].item())
+    gcp = gp.cu_pieces.cpu().numpy()
+    cond_img = sum(int(gcp[2 * k + 2] - gcp[2 * k + 1]) for k in range(0, len(g.samples), 2))
+    gv = torch.from_numpy(workloads.normal(g.seed, 23, (gn, c), "bf16").view(np.int16)).to(dev).view(torch.bfloat16)
+    # combine in place: read cond and uncond image rows, write cond image rows
+    timed("cfg_combine", lambda tr: mf.cfg_combine(gv, gp.cu_pieces, len(g.samples), len(g.samples) // 2, 4.5,
+                                                   out=gv, trace=tr), 3 * cond_img * row)
+    out["note"] = (f"latents [N][{c}] bf16 on the bench pack (N={n_tokens}, {noised} noised rows); CFG on the "
+                   f"1024^2 packed-CFG pack ({gn} tokens, {len(g.samples) // 2} pairs)")
+    return out
 
 
 def main():
@@ -297,6 +359,8 @@ def main():
     if roof["unit"] == "TFLOP/s":
         roof["peak_measured"] = round(probe["tflops"], 1)
         roof["frac_measured"] = round(roof["achieved"] / probe["tflops"], 4)
+    if args.flow:
+        result["flow"] = flow_timing(mf, workloads, w, samples, packres, N, dev)
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

@@ -293,6 +293,67 @@ mf_status mf_varlen_attn3d_bwd(const void* q, const void* k, const void* v, cons
                                size_t workspace_bytes, void* stream, mf_trace* trace);
 
 /*
+ * Rectified-flow objective on the packed latents.  Training regresses the
+ * model's velocity v(z_t, t) on the target z - eps, with model input
+ * z_t = (1 - t) z + t eps and eps ~ N(0, I) (Mage-Flow paper section 3.2.1 as
+ * summarised on paperlayer.ai, "Method"; rcap.io post, the pseudo-code's
+ * `loss = mse(v_pred, (z - noise))`); for editing, only target tokens carry
+ * the loss (paper section 3.2.2, hyper.ai summary).
+ *
+ * Latent tensors are [n_tokens][channels] rows in packed order, dtype MF_BF16
+ * or MF_F32, 16-byte aligned; channels is a power of two in [8, 512] (the
+ * latent space has 128 channels).  cu_pieces is the packer's output for the
+ * same samples: frames = 1 for a generation pack (mf_pack: start, image
+ * start per sample), frames = 2 for an editing pack (mf_pack_edit: start,
+ * source start, target start).  The noised rows of sample s are its image
+ * rows (frames = 1) or its target rows (frames = 2); text rows and editing
+ * source rows are conditioning.
+ */
+
+/* mf_rf_noise -- zt = (1 - t[s]) z + t[s] eps on sample s's noised rows,
+ * zt = z on every other row.  t: device float[n_samples]. */
+mf_status mf_rf_noise(const void* z, const void* eps, const float* t, void* zt, int32_t dtype,
+                      const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
+                      int32_t channels, void* stream, mf_trace* trace);
+
+/* Bytes of workspace mf_rf_loss needs (one float per row). */
+size_t mf_rf_loss_workspace_size(int32_t n_tokens);
+
+/*
+ * mf_rf_loss -- target, loss and gradient in one pass over v, z and eps.
+ * loss_sum   device float[n_samples] out: per sample, the sum over its noised
+ *            rows and channels of (v - (z - eps))^2, reduced in a fixed
+ *            order (deterministic).  The pack's mean-squared error is
+ *            sum(loss_sum) / M with M = channels x noised rows.
+ * grad       [n_tokens][channels] out, or NULL: grad_scale * (v - (z - eps))
+ *            on noised rows, 0 elsewhere (grad_scale = 2 / M gives the
+ *            gradient of the mean).
+ * workspace  >= mf_rf_loss_workspace_size(n_tokens) bytes, 4-byte aligned.
+ */
+mf_status mf_rf_loss(const void* v, const void* z, const void* eps, void* grad, float* loss_sum,
+                     int32_t dtype, const int32_t* cu_pieces, int32_t n_samples, int32_t frames,
+                     int32_t n_tokens, int32_t channels, float grad_scale, void* workspace,
+                     size_t workspace_bytes, void* stream, mf_trace* trace);
+
+/*
+ * mf_cfg_combine -- packed classifier-free guidance: the conditional and
+ * unconditional branches of each prompt run as consecutive samples of one
+ * pack (paper section 3.2.1; hyper.ai summary, "Experiment").  The pages
+ * give no combine formula; this is the usual guidance form (Ho and Salimans,
+ * "Classifier-Free Diffusion Guidance"):
+ *   out[cond image row r] = v_u[r] + scale * (v_c[r] - v_u[r])
+ * for pairs (2p, 2p + 1), p < n_pairs, of a generation pack (cu_pieces of
+ * mf_pack, n_samples samples, 2 * n_pairs <= n_samples).  Every other row of
+ * out is a copy of v; out may be v (in place).  A pair whose two images
+ * differ in token count is left as a copy; mismatched (device int32, or
+ * NULL) receives the number of such pairs.
+ */
+mf_status mf_cfg_combine(const void* v, void* out, int32_t* mismatched, int32_t dtype,
+                         const int32_t* cu_pieces, int32_t n_samples, int32_t n_pairs,
+                         int32_t n_tokens, int32_t channels, float scale, void* stream,
+                         mf_trace* trace);
+
+/*
  * mf_mfma_probe -- measurement helper, not a step of the path: the sustained
  * rate of the 32x32x16 bf16 matrix instruction on the caller's operand values
  * and the shader clock meanwhile.  Throughput figures of the attention

@@ -13,7 +13,8 @@ from ._binding import (  # noqa: F401
     mf_varlen_attn_workspace_size, status_string,
 )
 from .api import (  # noqa: F401
-    PROBE_VECTORS, PackResult, attn_bwd, attn_fwd, mfma_probe, pack, pack_edit, rope2d_apply, rope3d_apply,
+    PROBE_VECTORS, PackResult, attn_bwd, attn_fwd, cfg_combine, mfma_probe, pack, pack_edit, rf_loss, rf_noise,
+    rope2d_apply, rope3d_apply,
 )
 
 load_library()

@@ -29,7 +29,8 @@ EXPORTED = (
     "mf_status_string", "mf_abi_version", "mf_pack", "mf_rope2d_workspace_size",
     "mf_rope2d_apply", "mf_varlen_attn_workspace_size", "mf_varlen_attn_fwd",
     "mf_varlen_attn_bwd", "mf_mfma_probe", "mf_pack_edit", "mf_rope3d_workspace_size", "mf_rope3d_apply",
-    "mf_varlen_attn3d_fwd", "mf_varlen_attn3d_bwd",
+    "mf_varlen_attn3d_fwd", "mf_varlen_attn3d_bwd", "mf_rf_noise", "mf_rf_loss_workspace_size", "mf_rf_loss",
+    "mf_cfg_combine",
 )
 
 
@@ -130,6 +131,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mf_varlen_attn3d_fwd.argtypes = lib.mf_varlen_attn_fwd.argtypes
     lib.mf_varlen_attn3d_bwd.restype = _i32
     lib.mf_varlen_attn3d_bwd.argtypes = lib.mf_varlen_attn_bwd.argtypes
+    lib.mf_rf_noise.restype = _i32
+    lib.mf_rf_noise.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
+    lib.mf_rf_loss_workspace_size.restype = _sz
+    lib.mf_rf_loss_workspace_size.argtypes = [_i32]
+    lib.mf_rf_loss.restype = _i32
+    lib.mf_rf_loss.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp,
+                               _vp]
+    lib.mf_cfg_combine.restype = _i32
+    lib.mf_cfg_combine.argtypes = [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
     _lib = lib
     return lib
 
@@ -291,3 +301,30 @@ def mf_mfma_probe(operands: torch.Tensor, n_blocks: int, iters: int, sink: torch
     _check(lib().mf_mfma_probe(_ptr(operands), int(n_blocks), int(iters), _ptr(sink), _ptr(clocks),
                                ctypes.byref(khz), _stream(stream)), "mf_mfma_probe")
     return int(khz.value)
+
+
+def mf_rf_noise(z, eps, t, zt, cu_pieces, n_samples: int, frames: int, stream=None, trace=None) -> None:
+    n, c = z.shape
+    _check(lib().mf_rf_noise(_ptr(z), _ptr(eps), _ptr(t), _ptr(zt), dtype_code(z), _ptr(cu_pieces), int(n_samples),
+                             int(frames), int(n), int(c), _stream(stream), _trace(trace)), "mf_rf_noise")
+
+
+def mf_rf_loss_workspace_size(n_tokens: int) -> int:
+    return int(lib().mf_rf_loss_workspace_size(int(n_tokens)))
+
+
+def mf_rf_loss(v, z, eps, grad, loss_sum, cu_pieces, n_samples: int, frames: int, grad_scale: float, workspace,
+               stream=None, trace=None) -> None:
+    n, c = v.shape
+    _check(lib().mf_rf_loss(_ptr(v), _ptr(z), _ptr(eps), _ptr(grad), _ptr(loss_sum), dtype_code(v),
+                            _ptr(cu_pieces), int(n_samples), int(frames), int(n), int(c), float(grad_scale),
+                            _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream),
+                            _trace(trace)), "mf_rf_loss")
+
+
+def mf_cfg_combine(v, out, mismatched, cu_pieces, n_samples: int, n_pairs: int, scale: float, stream=None,
+                   trace=None) -> None:
+    n, c = v.shape
+    _check(lib().mf_cfg_combine(_ptr(v), _ptr(out), _ptr(mismatched), dtype_code(v), _ptr(cu_pieces),
+                                int(n_samples), int(n_pairs), int(n), int(c), float(scale), _stream(stream),
+                                _trace(trace)), "mf_cfg_combine")

@@ -143,3 +143,32 @@ def mfma_probe(operands: torch.Tensor, n_blocks: int, iters: int) -> dict:
     sclk_mhz = float(c[:, 0].sum() / c[:, 1].sum()) * khz / 1000.0
     flops = float(n_blocks) * 4 * 4 * iters * 32768
     return {"flops": flops, "ms": ms, "tflops": flops / ms / 1e9, "sclk_mhz": sclk_mhz}
+
+
+def rf_noise(z: torch.Tensor, eps: torch.Tensor, t: torch.Tensor, cu_pieces: torch.Tensor, n_samples: int,
+             frames: int = 1, out: Optional[torch.Tensor] = None, stream=None, trace=None) -> torch.Tensor:
+    """Model input z_t of the rectified-flow objective on [N][C] packed latents."""
+    zt = torch.empty_like(z) if out is None else out
+    B.mf_rf_noise(z, eps, t, zt, cu_pieces, n_samples, frames, stream, trace)
+    return zt
+
+
+def rf_loss(v: torch.Tensor, z: torch.Tensor, eps: torch.Tensor, cu_pieces: torch.Tensor, n_samples: int,
+            frames: int = 1, grad_scale: float = 1.0, with_grad: bool = True,
+            workspace: Optional[torch.Tensor] = None, stream=None, trace=None):
+    """(loss_sum [n_samples] float32, grad [N][C] or None)."""
+    loss = torch.empty(max(int(n_samples), 1), dtype=torch.float32, device=v.device)
+    grad = torch.empty_like(v) if with_grad else None
+    if workspace is None:
+        workspace = torch.empty(max(B.mf_rf_loss_workspace_size(v.shape[0]), 4), dtype=torch.uint8, device=v.device)
+    B.mf_rf_loss(v, z, eps, grad, loss, cu_pieces, n_samples, frames, grad_scale, workspace, stream, trace)
+    return loss[: int(n_samples)], grad
+
+
+def cfg_combine(v: torch.Tensor, cu_pieces: torch.Tensor, n_samples: int, n_pairs: int, scale: float,
+                out: Optional[torch.Tensor] = None, stream=None, trace=None):
+    """(guided copy of v (or out), device int32 [1] count of mismatched pairs)."""
+    o = torch.empty_like(v) if out is None else out
+    mismatched = torch.zeros(1, dtype=torch.int32, device=v.device)
+    B.mf_cfg_combine(v, o, mismatched, cu_pieces, n_samples, n_pairs, scale, stream, trace)
+    return o, mismatched

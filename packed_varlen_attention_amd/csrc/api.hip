@@ -475,4 +475,88 @@ mf_status mf_varlen_attn3d_bwd(const void* q, const void* k, const void* v, cons
                        trace);
 }
 
+// ---------------------------------------------------------------------------
+// Rectified-flow objective and packed CFG combine on [n_tokens][channels] latents.
+
+}  // extern "C"
+
+namespace {
+
+mf_status check_flow_common(int32_t dtype, const int32_t* cu_pieces, int32_t n_samples, int32_t frames,
+                            int32_t n_tokens, int32_t channels) {
+  if (dtype != MF_BF16 && dtype != MF_F32) return MF_ERR_UNSUPPORTED;
+  // a row's channels / 8 vectors must be a power of two within one wave
+  if (channels < 8 || channels > 512 || (channels & (channels - 1)) != 0) return MF_ERR_UNSUPPORTED;
+  if (cu_pieces == nullptr || n_samples < 0 || n_tokens < 0 || (frames != 1 && frames != 2)) return MF_ERR_INVALID_ARG;
+  if (static_cast<long long>(n_samples) * (frames + 1) >= 0x7fffffffLL) return MF_ERR_INVALID_ARG;
+  return MF_OK;
+}
+
+bool aligned_for(const void* p, int32_t /*dtype*/) { return p != nullptr && aligned16(p); }
+
+}  // namespace
+
+extern "C" {
+
+mf_status mf_rf_noise(const void* z, const void* eps, const float* t, void* zt, int32_t dtype,
+                      const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
+                      int32_t channels, void* stream, mf_trace* trace) {
+  mf_status st = check_flow_common(dtype, cu_pieces, n_samples, frames, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MF_OK;
+  if (!aligned_for(z, dtype) || !aligned_for(eps, dtype) || !aligned_for(zt, dtype)) return MF_ERR_INVALID_ARG;
+  if (n_samples > 0 && (t == nullptr || (reinterpret_cast<uintptr_t>(t) & 3u) != 0)) return MF_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Tracer tr(trace, s);
+  return from_hip(tr.run("rf_noise", [&] {
+    return mf::launch_rf_noise(z, eps, t, zt, dtype, cu_pieces, n_samples, frames, n_tokens, channels, s);
+  }));
+}
+
+size_t mf_rf_loss_workspace_size(int32_t n_tokens) {
+  if (n_tokens <= 0) return 0;
+  return align_up(static_cast<size_t>(n_tokens) * sizeof(float));
+}
+
+mf_status mf_rf_loss(const void* v, const void* z, const void* eps, void* grad, float* loss_sum, int32_t dtype,
+                     const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens, int32_t channels,
+                     float grad_scale, void* workspace, size_t workspace_bytes, void* stream, mf_trace* trace) {
+  mf_status st = check_flow_common(dtype, cu_pieces, n_samples, frames, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (isnan(grad_scale) || isinf(grad_scale)) return MF_ERR_INVALID_ARG;
+  if (n_samples > 0 && (loss_sum == nullptr || (reinterpret_cast<uintptr_t>(loss_sum) & 3u) != 0))
+    return MF_ERR_INVALID_ARG;
+  if (n_tokens > 0) {
+    if (!aligned_for(v, dtype) || !aligned_for(z, dtype) || !aligned_for(eps, dtype)) return MF_ERR_INVALID_ARG;
+    if (grad != nullptr && !aligned_for(grad, dtype)) return MF_ERR_INVALID_ARG;
+    if (workspace_bytes < mf_rf_loss_workspace_size(n_tokens)) return MF_ERR_WORKSPACE;
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return MF_ERR_INVALID_ARG;
+  }
+  if (n_samples == 0 && n_tokens == 0) return MF_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Tracer tr(trace, s);
+  return from_hip(tr.run("rf_loss", [&] {
+    return mf::launch_rf_loss(v, z, eps, grad, static_cast<float*>(workspace), loss_sum, dtype, cu_pieces, n_samples,
+                              frames, n_tokens, channels, grad_scale, s);
+  }));
+}
+
+mf_status mf_cfg_combine(const void* v, void* out, int32_t* mismatched, int32_t dtype, const int32_t* cu_pieces,
+                         int32_t n_samples, int32_t n_pairs, int32_t n_tokens, int32_t channels, float scale,
+                         void* stream, mf_trace* trace) {
+  mf_status st = check_flow_common(dtype, cu_pieces, n_samples, 1, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (n_pairs < 0 || 2LL * n_pairs > n_samples || isnan(scale) || isinf(scale)) return MF_ERR_INVALID_ARG;
+  if (mismatched != nullptr && (reinterpret_cast<uintptr_t>(mismatched) & 3u) != 0) return MF_ERR_INVALID_ARG;
+  if (n_tokens > 0 && (!aligned_for(v, dtype) || !aligned_for(out, dtype))) return MF_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Tracer tr(trace, s);
+  return from_hip(tr.run("cfg_combine", [&] {
+    return mf::launch_cfg_combine(v, out, mismatched, dtype, cu_pieces, n_pairs, n_tokens, channels, scale, s);
+  }));
+}
+
 }  // extern "C"

@@ -74,4 +74,14 @@ hipError_t launch_attn_bwd_dq(const AttnArgs& a, const void* qr, const void* kr,
                               const void* dob, const float* lse, const float* delta, void* dq,
                               hipStream_t stream);
 
+// Rectified-flow noising / loss and the packed CFG combine over [N][C]
+// latent rows (C / 8 a power of two <= 64); see flow.hip.
+hipError_t launch_rf_noise(const void* z, const void* eps, const float* t, void* zt, int dtype, const int* cu_pieces,
+                           int n_samples, int frames, int n_tokens, int channels, hipStream_t stream);
+hipError_t launch_rf_loss(const void* v, const void* z, const void* eps, void* grad, float* row_sum,
+                          float* loss_sum, int dtype, const int* cu_pieces, int n_samples, int frames, int n_tokens,
+                          int channels, float grad_scale, hipStream_t stream);
+hipError_t launch_cfg_combine(const void* v, void* out, int* mismatched, int dtype, const int* cu_pieces,
+                              int n_pairs, int n_tokens, int channels, float scale, hipStream_t stream);
+
 }  // namespace mf

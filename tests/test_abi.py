@@ -173,3 +173,25 @@ def test_editing_workspace_sizes(lib):
     n, h = 1000, 4
     table3 = 640 * 40 * 8
     assert lib.mf_varlen_attn_workspace_size(n, h, 128, 3, 640, 0, 0) >= table3 + n * h * 128 * 2
+
+
+def test_flow_argument_errors(lib):
+    # mf_rf_noise(z, eps, t, zt, dtype, cu_pieces, n_samples, frames, n_tokens, channels, stream, trace)
+    assert lib.mf_rf_noise(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 1, 8, 96, None, None) == -2     # channels
+    assert lib.mf_rf_noise(FAKE, FAKE, FAKE, FAKE, 2, FAKE, 2, 1, 8, 128, None, None) == -2    # dtype
+    assert lib.mf_rf_noise(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 3, 8, 128, None, None) == -1    # frames
+    assert lib.mf_rf_noise(FAKE, FAKE, None, FAKE, 0, FAKE, 2, 1, 8, 128, None, None) == -1    # t
+    assert lib.mf_rf_noise(FAKE + 8, FAKE, FAKE, FAKE, 0, FAKE, 2, 1, 8, 128, None, None) == -1
+    assert lib.mf_rf_noise(FAKE, FAKE, FAKE, FAKE, 0, None, 2, 1, 8, 128, None, None) == -1
+    assert lib.mf_rf_noise(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 1, 0, 128, None, None) == 0
+    # mf_rf_loss(v, z, eps, grad, loss, dtype, cu, n_samples, frames, n, C, scale, ws, wsb, stream, trace)
+    assert lib.mf_rf_loss(FAKE, FAKE, FAKE, None, FAKE, 0, FAKE, 2, 1, 8, 128, 1.0, FAKE, 4, None, None) == -3
+    assert lib.mf_rf_loss(FAKE, FAKE, FAKE, None, None, 0, FAKE, 2, 1, 8, 128, 1.0, FAKE, 64, None, None) == -1
+    assert lib.mf_rf_loss(FAKE, FAKE, FAKE, FAKE + 4, FAKE, 0, FAKE, 2, 1, 8, 128, 1.0, FAKE, 64, None, None) == -1
+    assert lib.mf_rf_loss(FAKE, FAKE, FAKE, None, FAKE, 0, FAKE, 2, 1, 8, 128, float("nan"), FAKE, 64, None,
+                          None) == -1
+    assert lib.mf_rf_loss_workspace_size(1000) == 4096
+    # mf_cfg_combine(v, out, mismatched, dtype, cu, n_samples, n_pairs, n, C, scale, stream, trace)
+    assert lib.mf_cfg_combine(FAKE, FAKE, None, 0, FAKE, 3, 2, 8, 128, 3.0, None, None) == -1   # 2 pairs > 3 samples
+    assert lib.mf_cfg_combine(FAKE, FAKE, FAKE + 2, 0, FAKE, 4, 2, 8, 128, 3.0, None, None) == -1
+    assert lib.mf_cfg_combine(FAKE, FAKE, None, 0, FAKE, 4, 2, 8, 1000, 3.0, None, None) == -2
