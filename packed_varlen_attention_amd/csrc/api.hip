@@ -420,12 +420,13 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
                             const_cast<int*>(aq.pt), s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
-  e = tr.run("attn_bwd_delta", [&] { return mf::launch_attn_bwd_delta(a, o, dout, lse, delta, lse2, s); });
+  // dq first: it also writes Delta and the log2-scaled LSE that dkdv reads.
+  e = tr.run("attn_bwd_dq", [&] {
+    return mf::launch_attn_bwd_dq(aq, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, s);
+  });
   if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("attn_bwd_dkdv",
              [&] { return mf::launch_attn_bwd_dkdv(a, qr, kr, vb, dob, lse2, delta, dk, dv, s); });
-  if (e != hipSuccess) return MF_ERR_HIP;
-  e = tr.run("attn_bwd_dq", [&] { return mf::launch_attn_bwd_dq(aq, qr, kr, vb, dob, lse2, delta, dq, s); });
   return from_hip(e);
 }
 

@@ -1,7 +1,7 @@
 // Backward of packed block-diagonal attention with axial 2D RoPE.
 //
 // With P = softmax(scale * Qr Kr^T) recomputed from the forward's LSE:
-//   Delta = rowsum(dO * O)                       delta kernel (HBM-bound)
+//   Delta = rowsum(dO * O)                       dq kernel prologue (written for dkdv)
 //   dV = P^T dO,  dKr = scale * dS^T Qr          dkdv kernel, per 32 keys/wave
 //                                                (K in registers, V rows in LDS)
 //   dQr = scale * dS Kr                          dq kernel,   per 32 queries/wave
@@ -23,68 +23,6 @@ constexpr int kQB = 32;         // queries per dkdv LDS tile
 constexpr int kQT = kDqTile;    // queries per dq workgroup (32 per wave)
 constexpr int kDqWaves = kQT / 32;
 constexpr int kKT = 64;         // keys per dq LDS tile
-
-// Delta[h][t] = dot(dO[t][h], O[t][h]) and the log2-scaled LSE, for a tile of
-// kDeltaTokens tokens x kDeltaHeads heads per workgroup.  The rows of one token
-// are contiguous in O and dO, so the loads are coalesced 16-byte reads, four
-// rows in flight per lane; the dot products go through LDS and leave as
-// kDeltaTokens consecutive floats per head (the outputs are head-major).
-constexpr int kDeltaTokens = 32;
-constexpr int kDeltaHeads = 8;
-constexpr int kDeltaUnroll = 4;
-
-template <int D, typename T>
-__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                    const float* __restrict__ lse, float* __restrict__ delta,
-                                                    float* __restrict__ lse2, int n_tokens, int heads) {
-  constexpr int kLanesPerRow = D / 8;
-  constexpr int kRowsPerPass = 256 / kLanesPerRow;
-  constexpr int kRows = kDeltaTokens * kDeltaHeads;
-  static_assert(kRows % (kRowsPerPass * kDeltaUnroll) == 0, "whole unrolled passes");
-  __shared__ float sDot[kDeltaHeads][kDeltaTokens + 1];
-  const int t0 = blockIdx.x * kDeltaTokens;
-  const int h0 = blockIdx.y * kDeltaHeads;
-  const int hc = min(kDeltaHeads, heads - h0);
-  const int sub = threadIdx.x % kLanesPerRow;
-  for (int r0 = threadIdx.x / kLanesPerRow; r0 < kRows; r0 += kRowsPerPass * kDeltaUnroll) {
-    float a[kDeltaUnroll][8], b[kDeltaUnroll][8];
-#pragma unroll
-    for (int u = 0; u < kDeltaUnroll; ++u) {
-      const int r = r0 + u * kRowsPerPass;
-      const int hl = r % kDeltaHeads;
-      const int t = t0 + r / kDeltaHeads;
-      if (hl < hc && t < n_tokens) {
-        const long long row = static_cast<long long>(t) * heads + h0 + hl;
-        load8<T>(o + row * D + sub * 8, a[u]);
-        load8<T>(dout + row * D + sub * 8, b[u]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[u][j] = b[u][j] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kDeltaUnroll; ++u) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc += a[u][j] * b[u][j];
-#pragma unroll
-      for (int m = kLanesPerRow / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-      const int r = r0 + u * kRowsPerPass;
-      if (sub == 0) sDot[r % kDeltaHeads][r / kDeltaHeads] = acc;
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < kRows; e += 256) {
-    const int hl = e / kDeltaTokens;
-    const int tl = e % kDeltaTokens;
-    const int t = t0 + tl;
-    if (hl < hc && t < n_tokens) {
-      const size_t i = static_cast<size_t>(h0 + hl) * n_tokens + t;
-      delta[i] = sDot[hl][tl];
-      lse2[i] = lse[i] * kLog2e;
-    }
-  }
-}
 
 template <int D, typename TOut>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(
@@ -289,7 +227,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
 template <int D, typename TOut>
 __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
-    const uint16_t* __restrict__ dob, const float* __restrict__ lse2, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dob, const TOut* __restrict__ o, const TOut* __restrict__ dout,
+    const float* __restrict__ lse, float* __restrict__ lse2, float* __restrict__ delta,
     TOut* __restrict__ dq, const int* __restrict__ cu, const int* __restrict__ order, const int* __restrict__ pt,
     int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax, const float2* __restrict__ tab,
     int max_pos, float scale, float scale_log2) {
@@ -333,9 +272,31 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
     qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + qrow * D + e0));
     df[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dob + qrow * D + e0));
   }
+  // This query's row statistics, also written for dkdv (which runs after
+  // dq): Delta = dot(dO, O) over the row -- each lane half holds half of it
+  // -- and the LSE in log2 units.
   const size_t si = static_cast<size_t>(head) * n_tokens + s0 + min(qi, L - 1);
-  const float l2 = lse2[si];
-  const float dl = delta[si];
+  float part = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int e0 = 16 * kk + 8 * hh;
+    float a[8], g[8];
+    load8<TOut>(o + qrow * D + e0, a);
+    if constexpr (std::is_same<TOut, uint16_t>::value) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g[j] = static_cast<float>(df[kk][j]);  // bf16 dO as given
+    } else {
+      load8<TOut>(dout + qrow * D + e0, g);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part += a[j] * g[j];
+  }
+  const float dl = part + __shfl_xor(part, 32, 64);
+  const float l2 = lse[si] * kLog2e;
+  if (qok && hh == 0) {
+    delta[si] = dl;
+    lse2[si] = l2;
+  }
 
   const size_t hD = static_cast<size_t>(heads) * D;
   const uint16_t* kseg = kr + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
@@ -474,17 +435,6 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
   }
 }
 
-template <int D, typename T>
-hipError_t launch_delta_t(const AttnArgs& a, const void* o, const void* dout, const float* lse, float* delta,
-                          float* lse2, hipStream_t stream) {
-  if (a.n_tokens == 0 || a.n_heads == 0) return hipSuccess;
-  const dim3 grid((a.n_tokens + kDeltaTokens - 1) / kDeltaTokens, (a.n_heads + kDeltaHeads - 1) / kDeltaHeads);
-  if (grid.y > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((delta_kernel<D, T>), grid, dim3(256), 0, stream,
-                     static_cast<const T*>(o), static_cast<const T*>(dout), lse, delta, lse2, a.n_tokens, a.n_heads);
-  return hipGetLastError();
-}
-
 template <int D, typename TOut>
 hipError_t launch_dkdv_t(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,
                          const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
@@ -501,27 +451,20 @@ hipError_t launch_dkdv_t(const AttnArgs& a, const void* qr, const void* kr, cons
 
 template <int D, typename TOut>
 hipError_t launch_dq_t(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,
-                       const float* lse, const float* delta, void* dq, hipStream_t stream) {
+                       const void* o, const void* dout, const float* lse, float* lse2, float* delta, void* dq,
+                       hipStream_t stream) {
   const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kQT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((dq_kernel<D, TOut>), dim3(static_cast<unsigned>(blocks)), dim3(kDqWaves * 64), 0, stream,
                      static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
-                     static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob), lse, delta,
+                     static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob),
+                     static_cast<const TOut*>(o), static_cast<const TOut*>(dout), lse, lse2, delta,
                      static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
                      a.pos, a.nax, a.tab, a.max_pos, a.scale, a.scale * kLog2e);
   return hipGetLastError();
 }
 
 }  // namespace
-
-hipError_t launch_attn_bwd_delta(const AttnArgs& a, const void* o, const void* dout, const float* lse, float* delta,
-                                 float* lse2, hipStream_t stream) {
-  if (a.head_dim == 128)
-    return a.dtype == kDtypeBf16 ? launch_delta_t<128, uint16_t>(a, o, dout, lse, delta, lse2, stream)
-                                 : launch_delta_t<128, float>(a, o, dout, lse, delta, lse2, stream);
-  return a.dtype == kDtypeBf16 ? launch_delta_t<64, uint16_t>(a, o, dout, lse, delta, lse2, stream)
-                               : launch_delta_t<64, float>(a, o, dout, lse, delta, lse2, stream);
-}
 
 hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,
                                 const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
@@ -533,12 +476,14 @@ hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, const void* qr, const void* k
 }
 
 hipError_t launch_attn_bwd_dq(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,
-                              const float* lse, const float* delta, void* dq, hipStream_t stream) {
+                              const void* o, const void* dout, const float* lse, float* lse2, float* delta, void* dq,
+                              hipStream_t stream) {
   if (a.head_dim == 128)
-    return a.dtype == kDtypeBf16 ? launch_dq_t<128, uint16_t>(a, qr, kr, vb, dob, lse, delta, dq, stream)
-                                 : launch_dq_t<128, float>(a, qr, kr, vb, dob, lse, delta, dq, stream);
-  return a.dtype == kDtypeBf16 ? launch_dq_t<64, uint16_t>(a, qr, kr, vb, dob, lse, delta, dq, stream)
-                               : launch_dq_t<64, float>(a, qr, kr, vb, dob, lse, delta, dq, stream);
+    return a.dtype == kDtypeBf16
+               ? launch_dq_t<128, uint16_t>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream)
+               : launch_dq_t<128, float>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream);
+  return a.dtype == kDtypeBf16 ? launch_dq_t<64, uint16_t>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream)
+                               : launch_dq_t<64, float>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream);
 }
 
 }  // namespace mf

@@ -61,18 +61,17 @@ struct AttnArgs {
 hipError_t launch_attn_fwd(const AttnArgs& a, const void* q, const void* kr, const void* vb, void* o,
                            float* lse, hipStream_t stream);
 
-// delta = rowsum(dout * o), lse2 = lse * log2(e), both [H][N].
-hipError_t launch_attn_bwd_delta(const AttnArgs& a, const void* o, const void* dout, const float* lse, float* delta,
-                                 float* lse2, hipStream_t stream);
-
 // qr/kr rotated bf16, vb/dob bf16, lse2 in log2 units; outputs in a.dtype.
 hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, const void* qr, const void* kr, const void* vb,
                                 const void* dob, const float* lse, const float* delta, void* dk, void* dv,
                                 hipStream_t stream);
 
+// dq also writes the row statistics dkdv reads (so it runs first):
+// delta = rowsum(dout * o), lse2 = lse * log2(e), both [H][N].  o and dout
+// are the caller's tensors (a.dtype).
 hipError_t launch_attn_bwd_dq(const AttnArgs& a, const void* qr, const void* kr, const void* vb,
-                              const void* dob, const float* lse, const float* delta, void* dq,
-                              hipStream_t stream);
+                              const void* dob, const void* o, const void* dout, const float* lse, float* lse2,
+                              float* delta, void* dq, hipStream_t stream);
 
 // Rectified-flow noising / loss and the packed CFG combine over [N][C]
 // latent rows (C / 8 a power of two <= 64); see flow.hip.
