@@ -167,3 +167,16 @@ def test_full_size_sampled_rows(name):
     assert_close(got_l, ref_l, LSE_MAX, LSE_MAX, f"LSE {name} sampled")
     # every row of every head is a convex combination of its segment's V rows
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse[:, : c.n]).all()
+
+
+def test_more_segments_than_the_scheduler_sorts():
+    """Over 1024 segments the schedule keeps the given order instead of sorting
+    by length: results must not depend on that."""
+    rng = np.random.default_rng(77)
+    samples = [(int(rng.integers(0, 12)), int(rng.integers(0, 4)), int(rng.integers(0, 4))) for _ in range(1500)]
+    c = Case(samples, 1 << 20, 2, 64, "bf16", seed=28)
+    assert len(c.cu) - 1 > 1024
+    o, lse = _run(c)
+    ref_o, ref_l = _full_ref(c)
+    assert_close(host_f64(o)[: c.n], ref_o[: c.n], O_MAX, O_MEAN, "O 1500 segments")
+    assert_close(host_f64(lse)[:, : c.n], ref_l[:, : c.n], LSE_MAX, LSE_MAX, "LSE 1500 segments")
