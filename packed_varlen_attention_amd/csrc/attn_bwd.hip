@@ -33,11 +33,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     const float2* __restrict__ tab, int max_pos, float scale, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int CH = D / 8;
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kQB * kRowBytes;
-  constexpr int kRowsPerInst = 1024 / kRowBytes;
-  constexpr int kInstPerWave = kQB / kRowsPerInst / 4;
   // LDS: Q tiles [2], dO tiles [2], then per buffer 32 log2-LSE + 32 Delta
   __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes + 2 * 2 * kQB * 4 + kKB * kRowBytes];
 
@@ -67,31 +64,18 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   }
 
   // ---- global -> LDS copies of the Q / dO tiles and their row statistics.
-  const size_t hD = static_cast<size_t>(heads) * D;
-  const uint16_t* qseg = qr + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
-  const uint16_t* oseg = dob + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
+  const unsigned pitch = static_cast<unsigned>(heads) * D * 2;  // bytes per token row, < 2^24
+  const uint16_t* qseg = qr + (static_cast<size_t>(s0) * heads + head) * D;
+  const uint16_t* oseg = dob + (static_cast<size_t>(s0) * heads + head) * D;
   const float* stat_src = (lane < 32 ? lse2 : delta) + static_cast<size_t>(head) * n_tokens + s0;
-  int ld_row[kInstPerWave], ld_off[kInstPerWave];
-#pragma unroll
-  for (int r = 0; r < kInstPerWave; ++r) {
-    const int inst = wave * kInstPerWave + r;
-    ld_row[r] = inst * kRowsPerInst + lane / CH;
-    ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
-  }
+  const TileCopy<D, kQB, 4> copy(wave, lane, pitch);
   lds_char* const sQ0 = (lds_char*)(smem);
   lds_char* const sO0 = sQ0 + 2 * kTileBytes;
   lds_char* const sS0 = sQ0 + 4 * kTileBytes;  // [buf][lse2 x 32, delta x 32]
   lds_char* const sVb = sS0 + 2 * 2 * kQB * 4;   // V rows of this workgroup's keys
   auto load_tile = [&](int q0, int buf) {
-    const bool tail = q0 + kQB > L;
-#pragma unroll
-    for (int r = 0; r < kInstPerWave; ++r) {
-      const int row = tail ? min(q0 + ld_row[r], L - 1) : q0 + ld_row[r];
-      const size_t off = static_cast<size_t>(row) * hD + ld_off[r];
-      const int dst = buf * kTileBytes + (wave * kInstPerWave + r) * 1024;
-      __builtin_amdgcn_global_load_lds(qseg + off, sQ0 + dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(oseg + off, sO0 + dst, 16, 0, 0);
-    }
+    copy(qseg, q0, L, sQ0 + buf * kTileBytes);
+    copy(oseg, q0, L, sO0 + buf * kTileBytes);
     if (wave == 0) {
       const int row = min(q0 + (lane & 31), L - 1);
       __builtin_amdgcn_global_load_lds(stat_src + row, sS0 + buf * 2 * kQB * 4, 4, 0, 0);
@@ -151,14 +135,13 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) acc = mfma32(row_frag(sQ, kk), kf[kk], acc);
+    if (q0 + kQB > L) {  // only the segment's last tile holds rows past its end: exp2(-inf) = 0
+#pragma unroll
+      for (int g = 0; g < 2; ++g) mask_rows8(acc, g, L - (q0 + 16 * g + 8 * hh), -INFINITY);
+    }
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(acc[i], scale_log2, -st[acc_row(i, hh)]));
-    if (q0 + kQB > L) {  // only the segment's last tile holds rows past its end
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (q0 + acc_row(i, hh) >= L) p[i] = 0.f;
-    }
     bf16x8 pb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) pb[i >> 3][i & 7] = static_cast<__bf16>(p[i]);
@@ -190,16 +173,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     __syncthreads();
   };
   {
-    const uint16_t* vseg = vb + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
-    constexpr int kVInst = kKB / kRowsPerInst / 4;
-#pragma unroll
-    for (int r = 0; r < kVInst; ++r) {
-      const int inst = wave * kVInst + r;
-      const int row = inst * kRowsPerInst + lane / CH;
-      const int chunk = (lane % CH) ^ Tile<D>::swz(row);
-      const int vrow = min(kbase + row, L - 1);
-      __builtin_amdgcn_global_load_lds(vseg + static_cast<size_t>(vrow) * hD + chunk * 8, sVb + inst * 1024, 16, 0, 0);
-    }
+    const uint16_t* vseg = vb + (static_cast<size_t>(s0) * heads + head) * D;
+    const TileCopy<D, kKB, 4> copy_v(wave, lane, pitch);
+    copy_v(vseg, kbase, L, sVb);
   }
   load_tile(0, 0);
   wait_vmem();
@@ -234,12 +210,9 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
     int max_pos, float scale, float scale_log2) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int CH = D / 8;
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kKT * kRowBytes;
-  constexpr int kRowsPerInst = 1024 / kRowBytes;
-  constexpr int kInstPerWave = kKT / kRowsPerInst / kDqWaves;
-  static_assert(kInstPerWave >= 1, "every wave issues whole tile copies");
+  constexpr int kInstPerWave = TileCopy<D, kKT, kDqWaves>::kCopies;  // copy instructions per wave and tile
   // LDS: three K and three V tiles, six separate objects so the compiler can
   // tell the tile being read from the tiles being filled by in-flight copies.
   __shared__ __attribute__((aligned(16))) char smemK0[kTileBytes];
@@ -298,28 +271,15 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
     lse2[si] = l2;
   }
 
-  const size_t hD = static_cast<size_t>(heads) * D;
-  const uint16_t* kseg = kr + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
-  const uint16_t* vseg = vb + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
-  int ld_row[kInstPerWave], ld_off[kInstPerWave];
-#pragma unroll
-  for (int r = 0; r < kInstPerWave; ++r) {
-    const int inst = wave * kInstPerWave + r;
-    ld_row[r] = inst * kRowsPerInst + lane / CH;
-    ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
-  }
+  const unsigned pitch = static_cast<unsigned>(heads) * D * 2;  // bytes per token row, < 2^24
+  const uint16_t* kseg = kr + (static_cast<size_t>(s0) * heads + head) * D;
+  const uint16_t* vseg = vb + (static_cast<size_t>(s0) * heads + head) * D;
+  const TileCopy<D, kKT, kDqWaves> copy(wave, lane, pitch);
   lds_char* const sKb[3] = {(lds_char*)(smemK0), (lds_char*)(smemK1), (lds_char*)(smemK2)};
   lds_char* const sVb[3] = {(lds_char*)(smemV0), (lds_char*)(smemV1), (lds_char*)(smemV2)};
   auto load_tile = [&](int k0, lds_char* dK, lds_char* dV) {
-    const bool tail = k0 + kKT > L;
-#pragma unroll
-    for (int r = 0; r < kInstPerWave; ++r) {
-      const int row = tail ? min(k0 + ld_row[r], L - 1) : k0 + ld_row[r];
-      const size_t off = static_cast<size_t>(row) * hD + ld_off[r];
-      const int dst = (wave * kInstPerWave + r) * 1024;
-      __builtin_amdgcn_global_load_lds(kseg + off, dK + dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vseg + off, dV + dst, 16, 0, 0);
-    }
+    copy(kseg, k0, L, dK);
+    copy(vseg, k0, L, dV);
   };
   int roff[NKK];
 #pragma unroll
@@ -382,14 +342,13 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
         sacc = mfma32(ka, qf[kk], sacc);
         dpacc = mfma32(va, df[kk], dpacc);
       }
+      if (k0 + kKT > L) {  // only the segment's last tile holds keys past its end: exp2(-inf) = 0
+#pragma unroll
+        for (int g = 0; g < 2; ++g) mask_rows8(sacc, g, L - (k0 + 32 * kb + 16 * g + 8 * hh), -INFINITY);
+      }
       float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, -l2));
-      if (k0 + kKT > L) {  // only the segment's last tile holds keys past its end
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (k0 + kb * 32 + acc_row(i, hh) >= L) p[i] = 0.f;
-      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) dsb[2 * kb + (i >> 3)][i & 7] = static_cast<__bf16>(p[i] * (dpacc[i] - dl));
     }

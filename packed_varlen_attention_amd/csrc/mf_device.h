@@ -62,6 +62,20 @@ __device__ __forceinline__ int perm32(int m) {
 // Tile row of accumulator element i for lane half h (after perm32 rows).
 __device__ __forceinline__ int acc_row(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
 
+// Masks the 8 accumulator elements of group g (elements 8g .. 8g + 7, the
+// rows acc_row(8g + c, h) = 16g + 8h + c of a 32-row block): element c is set
+// to `fill` unless c < valid.  Built from bit tests instead of compares, so
+// it holds no lane masks in scalar registers.
+__device__ __forceinline__ void mask_rows8(f32x16& acc, int g, int valid, float fill) {
+  const unsigned keep_bits = (1u << min(max(valid, 0), 8)) - 1u;  // bit c: element c is kept
+  const int fill_bits = __float_as_int(fill);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int keep = static_cast<int>(keep_bits << (31 - c)) >> 31;  // 0 or -1
+    acc[8 * g + c] = __int_as_float((__float_as_int(acc[8 * g + c]) & keep) | (fill_bits & ~keep));
+  }
+}
+
 // A [rows][D] bf16 tile in LDS, rows of D*2 bytes, 16-byte chunks XOR-swizzled
 // per row so that both row-fragment and transpose reads spread over banks.
 template <int D>
@@ -112,29 +126,53 @@ __device__ __forceinline__ bf16x8 lds_col_frag(const lds_char* tile, int rbase, 
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Asynchronous copy of one [rows][D] bf16 tile from global memory straight
-// into a swizzled LDS tile (global_load_lds_dwordx4: lane i of a wave lands
-// its 16 bytes at the wave's LDS base + 16 i).  The wave covers 1 KB per
-// instruction; the swizzle is applied by choosing which global chunk each
-// lane fetches.  `rows` must be a multiple of 4 * (1024 / (D * 2)); the caller
-// waits on vmcnt and then a barrier before the tile is read.
-// row_addr(r) gives the global address of tile row r (already clamped).
-template <int D, int kRows, int kWaves, typename RowAddr>
-__device__ __forceinline__ void tile_load_async(lds_char* tile, int wave, int lane, RowAddr row_addr) {
-  constexpr int kRowsPerInst = 1024 / (D * 2);
-  constexpr int kInst = kRows / kRowsPerInst;
-  static_assert(kInst % kWaves == 0, "tile rows must split evenly over the waves");
-  constexpr int kPerWave = kInst / kWaves;
-  constexpr int CH = D / 8;
-#pragma unroll
-  for (int r = 0; r < kPerWave; ++r) {
-    const int inst = wave * kPerWave + r;
-    const int row = inst * kRowsPerInst + lane / CH;
-    const int chunk = (lane % CH) ^ Tile<D>::swz(row);
-    const uint16_t* src = row_addr(row) + chunk * 8;
-    __builtin_amdgcn_global_load_lds(src, tile + inst * 1024, 16, 0, 0);
+// Asynchronous copies of a [kRows][D] bf16 tile from a row-strided global
+// matrix straight into a swizzled LDS tile (global_load_lds_dwordx4: lane i
+// of a wave lands its 16 bytes at the wave's LDS base + 16 i, so a copy
+// instruction fills 1 KB = kRowsPerInst whole rows; the swizzle is applied by
+// choosing which global chunk each lane fetches).
+//
+// Copy r of wave w fills tile rows kStride r + kRowsPerInst w + lane / (D/8),
+// kStride = kRowsPerInst * kWaves.  kStride is a multiple of the swizzle's
+// 16-row period, so all copies of a lane fetch the same chunk.  The source
+// is a block-uniform tile base (scalar registers) plus a 32-bit lane offset
+// per copy; rows at or past `valid` re-read row valid - 1 (the caller masks
+// what they feed), a clamp taken on the byte offset itself:
+// min(row pitch + chunk, last pitch + chunk) = min(row, last) pitch + chunk,
+// so each copy costs a lane one add and one min.  The caller waits on
+// vmcnt, then a barrier, before the tile is read.
+template <int D, int kRows, int kWaves>
+struct TileCopy {
+  static constexpr int kRowsPerInst = 1024 / (D * 2);
+  static constexpr int kStride = kRowsPerInst * kWaves;
+  static constexpr int kCopies = kRows / kStride;  // copy instructions per wave and tile
+  static_assert(kCopies >= 1 && kRows % kStride == 0, "tile rows must split evenly over the waves");
+  static_assert(kStride % 16 == 0, "the chunk swizzle repeats every 16 rows");
+
+  unsigned off0;   // byte offset of this lane's chunk in copy 0, from the tile's first row
+  unsigned chunk;  // byte offset of the lane's swizzled 16-byte chunk inside a row
+  unsigned pitch;  // bytes per matrix row, below 2^24
+  int wave;        // wave-uniform
+
+  __device__ __forceinline__ TileCopy(int wave_, int lane, unsigned pitch_) : pitch(pitch_), wave(wave_) {
+    const int row = wave * kRowsPerInst + lane / (D / 8);
+    chunk = static_cast<unsigned>((lane % (D / 8)) ^ Tile<D>::swz(row)) * 16u;
+    off0 = static_cast<unsigned>(row) * pitch + chunk;
   }
-}
+  // Copy matrix rows [r0, r0 + kRows) of `base` into `tile`; 0 <= r0 < valid.
+  __device__ __forceinline__ void operator()(const void* base, int r0, int valid, lds_char* tile) const {
+    const char* src = static_cast<const char*>(base) + static_cast<size_t>(r0) * pitch;  // block-uniform
+    const unsigned last = static_cast<unsigned>(valid - 1 - r0) * pitch + chunk;
+#pragma unroll
+    for (int r = 0; r < kCopies; ++r) {
+      unsigned o = min(off0 + static_cast<unsigned>(r * kStride) * pitch, last);
+      // Opaque to the optimiser, so the add stays a 32-bit lane offset on a
+      // scalar base instead of being folded into a 64-bit per-lane select.
+      asm("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(src + o, tile + (r * kWaves + wave) * 1024, 16, 0, 0);
+    }
+  }
+};
 
 // Wait until this wave's outstanding global loads (including loads into LDS)
 // have completed.
