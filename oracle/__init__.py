@@ -24,7 +24,10 @@ Sources (the Mage-Flow pages):
   target -- paper section 3.2.2 "Conditioning and rectified-flow training"
   (hyper.ai summary); paperlayer.ai summary, "Method";
 * the rectified flow-matching objective on the packed latents and the packed
-  CFG combine -- ``oracle.flow``.
+  CFG combine -- ``oracle.flow``;
+* the attention sub-block's fused chains (adaptive normalisation, the
+  modality-specific QKV projection with the rotary embedding, the gated
+  residual) -- ``oracle.block``.
 
 The pages fix no formula for the rotation, the position assignment, the
 softmax scale or the log-sum-exp.  The readings taken here are listed in each
@@ -37,3 +40,4 @@ from .pack import pack, positions, gather, pack_edit, positions_edit, gather_edi
 from .rope import inv_freq, rope2d, rope3d, rope_axes, blocks3d  # noqa: F401
 from .attention import attn_fwd, attn_bwd, attn_fwd_rows  # noqa: F401
 from . import flow  # noqa: F401
+from . import block  # noqa: F401

@@ -39,6 +39,14 @@ STREAM_Q = 1
 STREAM_K = 2
 STREAM_V = 3
 STREAM_DO = 4
+# attention sub-block chains (adaptive norm, projections, gated residual)
+STREAM_X = 20
+STREAM_MOD = 21      # + 0 shift, + 1 scale, + 2 gate
+STREAM_WQKV = 24     # + modality (0 text, 1 image)
+STREAM_BQKV = 26     # + modality
+STREAM_WO = 28       # + modality
+STREAM_BO = 30       # + modality
+STREAM_O = 32
 
 Sample = Tuple[int, int, int]  # (text_len, grid_h, grid_w)
 
@@ -220,3 +228,29 @@ def qkv(seed: int, n_tokens: int, n_heads: int, head_dim: int, dtype: str):
 
 def dout(seed: int, n_tokens: int, n_heads: int, head_dim: int, dtype: str):
     return normal(seed, STREAM_DO, (n_tokens, n_heads, head_dim), dtype)
+
+
+def block_inputs(seed: int, n_tokens: int, n_samples: int, channels: int, dtype: str = "bf16"):
+    """Seeded inputs of the attention sub-block chains.
+
+    x [N][C] residual stream and o [N][C] attention output ~ N(0, 1);
+    shift, scale, gate [S][2][C] float32 ~ N(0, 0.1^2) (modality 0 text,
+    1 image); per modality W_qkv [3C][C] and W_o [C][C] ~ N(0, 1/C) (unit-
+    variance outputs), biases b_qkv [3C] and b_o [C] float32 ~ N(0, 0.02^2).
+    Matrices are bf16 bit patterns for dtype "bf16".
+    """
+    c = int(channels)
+    w_scale = 1.0 / np.sqrt(c)
+    out = {
+        "x": normal(seed, STREAM_X, (n_tokens, c), dtype),
+        "o": normal(seed, STREAM_O, (n_tokens, c), dtype),
+        "shift": normal(seed, STREAM_MOD, (n_samples, 2, c), "f32", 0.1),
+        "scale": normal(seed, STREAM_MOD + 1, (n_samples, 2, c), "f32", 0.1),
+        "gate": normal(seed, STREAM_MOD + 2, (n_samples, 2, c), "f32", 0.1),
+    }
+    for m in range(2):
+        out[f"w_qkv{m}"] = normal(seed, STREAM_WQKV + m, (3 * c, c), dtype, w_scale)
+        out[f"b_qkv{m}"] = normal(seed, STREAM_BQKV + m, (3 * c,), "f32", 0.02)
+        out[f"w_o{m}"] = normal(seed, STREAM_WO + m, (c, c), dtype, w_scale)
+        out[f"b_o{m}"] = normal(seed, STREAM_BO + m, (c,), "f32", 0.02)
+    return out
