@@ -71,7 +71,7 @@ typedef int32_t mf_status;
 #define MF_BF16 0
 #define MF_F32 1
 
-#define MF_ABI_VERSION 2
+#define MF_ABI_VERSION 3
 
 /* One sample descriptor: text tokens, then a grid_h x grid_w latent grid. */
 typedef struct mf_sample {
@@ -352,6 +352,82 @@ mf_status mf_cfg_combine(const void* v, void* out, int32_t* mismatched, int32_t 
                          const int32_t* cu_pieces, int32_t n_samples, int32_t n_pairs,
                          int32_t n_tokens, int32_t channels, float scale, void* stream,
                          mf_trace* trace);
+
+/*
+ * The attention sub-block's fused chains around the packed joint attention.
+ * The backbone follows MMDiT: joint self-attention over the concatenated
+ * text and image tokens, with normalisation and projection layers specific
+ * to each modality (Mage-Flow paper section 3.2.1, paperlayer.ai summary;
+ * ai.thesatyajit.com explainer, Figure 5 caption); the training system fuses
+ * the blocks' chains of adaptive normalisation, rotary embeddings and gated
+ * residual updates (paper section 3.3 "Training Infrastructure").
+ *
+ * Rows are tokens in packed order: activations are bf16 [n_tokens][channels]
+ * (channels = n_heads x head_dim), 16-byte aligned.  cu_pieces is the
+ * packer's output for the same samples (frames = 1: mf_pack, frames = 2:
+ * mf_pack_edit); the first piece of a sample is its text (modality 0), the
+ * other pieces are image grids (modality 1).  Per-sample modulation vectors
+ * shift, scale, gate are device float [n_samples][2][channels] (16-byte
+ * aligned), indexed by (sample, modality).  Weights are bf16 [out][in]
+ * (row-major, 16-byte aligned), one matrix per modality; biases are device
+ * float[out] or NULL.  Only dtype MF_BF16 exists here.
+ *
+ * Size limits: channels a multiple of 256 (mf_adaln_modulate: of 512, at most
+ * 8192); head_dim 64 or 128; n_heads <= 65535.  Rows of cu_pieces outside
+ * [0, n_tokens] are clamped away on the device (an inconsistent cu_pieces
+ * yields unwritten rows, never an out-of-bounds access).
+ */
+
+/* Bytes of workspace mf_qkv_rope and mf_out_gated_residual need (tile table
+ * of (frames + 1) n_samples + 1 ints, then, for mf_qkv_rope, the rotary table
+ * of max_pos positions). */
+size_t mf_block_workspace_size(int32_t n_samples, int32_t frames, int32_t head_dim, int32_t max_pos);
+
+/*
+ * mf_adaln_modulate -- h = LN(x) * (1 + scale[s][m]) + shift[s][m] per token
+ * of sample s, modality m.  LN is LayerNorm over the channels without an
+ * affine of its own: population variance, statistics in fp32, eps as given
+ * (1e-6 is the DiT convention).  h may be x (in place).  Rows outside every
+ * piece are normalised without modulation.
+ */
+mf_status mf_adaln_modulate(const void* x, const float* shift, const float* scale, void* h,
+                            const int32_t* cu_pieces, int32_t n_samples, int32_t frames,
+                            int32_t n_tokens, int32_t channels, float eps, void* stream,
+                            mf_trace* trace);
+
+/*
+ * mf_qkv_rope -- [q | k | v] = h W_m^T + b_m with the token's modality m
+ * (W_m bf16 [3 channels][channels], b_m float[3 channels] or NULL), q and k
+ * rotated by the token's position, all three written bf16
+ * [n_tokens][n_heads][head_dim] (q, k, v must not overlap h).  pos is the
+ * packer's positions ([n_tokens][2] with nax = 2, [n_tokens][3] with nax = 3,
+ * the same rotation as mf_rope2d_apply / mf_rope3d_apply with theta and
+ * max_pos), or NULL for no rotation.  The rotated q and k feed
+ * mf_varlen_attn_fwd with pos = NULL; its backward then returns gradients
+ * with respect to the rotated q and k.
+ * workspace  >= mf_block_workspace_size(n_samples, frames, head_dim, max_pos)
+ *            bytes, 256-byte aligned.
+ */
+mf_status mf_qkv_rope(const void* h, const void* w_text, const void* w_image, const float* b_text,
+                      const float* b_image, void* q, void* k, void* v, const int32_t* cu_pieces,
+                      int32_t n_samples, int32_t frames, const int32_t* pos, int32_t nax,
+                      double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                      int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream,
+                      mf_trace* trace);
+
+/*
+ * mf_out_gated_residual -- y = x + gate[s][m] * (o W_o,m^T + b_o,m) with the
+ * token's sample s and modality m (W_o,m bf16 [channels][channels], b_o,m
+ * float[channels] or NULL).  o is the attention output ([N][H][D] is
+ * [N][channels]); y may be x (in place) but must not overlap o.
+ * workspace  >= mf_block_workspace_size(n_samples, frames, 64, 0) bytes,
+ *            256-byte aligned.
+ */
+mf_status mf_out_gated_residual(const void* o, const void* x, const void* w_text, const void* w_image,
+                                const float* b_text, const float* b_image, const float* gate, void* y,
+                                const int32_t* cu_pieces, int32_t n_samples, int32_t frames,
+                                int32_t n_tokens, int32_t channels, void* workspace,
+                                size_t workspace_bytes, void* stream, mf_trace* trace);
 
 /*
  * mf_mfma_probe -- measurement helper, not a step of the path: the sustained

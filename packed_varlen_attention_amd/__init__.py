@@ -10,11 +10,12 @@ from ._binding import (  # noqa: F401
     MF_ERR_WORKSPACE, MF_OK, MFError, abi_version, dtype_code, load_library, mf_mfma_probe, mf_pack, mf_pack_edit,
     mf_rope3d_apply, mf_rope3d_workspace_size,
     mf_rope2d_apply, mf_rope2d_workspace_size, mf_varlen_attn_bwd, mf_varlen_attn_fwd,
-    mf_varlen_attn_workspace_size, status_string,
+    mf_varlen_attn_workspace_size, status_string, mf_adaln_modulate, mf_block_workspace_size, mf_out_gated_residual,
+    mf_qkv_rope,
 )
 from .api import (  # noqa: F401
     PROBE_VECTORS, PackResult, attn_bwd, attn_fwd, cfg_combine, mfma_probe, pack, pack_edit, rf_loss, rf_noise,
-    rope2d_apply, rope3d_apply,
+    rope2d_apply, rope3d_apply, adaln_modulate, block_workspace, out_gated_residual, qkv_rope,
 )
 
 load_library()

@@ -30,7 +30,7 @@ EXPORTED = (
     "mf_rope2d_apply", "mf_varlen_attn_workspace_size", "mf_varlen_attn_fwd",
     "mf_varlen_attn_bwd", "mf_mfma_probe", "mf_pack_edit", "mf_rope3d_workspace_size", "mf_rope3d_apply",
     "mf_varlen_attn3d_fwd", "mf_varlen_attn3d_bwd", "mf_rf_noise", "mf_rf_loss_workspace_size", "mf_rf_loss",
-    "mf_cfg_combine",
+    "mf_cfg_combine", "mf_block_workspace_size", "mf_adaln_modulate", "mf_qkv_rope", "mf_out_gated_residual",
 )
 
 
@@ -140,6 +140,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                _vp]
     lib.mf_cfg_combine.restype = _i32
     lib.mf_cfg_combine.argtypes = [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
+    lib.mf_block_workspace_size.restype = _sz
+    lib.mf_block_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
+    lib.mf_adaln_modulate.restype = _i32
+    lib.mf_adaln_modulate.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
+    lib.mf_qkv_rope.restype = _i32
+    lib.mf_qkv_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _dbl, _i32,
+                                _i32, _i32, _i32, _vp, _sz, _vp, _vp]
+    lib.mf_out_gated_residual.restype = _i32
+    lib.mf_out_gated_residual.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp,
+                                          _sz, _vp, _vp]
     _lib = lib
     return lib
 
@@ -328,3 +338,35 @@ def mf_cfg_combine(v, out, mismatched, cu_pieces, n_samples: int, n_pairs: int, 
     _check(lib().mf_cfg_combine(_ptr(v), _ptr(out), _ptr(mismatched), dtype_code(v), _ptr(cu_pieces),
                                 int(n_samples), int(n_pairs), int(n), int(c), float(scale), _stream(stream),
                                 _trace(trace)), "mf_cfg_combine")
+
+
+def mf_block_workspace_size(n_samples: int, frames: int, head_dim: int, max_pos: int) -> int:
+    return int(lib().mf_block_workspace_size(int(n_samples), int(frames), int(head_dim), int(max_pos)))
+
+
+def mf_adaln_modulate(x, shift, scale, h, cu_pieces, n_samples: int, frames: int, eps: float = 1e-6, stream=None,
+                      trace=None) -> None:
+    n, c = x.shape
+    _check(lib().mf_adaln_modulate(_ptr(x), _ptr(shift), _ptr(scale), _ptr(h), _ptr(cu_pieces), int(n_samples),
+                                   int(frames), int(n), int(c), float(eps), _stream(stream), _trace(trace)),
+           "mf_adaln_modulate")
+
+
+def mf_qkv_rope(h, w_text, w_image, b_text, b_image, q, k, v, cu_pieces, n_samples: int, frames: int, pos,
+                theta: float, max_pos: int, workspace, stream=None, trace=None) -> None:
+    n, heads, d = q.shape
+    nax = int(pos.shape[-1]) if pos is not None else 2
+    _check(lib().mf_qkv_rope(_ptr(h), _ptr(w_text), _ptr(w_image), _ptr(b_text), _ptr(b_image), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(cu_pieces), int(n_samples), int(frames), _ptr(pos), nax, float(theta),
+                             int(max_pos), int(n), int(heads), int(d), _ptr(workspace),
+                             int(workspace.numel() * workspace.element_size()), _stream(stream), _trace(trace)),
+           "mf_qkv_rope")
+
+
+def mf_out_gated_residual(o, x, w_text, w_image, b_text, b_image, gate, y, cu_pieces, n_samples: int, frames: int,
+                          workspace, stream=None, trace=None) -> None:
+    n, c = x.shape
+    _check(lib().mf_out_gated_residual(_ptr(o), _ptr(x), _ptr(w_text), _ptr(w_image), _ptr(b_text), _ptr(b_image),
+                                       _ptr(gate), _ptr(y), _ptr(cu_pieces), int(n_samples), int(frames), int(n),
+                                       int(c), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                       _stream(stream), _trace(trace)), "mf_out_gated_residual")

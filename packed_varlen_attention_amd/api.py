@@ -172,3 +172,46 @@ def cfg_combine(v: torch.Tensor, cu_pieces: torch.Tensor, n_samples: int, n_pair
     mismatched = torch.zeros(1, dtype=torch.int32, device=v.device)
     B.mf_cfg_combine(v, o, mismatched, cu_pieces, n_samples, n_pairs, scale, stream, trace)
     return o, mismatched
+
+
+def block_workspace(n_samples: int, frames: int, head_dim: int, max_pos: int, device) -> torch.Tensor:
+    nbytes = max(B.mf_block_workspace_size(n_samples, frames, head_dim, max_pos), 256)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def adaln_modulate(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, cu_pieces: torch.Tensor,
+                   n_samples: int, frames: int = 1, eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+                   stream=None, trace=None) -> torch.Tensor:
+    """h = LN(x) (1 + scale[s][m]) + shift[s][m] over packed bf16 [N][C] rows."""
+    h = torch.empty_like(x) if out is None else out
+    B.mf_adaln_modulate(x, shift, scale, h, cu_pieces, n_samples, frames, eps, stream, trace)
+    return h
+
+
+def qkv_rope(h: torch.Tensor, w: Tuple[torch.Tensor, torch.Tensor],
+             b: Tuple[Optional[torch.Tensor], Optional[torch.Tensor]], cu_pieces: torch.Tensor, n_samples: int,
+             frames: int, pos: Optional[torch.Tensor], n_heads: int, theta: float = 10000.0, max_pos: int = 1,
+             out=None, workspace: Optional[torch.Tensor] = None, stream=None, trace=None):
+    """(q, k, v) bf16 [N][H][D]: the modality's projection of h, q and k rotated by pos."""
+    n, c = h.shape
+    d = c // n_heads
+    if out is None:
+        out = tuple(torch.empty((n, n_heads, d), dtype=h.dtype, device=h.device) for _ in range(3))
+    if workspace is None:
+        workspace = block_workspace(n_samples, frames, d, max_pos if pos is not None else 0, h.device)
+    B.mf_qkv_rope(h, w[0], w[1], b[0], b[1], out[0], out[1], out[2], cu_pieces, n_samples, frames, pos, theta,
+                  max_pos, workspace, stream, trace)
+    return out
+
+
+def out_gated_residual(o: torch.Tensor, x: torch.Tensor, w: Tuple[torch.Tensor, torch.Tensor],
+                       b: Tuple[Optional[torch.Tensor], Optional[torch.Tensor]], gate: torch.Tensor,
+                       cu_pieces: torch.Tensor, n_samples: int, frames: int = 1, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None, trace=None) -> torch.Tensor:
+    """y = x + gate[s][m] (o W_o,m^T + b_o,m); out may be x."""
+    y = torch.empty_like(x) if out is None else out
+    if workspace is None:
+        workspace = block_workspace(n_samples, frames, 64, 0, x.device)
+    B.mf_out_gated_residual(o, x, w[0], w[1], b[0], b[1], gate, y, cu_pieces, n_samples, frames, workspace, stream,
+                            trace)
+    return y

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmf.so")
-SOURCES = ["api.hip", "pack.hip", "rope.hip", "sched.hip", "attn_fwd.hip", "attn_bwd.hip", "flow.hip", "probe.hip"]
+SOURCES = ["api.hip", "pack.hip", "rope.hip", "sched.hip", "attn_fwd.hip", "attn_bwd.hip", "flow.hip", "block.hip",
+           "probe.hip"]
 ARCH = "gfx950"
 
 

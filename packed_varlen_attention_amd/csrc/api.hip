@@ -561,3 +561,130 @@ mf_status mf_cfg_combine(const void* v, void* out, int32_t* mismatched, int32_t 
 }
 
 }  // extern "C"
+
+// The attention sub-block's fused chains (adaptive norm, QKV projection with
+// the rotary embedding, output projection with the gated residual).
+
+namespace {
+
+size_t block_tiles_bytes(int32_t n_samples, int32_t frames) {
+  return align_up((static_cast<size_t>(n_samples) * (frames + 1) + 1) * sizeof(int32_t));
+}
+
+mf_status check_block_common(const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
+                             int32_t channels) {
+  if (cu_pieces == nullptr || n_samples < 0 || n_tokens < 0 || (frames != 1 && frames != 2))
+    return MF_ERR_INVALID_ARG;
+  if (static_cast<long long>(n_samples) * (frames + 1) >= 0x7fffffffLL) return MF_ERR_INVALID_ARG;
+  if (channels < 256 || channels % 256 != 0 || channels > 65535 * 128) return MF_ERR_UNSUPPORTED;
+  return MF_OK;
+}
+
+bool aligned16_or_null(const void* p) { return p == nullptr || aligned16(p); }
+
+}  // namespace
+
+extern "C" {
+
+size_t mf_block_workspace_size(int32_t n_samples, int32_t frames, int32_t head_dim, int32_t max_pos) {
+  if (n_samples < 0 || (frames != 1 && frames != 2)) return 0;
+  if (static_cast<long long>(n_samples) * (frames + 1) >= 0x7fffffffLL) return 0;
+  size_t total = block_tiles_bytes(n_samples, frames);
+  if (max_pos > 0 && (head_dim == 64 || head_dim == 128))
+    total += align_up(static_cast<size_t>(max_pos) * mf::rope_table_width(head_dim, 3) * sizeof(float2));
+  return total;
+}
+
+mf_status mf_adaln_modulate(const void* x, const float* shift, const float* scale, void* h,
+                            const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
+                            int32_t channels, float eps, void* stream, mf_trace* trace) {
+  mf_status st = check_block_common(cu_pieces, n_samples, frames, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (channels % 512 != 0 || channels > 8192) return MF_ERR_UNSUPPORTED;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (!(eps > 0.0f) || isinf(eps)) return MF_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MF_OK;
+  if (x == nullptr || h == nullptr || !aligned16(x) || !aligned16(h)) return MF_ERR_INVALID_ARG;
+  if (n_samples > 0 && (shift == nullptr || scale == nullptr || !aligned16(shift) || !aligned16(scale)))
+    return MF_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Tracer tr(trace, s);
+  return from_hip(tr.run("adaln", [&] {
+    return mf::launch_adaln(x, shift, scale, cu_pieces, n_samples, frames, n_tokens, channels, eps, h, s);
+  }));
+}
+
+mf_status mf_qkv_rope(const void* h, const void* w_text, const void* w_image, const float* b_text,
+                      const float* b_image, void* q, void* k, void* v, const int32_t* cu_pieces, int32_t n_samples,
+                      int32_t frames, const int32_t* pos, int32_t nax, double theta, int32_t max_pos,
+                      int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* workspace, size_t workspace_bytes,
+                      void* stream, mf_trace* trace) {
+  if (head_dim != 64 && head_dim != 128) return MF_ERR_UNSUPPORTED;
+  if (n_heads < 1 || n_heads > 65535) return MF_ERR_INVALID_ARG;
+  const int32_t channels = n_heads * head_dim;
+  mf_status st = check_block_common(cu_pieces, n_samples, frames, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (pos != nullptr) {
+    if (nax != 2 && nax != 3) return MF_ERR_INVALID_ARG;
+    if (max_pos < 1 || !(theta > 0.0) || isinf(theta)) return MF_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(pos) & (nax == 2 ? 7u : 3u)) != 0) return MF_ERR_INVALID_ARG;
+  }
+  if (n_tokens == 0) return MF_OK;
+  if (h == nullptr || q == nullptr || k == nullptr || v == nullptr || w_text == nullptr || w_image == nullptr)
+    return MF_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w_text) ||
+      !aligned16(w_image) || !aligned16_or_null(b_text) || !aligned16_or_null(b_image))
+    return MF_ERR_INVALID_ARG;
+  const size_t need = mf_block_workspace_size(n_samples, frames, head_dim, pos != nullptr ? max_pos : 0);
+  if (workspace_bytes < need) return MF_ERR_WORKSPACE;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int* tstart = reinterpret_cast<int*>(ws);
+  float2* tab = reinterpret_cast<float2*>(ws + block_tiles_bytes(n_samples, frames));
+  const int n_pieces = (frames + 1) * n_samples;
+  Tracer tr(trace, s);
+  hipError_t e = tr.run("piece_tiles", [&] { return mf::launch_piece_tiles(cu_pieces, n_pieces, n_tokens, tstart, s); });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  if (pos != nullptr) {
+    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, nax, theta, s); });
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
+  return from_hip(tr.run("qkv_rope", [&] {
+    return mf::launch_qkv_rope(h, w_text, w_image, b_text, b_image, cu_pieces, tstart, n_samples, frames, n_tokens,
+                               n_heads, head_dim, pos, nax, tab, max_pos, q, k, v, s);
+  }));
+}
+
+mf_status mf_out_gated_residual(const void* o, const void* x, const void* w_text, const void* w_image,
+                                const float* b_text, const float* b_image, const float* gate, void* y,
+                                const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
+                                int32_t channels, void* workspace, size_t workspace_bytes, void* stream,
+                                mf_trace* trace) {
+  mf_status st = check_block_common(cu_pieces, n_samples, frames, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MF_OK;
+  if (o == nullptr || x == nullptr || y == nullptr || w_text == nullptr || w_image == nullptr)
+    return MF_ERR_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(x) || !aligned16(y) || !aligned16(w_text) || !aligned16(w_image) ||
+      !aligned16_or_null(b_text) || !aligned16_or_null(b_image))
+    return MF_ERR_INVALID_ARG;
+  if (n_samples > 0 && (gate == nullptr || !aligned16(gate))) return MF_ERR_INVALID_ARG;
+  const size_t need = mf_block_workspace_size(n_samples, frames, 64, 0);
+  if (workspace_bytes < need) return MF_ERR_WORKSPACE;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* tstart = static_cast<int*>(workspace);
+  const int n_pieces = (frames + 1) * n_samples;
+  Tracer tr(trace, s);
+  hipError_t e = tr.run("piece_tiles", [&] { return mf::launch_piece_tiles(cu_pieces, n_pieces, n_tokens, tstart, s); });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  return from_hip(tr.run("out_gated", [&] {
+    return mf::launch_out_gated(o, x, w_text, w_image, b_text, b_image, gate, cu_pieces, tstart, n_samples, frames,
+                                n_tokens, channels, y, s);
+  }));
+}
+
+}  // extern "C"

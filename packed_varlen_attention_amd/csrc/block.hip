@@ -1,0 +1,414 @@
+// The attention sub-block's fused chains around the packed joint attention:
+// adaptive normalisation, the modality-specific QKV projection with the
+// rotary embedding in its epilogue, and the output projection with the gated
+// residual update in its epilogue.
+//
+// The backbone follows MMDiT -- joint self-attention over the concatenated
+// text and image tokens with normalisation and projection layers specific to
+// each modality (Mage-Flow paper section 3.2.1 "Model Architecture and Native
+// Packing", paperlayer.ai summary; ai.thesatyajit.com explainer, Figure 5
+// caption) -- and its training system fuses the transformer blocks' memory-
+// bound chains of adaptive normalisation, rotary embeddings and gated
+// residual updates (paper section 3.3 "Training Infrastructure").
+//
+// Rows are tokens in packed order, [N][C] with C = H D.  A token's sample and
+// modality come from cu_pieces (frames + 1 pieces per sample; the first piece
+// of a sample is its text, the others image grids).
+//   adaln:  h = LN(x) (1 + scale[s][m]) + shift[s][m], LayerNorm without
+//           affine, population variance, fp32 statistics.
+//   qkv:    [q | k | v] = h W_m^T + b_m; q and k rotated by the token's
+//           position, written [N][H][D] (the attention then needs no rotation).
+//   out:    y = x + gate[s][m] (o W_o,m^T + b_o,m).
+// The projections tile the token rows per piece, so a tile never mixes
+// modalities and takes one weight matrix.
+#include "mf_device.h"
+#include "mf_kernels.h"
+
+namespace mf {
+
+namespace {
+
+constexpr int kPT = 256;     // token rows per projection tile
+constexpr int kFT = 256;     // output features per projection tile
+constexpr int kKS = 64;      // reduction slice per pipeline step (one 128-byte LDS row)
+constexpr int kPWaves = 8;   // 4 x 2 waves, each 64 tokens x 128 features
+constexpr int kXcds = 8;     // workgroups are dealt round-robin to the XCDs
+
+// Rows of piece i, clamped to [0, n_tokens] (cu_pieces is device data the
+// host cannot check; a malformed one yields empty pieces, never a read past
+// the tensors).
+__device__ __forceinline__ void piece_rows(const int* __restrict__ cp, int i, int n_tokens, int& a, int& e) {
+  a = min(max(cp[i], 0), n_tokens);
+  e = min(max(cp[i + 1], a), n_tokens);
+}
+
+// tstart[p] = sum over pieces q < p of ceil(len_q / kPT); tstart[m] = total.
+__global__ __launch_bounds__(1024) void piece_tiles_kernel(const int* __restrict__ cp, int m, int n_tokens,
+                                                           int* __restrict__ tstart) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (m + 1023) / 1024;
+  const int a = min(t * per, m), b = min(a + per, m);
+  int sum = 0;
+  for (int i = a; i < b; ++i) {
+    int r0, r1;
+    piece_rows(cp, i, n_tokens, r0, r1);
+    sum += (r1 - r0 + kPT - 1) / kPT;
+  }
+  part[t] = sum;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    tstart[m] = run;
+  }
+  __syncthreads();
+  int run = part[t];
+  for (int i = a; i < b; ++i) {
+    int r0, r1;
+    piece_rows(cp, i, n_tokens, r0, r1);
+    tstart[i] = run;
+    run += (r1 - r0 + kPT - 1) / kPT;
+  }
+}
+
+// Index i with cp[i] <= row < cp[i + 1] among cp[0..m], or -1.
+__device__ __forceinline__ int piece_of_row(const int* __restrict__ cp, int m, int row) {
+  if (m <= 0 || row < cp[0] || row >= cp[m]) return -1;
+  int lo = 0, hi = m;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cp[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One wave per token row; lane l holds the 8-element chunks l, l + 64, ...
+// (coalesced 1 KB per load across the wave).  C = 512 cpl, cpl <= kMaxCpl.
+constexpr int kMaxCpl = 16;
+__global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__ x, const float* __restrict__ shift,
+                                                    const float* __restrict__ scale, const int* __restrict__ cp,
+                                                    int m, int per, int n_tokens, int channels, float eps,
+                                                    uint16_t* __restrict__ h) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_tokens) return;
+  const int lane = threadIdx.x & 63;
+  const int cpl = channels / 512;
+  const uint16_t* xr = x + static_cast<size_t>(row) * channels;
+  float v[kMaxCpl][8];
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxCpl; ++c)
+    if (c < cpl) {
+      load8<uint16_t>(xr + (c * 64 + lane) * 8, v[c]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += v[c][j];
+    }
+  const float mean = wave_sum(sum) / static_cast<float>(channels);
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxCpl; ++c)
+    if (c < cpl) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[c][j] -= mean;
+        ss += v[c][j] * v[c][j];
+      }
+    }
+  const float rstd = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(channels) + eps);
+  const int i = piece_of_row(cp, m, row);
+  const float* sh = nullptr;
+  const float* sc = nullptr;
+  if (i >= 0) {
+    const size_t off = (static_cast<size_t>(i / per) * 2 + (i % per == 0 ? 0 : 1)) * channels;
+    sh = shift + off;
+    sc = scale + off;
+  }
+  uint16_t* hr = h + static_cast<size_t>(row) * channels;
+#pragma unroll
+  for (int c = 0; c < kMaxCpl; ++c)
+    if (c < cpl) {
+      const int e = (c * 64 + lane) * 8;
+      float o[8];
+      if (sh != nullptr) {
+        const float4 s0 = *reinterpret_cast<const float4*>(sc + e), s1 = *reinterpret_cast<const float4*>(sc + e + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(sh + e), b1 = *reinterpret_cast<const float4*>(sh + e + 4);
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = v[c][j] * rstd * (1.0f + sv[j]) + bv[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = v[c][j] * rstd;
+      }
+      store8<uint16_t>(hr + e, o);
+    }
+}
+
+struct ProjArgs {
+  const uint16_t* act;  // [n_tokens][k]
+  const uint16_t* w0;   // text weights [n_out][k]
+  const uint16_t* w1;   // image weights
+  const float* b0;      // text bias [n_out] or nullptr
+  const float* b1;      // image bias
+  const int* cp;        // cu_pieces
+  const int* tstart;    // first tile of each piece; tstart[n_pieces] = tiles
+  int n_pieces, per, n_tokens, k, n_out, n_ntiles;
+  // qkv epilogue
+  uint16_t* q;
+  uint16_t* kk;
+  uint16_t* v;
+  const int* pos;  // [n_tokens][nax] or nullptr
+  int nax;
+  const float2* tab;
+  int max_pos;
+  // gated-residual epilogue
+  const uint16_t* x;
+  const float* gate;  // [S][2][n_out]
+  uint16_t* y;
+};
+
+enum { kEpiQkvRope = 0, kEpiGatedResidual = 1 };
+
+// out = act W^T (+ b) over one 256-token x 256-feature tile.  MFMA A operand
+// = weight rows (features), B operand = token rows, so the accumulator holds
+// the transposed tile: lane element e of block (mb, nb) is feature
+// 32 nb + 8 (e/4) + 4 (lane/32) + e%4 of token 32 mb + lane%32 -- four
+// consecutive features per lane group, the rotary pairs inside one lane.
+template <int D, int kEpi>
+__global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
+  constexpr int kTileBytes = 256 * kKS * 2;  // 256 rows of 128 bytes
+  __shared__ __attribute__((aligned(16))) char smemA0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemA1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemB0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemB1[kTileBytes];
+
+  // Workgroups are dealt to the XCDs round-robin.  Blocks b, b + 8, b + 16,
+  // ... (one XCD) share a token tile and sweep the feature tiles, so the
+  // token rows are fetched into that XCD's L2 once per slice.
+  const int b = blockIdx.x;
+  const int grp = b / (kXcds * a.n_ntiles), within = b % (kXcds * a.n_ntiles);
+  const int nt = within / kXcds;
+  const int mt = grp * kXcds + within % kXcds;
+  const int total = a.tstart[a.n_pieces];
+  if (mt >= total) return;
+  int lo = 0, hi = a.n_pieces;  // piece p: tstart[p] <= mt < tstart[p + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tstart[mid] <= mt) lo = mid; else hi = mid;
+  }
+  const int piece = lo;
+  int pa, mend;
+  piece_rows(a.cp, piece, a.n_tokens, pa, mend);
+  const int m0 = pa + (mt - a.tstart[piece]) * kPT;
+  if (m0 >= mend) return;
+  const int modality = piece % a.per == 0 ? 0 : 1;
+  const int sample = piece / a.per;
+  const uint16_t* w = modality ? a.w1 : a.w0;
+  const float* bias = modality ? a.b1 : a.b0;
+  const int n0 = nt * kFT;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5;
+  const int wm = wave >> 1;  // token rows 64 wm .. + 64
+  const int wn = wave & 1;   // features 128 wn .. + 128
+
+  const TileCopy<kKS, 256, kPWaves> copy(wave, lane, static_cast<unsigned>(a.k) * 2u);
+  lds_char* const sA[2] = {(lds_char*)smemA0, (lds_char*)smemA1};
+  lds_char* const sB[2] = {(lds_char*)smemB0, (lds_char*)smemB1};
+  auto load_stage = [&](int ks, int buf) {
+    copy(a.act + ks * kKS, m0, mend, sA[buf]);
+    copy(w + ks * kKS, n0, a.n_out, sB[buf]);
+  };
+
+  // Row fragments: the chunk swizzle of Tile<64> depends on (row / 2) % 8,
+  // the same for every 32-row block, so one offset per reduction step kk.
+  const int r32 = lane & 31;
+  int off[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) off[kk] = Tile<kKS>::off(r32, 2 * kk + hh);
+  auto frag = [&](const lds_char* t, int row0, int kk) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(t + off[kk] + row0 * (kKS * 2));
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+  const int nsteps = a.k / kKS;
+  auto step = [&](int ks, auto buf_tag) {
+    constexpr int bf = decltype(buf_tag)::value;
+    if (ks + 1 < nsteps) load_stage(ks + 1, 1 - bf);
+    const lds_char* A = sA[bf];
+    const lds_char* B = sB[bf];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 tf[2], wf[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) tf[mb] = frag(A, 64 * wm + 32 * mb, kk);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) wf[nb] = frag(B, 128 * wn + 32 * nb, kk);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma32(wf[nb], tf[mb], acc[mb][nb]);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+  load_stage(0, 0);
+  wait_vmem();
+  __syncthreads();
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int ks = 0;
+  for (; ks + 2 <= nsteps; ks += 2) {
+    step(ks, B0{});
+    step(ks + 1, B1{});
+  }
+  if (ks < nsteps) step(ks, B0{});
+
+  // ---- epilogue
+  const int C = a.n_out / (kEpi == kEpiQkvRope ? 3 : 1);
+  const int part = kEpi == kEpiQkvRope ? n0 / C : 0;  // q, k or v (a tile never straddles two)
+  uint16_t* out = kEpi == kEpiQkvRope ? (part == 0 ? a.q : part == 1 ? a.kk : a.v) : a.y;
+  const bool rotate = kEpi == kEpiQkvRope && part < 2 && a.pos != nullptr;
+  const float* gate = nullptr;
+  if constexpr (kEpi == kEpiGatedResidual) gate = a.gate + (static_cast<size_t>(sample) * 2 + modality) * C;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int tok = m0 + 64 * wm + 32 * mb + r32;
+    if (tok >= mend) continue;
+    Pos3 p = {0, 0, 0};
+    if (rotate) p = load_pos(a.pos, tok, a.nax);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;  // 4 consecutive features
+        float xv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[j] = acc[mb][nb][4 * g + j] + (bias != nullptr ? bias[n + j] : 0.f);
+        const int c = n - part * C;
+        if constexpr (kEpi == kEpiQkvRope) {
+          if (rotate) rotate_n<D, 4>(xv, c % D, p, a.tab, a.max_pos, 1.0f, a.nax);
+        } else {
+          float r[4];
+          const u32x2 raw = *reinterpret_cast<const u32x2*>(a.x + static_cast<size_t>(tok) * C + c);
+          r[0] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] & 0xffffu));
+          r[1] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] >> 16));
+          r[2] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] & 0xffffu));
+          r[3] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] >> 16));
+          const float4 gv = *reinterpret_cast<const float4*>(gate + c);
+          xv[0] = r[0] + gv.x * xv[0];
+          xv[1] = r[1] + gv.y * xv[1];
+          xv[2] = r[2] + gv.z * xv[2];
+          xv[3] = r[3] + gv.w * xv[3];
+        }
+        store4<uint16_t>(out + static_cast<size_t>(tok) * C + c, xv[0], xv[1], xv[2], xv[3]);
+      }
+  }
+}
+
+template <int D, int kEpi>
+hipError_t launch_proj_t(const ProjArgs& a, int mtiles_max, hipStream_t stream) {
+  const long long groups = (mtiles_max + kXcds - 1) / kXcds;
+  const long long blocks = groups * kXcds * a.n_ntiles;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((proj_kernel<D, kEpi>), dim3(static_cast<unsigned>(blocks)), dim3(kPWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+int mtiles_bound(int n_tokens, int n_pieces) { return (n_tokens + kPT - 1) / kPT + n_pieces; }
+
+}  // namespace
+
+int block_tile_rows() { return kPT; }
+
+hipError_t launch_piece_tiles(const int* cu_pieces, int n_pieces, int n_tokens, int* tstart, hipStream_t stream) {
+  hipLaunchKernelGGL(piece_tiles_kernel, dim3(1), dim3(1024), 0, stream, cu_pieces, n_pieces, n_tokens, tstart);
+  return hipGetLastError();
+}
+
+hipError_t launch_adaln(const void* x, const float* shift, const float* scale, const int* cu_pieces, int n_samples,
+                        int frames, int n_tokens, int channels, float eps, void* h, hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  const int per = frames + 1;
+  hipLaunchKernelGGL(adaln_kernel, dim3(static_cast<unsigned>((n_tokens + 3) / 4)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), shift, scale, cu_pieces, per * n_samples, per, n_tokens,
+                     channels, eps, static_cast<uint16_t*>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_rope(const void* h, const void* w_text, const void* w_image, const float* b_text,
+                           const float* b_image, const int* cu_pieces, const int* tstart, int n_samples, int frames,
+                           int n_tokens, int n_heads, int head_dim, const int* pos, int nax, const float2* tab,
+                           int max_pos, void* q, void* k, void* v, hipStream_t stream) {
+  ProjArgs a = {};
+  const int c = n_heads * head_dim;
+  a.act = static_cast<const uint16_t*>(h);
+  a.w0 = static_cast<const uint16_t*>(w_text);
+  a.w1 = static_cast<const uint16_t*>(w_image);
+  a.b0 = b_text;
+  a.b1 = b_image;
+  a.cp = cu_pieces;
+  a.tstart = tstart;
+  a.per = frames + 1;
+  a.n_pieces = a.per * n_samples;
+  a.n_tokens = n_tokens;
+  a.k = c;
+  a.n_out = 3 * c;
+  a.n_ntiles = 3 * c / kFT;
+  a.q = static_cast<uint16_t*>(q);
+  a.kk = static_cast<uint16_t*>(k);
+  a.v = static_cast<uint16_t*>(v);
+  a.pos = pos;
+  a.nax = nax;
+  a.tab = tab;
+  a.max_pos = max_pos;
+  const int mt = mtiles_bound(n_tokens, a.n_pieces);
+  return head_dim == 128 ? launch_proj_t<128, kEpiQkvRope>(a, mt, stream)
+                         : launch_proj_t<64, kEpiQkvRope>(a, mt, stream);
+}
+
+hipError_t launch_out_gated(const void* o, const void* x, const void* w_text, const void* w_image,
+                            const float* b_text, const float* b_image, const float* gate, const int* cu_pieces,
+                            const int* tstart, int n_samples, int frames, int n_tokens, int channels, void* y,
+                            hipStream_t stream) {
+  ProjArgs a = {};
+  a.act = static_cast<const uint16_t*>(o);
+  a.w0 = static_cast<const uint16_t*>(w_text);
+  a.w1 = static_cast<const uint16_t*>(w_image);
+  a.b0 = b_text;
+  a.b1 = b_image;
+  a.cp = cu_pieces;
+  a.tstart = tstart;
+  a.per = frames + 1;
+  a.n_pieces = a.per * n_samples;
+  a.n_tokens = n_tokens;
+  a.k = channels;
+  a.n_out = channels;
+  a.n_ntiles = channels / kFT;
+  a.x = static_cast<const uint16_t*>(x);
+  a.gate = gate;
+  a.y = static_cast<uint16_t*>(y);
+  return launch_proj_t<128, kEpiGatedResidual>(a, mtiles_bound(n_tokens, a.n_pieces), stream);
+}
+
+}  // namespace mf

@@ -83,4 +83,21 @@ hipError_t launch_rf_loss(const void* v, const void* z, const void* eps, void* g
 hipError_t launch_cfg_combine(const void* v, void* out, int* mismatched, int dtype, const int* cu_pieces,
                               int n_pairs, int n_tokens, int channels, float scale, hipStream_t stream);
 
+// The attention sub-block's fused chains (see block.hip).  Projections tile
+// the token rows per piece: tstart (n_pieces + 1 ints) holds each piece's
+// first tile, written by launch_piece_tiles.  bf16 [N][C] rows, C = H D, a
+// multiple of 256 (512 for adaln); weights bf16 [out][in], biases and the
+// modulation vectors ([S][2][C]) fp32.
+int block_tile_rows();
+hipError_t launch_piece_tiles(const int* cu_pieces, int n_pieces, int n_tokens, int* tstart, hipStream_t stream);
+hipError_t launch_adaln(const void* x, const float* shift, const float* scale, const int* cu_pieces, int n_samples,
+                        int frames, int n_tokens, int channels, float eps, void* h, hipStream_t stream);
+hipError_t launch_qkv_rope(const void* h, const void* w_text, const void* w_image, const float* b_text,
+                           const float* b_image, const int* cu_pieces, const int* tstart, int n_samples, int frames,
+                           int n_tokens, int n_heads, int head_dim, const int* pos, int nax, const float2* tab,
+                           int max_pos, void* q, void* k, void* v, hipStream_t stream);
+hipError_t launch_out_gated(const void* o, const void* x, const void* w_text, const void* w_image,
+                            const float* b_text, const float* b_image, const float* gate, const int* cu_pieces,
+                            const int* tstart, int n_samples, int frames, int n_tokens, int channels, void* y,
+                            hipStream_t stream);
 }  // namespace mf

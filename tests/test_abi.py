@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     import packed_varlen_attention_amd as m
-    assert m.abi_version() == 2
+    assert m.abi_version() == 3
     for code in (0, -1, -2, -3, -4):
         assert len(m.status_string(code)) > 0
     assert m.status_string(7) == "unknown status"
@@ -195,3 +195,56 @@ def test_flow_argument_errors(lib):
     assert lib.mf_cfg_combine(FAKE, FAKE, None, 0, FAKE, 3, 2, 8, 128, 3.0, None, None) == -1   # 2 pairs > 3 samples
     assert lib.mf_cfg_combine(FAKE, FAKE, FAKE + 2, 0, FAKE, 4, 2, 8, 128, 3.0, None, None) == -1
     assert lib.mf_cfg_combine(FAKE, FAKE, None, 0, FAKE, 4, 2, 8, 1000, 3.0, None, None) == -2
+
+
+def test_block_workspace_sizes(lib):
+    # tile table of (frames + 1) n_samples + 1 ints, then the 3-axis rotary table (5D/16 pairs per position)
+    assert lib.mf_block_workspace_size(9, 1, 128, 0) == 256
+    assert lib.mf_block_workspace_size(100, 2, 128, 0) == 1280               # 301 ints -> 1204 -> 1280
+    assert lib.mf_block_workspace_size(9, 1, 128, 640) == 256 + 640 * 40 * 8  # 204 800, already aligned
+    assert lib.mf_block_workspace_size(9, 3, 128, 0) == 0                    # bad frames
+    assert lib.mf_block_workspace_size(-1, 1, 128, 0) == 0
+
+
+def test_block_argument_errors(lib):
+    ws = lib.mf_block_workspace_size(2, 1, 128, 64)
+    # mf_adaln_modulate(x, shift, scale, h, cu, n_samples, frames, n, C, eps, stream, trace)
+    assert lib.mf_adaln_modulate(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 8, 768, 1e-6, None, None) == -2   # C % 512
+    assert lib.mf_adaln_modulate(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 8, 16384, 1e-6, None, None) == -2  # C > 8192
+    assert lib.mf_adaln_modulate(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 8, 3072, 0.0, None, None) == -1   # eps
+    assert lib.mf_adaln_modulate(FAKE, None, FAKE, FAKE, FAKE, 2, 1, 8, 3072, 1e-6, None, None) == -1  # shift
+    assert lib.mf_adaln_modulate(FAKE + 8, FAKE, FAKE, FAKE, FAKE, 2, 1, 8, 3072, 1e-6, None, None) == -1
+    assert lib.mf_adaln_modulate(FAKE, FAKE, FAKE, FAKE, None, 2, 1, 8, 3072, 1e-6, None, None) == -1  # cu
+    assert lib.mf_adaln_modulate(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 8, 3072, 1e-6, None, None) == -1  # frames
+    assert lib.mf_adaln_modulate(None, None, None, None, FAKE, 2, 1, 0, 3072, 1e-6, None, None) == 0  # empty
+    # mf_qkv_rope(h, wt, wi, bt, bi, q, k, v, cu, n_samples, frames, pos, nax, theta, max_pos, n, H, D, ws, wsb, ...)
+    def qkv(**kw):
+        a = dict(h=FAKE, wt=FAKE, wi=FAKE, bt=None, bi=None, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, ns=2, fr=1, pos=FAKE,
+                 nax=2, theta=10000.0, max_pos=64, n=8, H=24, D=128, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return lib.mf_qkv_rope(a["h"], a["wt"], a["wi"], a["bt"], a["bi"], a["q"], a["k"], a["v"], a["cu"], a["ns"],
+                               a["fr"], a["pos"], a["nax"], a["theta"], a["max_pos"], a["n"], a["H"], a["D"], a["ws"],
+                               a["wsb"], None, None)
+    assert qkv(D=96) == -2
+    assert qkv(H=3, D=64) == -2                 # channels 192 not a multiple of 256
+    assert qkv(H=0) == -1
+    assert qkv(nax=4) == -1
+    assert qkv(theta=0.0) == -1
+    assert qkv(max_pos=0) == -1
+    assert qkv(pos=FAKE + 4) == -1              # 2D positions are 8-byte aligned
+    assert qkv(wi=None) == -1
+    assert qkv(bt=FAKE + 4) == -1
+    assert qkv(q=FAKE + 8) == -1
+    assert qkv(wsb=ws - 1) == -3
+    assert qkv(ws=FAKE + 16) == -1
+    assert qkv(n=0, h=None, q=None) == 0        # empty: nothing to launch
+    # mf_out_gated_residual(o, x, wt, wi, bt, bi, gate, y, cu, n_samples, frames, n, C, ws, wsb, stream, trace)
+    wso = lib.mf_block_workspace_size(2, 1, 64, 0)
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 2, 1, 8, 3000, FAKE, wso,
+                                     None, None) == -2
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, 2, 1, 8, 3072, FAKE, wso,
+                                     None, None) == -1  # gate
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 2, 1, 8, 3072, FAKE, 4,
+                                     None, None) == -3
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE + 2, FAKE, 2, 1, 8, 3072, FAKE,
+                                     wso, None, None) == -1
