@@ -53,6 +53,10 @@ def parse_args():
                     help="after timing, also time the rectified-flow noising / loss passes on the pack's latents "
                          "(128 channels, bf16) and the CFG combine on the 1024^2 packed-CFG pack; reported under "
                          "'flow', not part of the step")
+    ap.add_argument("--block", action="store_true",
+                    help="after timing, also time the attention sub-block chains (adaLN, QKV projection with the "
+                         "RoPE epilogue, output projection with the gated residual) on the pack at the model width "
+                         "(24 heads x 128 = 3072 channels); reported under 'block', not part of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -188,6 +192,87 @@ def flow_timing(mf, workloads, w, samples, packres, n_tokens: int, dev, reps: in
                                                    out=gv, trace=tr), 3 * cond_img * row)
     out["note"] = (f"latents [N][{c}] bf16 on the bench pack (N={n_tokens}, {noised} noised rows); CFG on the "
                    f"1024^2 packed-CFG pack ({gn} tokens, {len(g.samples) // 2} pairs)")
+    return out
+
+
+def block_timing(mf, workloads, w, packres, n_tokens: int, max_pos: int, dev, reps: int = 10) -> dict:
+    """Per-launch time and rate of the sub-block chain kernels on the bench pack, plus (for context only) the
+    library GEMM of the same shapes without an epilogue."""
+    import numpy as np
+    import torch
+
+    heads, hd = w.n_heads, w.head_dim
+    c = heads * hd
+    frames = 2 if w.editing else 1
+    s = int(packres.counts[0].item())
+    d = workloads.block_inputs(w.seed + 100, n_tokens, s, c)
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def f32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    x, o = bf(d["x"]), bf(d["o"])
+    shift, scale, gate = f32(d["shift"]), f32(d["scale"]), f32(d["gate"])
+    wq = (bf(d["w_qkv0"]), bf(d["w_qkv1"]))
+    bq = (f32(d["b_qkv0"]), f32(d["b_qkv1"]))
+    wo = (bf(d["w_o0"]), bf(d["w_o1"]))
+    bo = (f32(d["b_o0"]), f32(d["b_o1"]))
+    cp = packres.cu_pieces
+    pos = packres.pos[:n_tokens]
+    h = torch.empty_like(x)
+    qkv = tuple(torch.empty((n_tokens, heads, hd), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    y = torch.empty_like(x)
+    ws = mf.block_workspace(s, frames, hd, max_pos, dev)
+    out = {}
+
+    def timed(name, fn, kernel, flops, nbytes):
+        tr = mf.KernelTrace(4)
+        fn(None)
+        torch.cuda.synchronize()
+        total = 0.0
+        for _ in range(reps):
+            fn(tr)
+            torch.cuda.synchronize()
+            total += sum(ms for nm, ms in tr.results() if nm == kernel)
+        ms = total / reps
+        e = {"ms": round(ms, 4), "bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        if flops:
+            e["flops"] = flops
+            e["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        out[name] = e
+
+    row = 2 * c
+    timed("adaln", lambda tr: mf.adaln_modulate(x, shift, scale, cp, s, frames, out=h, trace=tr), "adaln", 0,
+          2 * n_tokens * row)
+    timed("qkv_rope", lambda tr: mf.qkv_rope(h, wq, bq, cp, s, frames, pos, heads, 10000.0, max_pos, out=qkv,
+                                             workspace=ws, trace=tr), "qkv_rope",
+          2 * n_tokens * c * 3 * c, n_tokens * row + 3 * n_tokens * row + 3 * c * row)
+    timed("out_gated", lambda tr: mf.out_gated_residual(o, x, wo, bo, gate, cp, s, frames, out=y, workspace=ws,
+                                                        trace=tr), "out_gated",
+          2 * n_tokens * c * c, 3 * n_tokens * row + c * row)
+
+    # context: the library GEMM (hipBLASLt through torch.mm) of the same shapes, no epilogue, one weight
+    def lib_ms(a, b_t):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.mm(a, b_t)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch.mm(a, b_t)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    wq_t = wq[1].t().contiguous()
+    wo_t = wo[1].t().contiguous()
+    mq, mo = lib_ms(h, wq_t), lib_ms(o, wo_t)
+    out["library_gemm_context"] = {
+        "qkv_ms": round(mq, 4), "qkv_tflops": round(2 * n_tokens * c * 3 * c / (mq * 1e-3) / 1e12, 1),
+        "out_ms": round(mo, 4), "out_tflops": round(2 * n_tokens * c * c / (mo * 1e-3) / 1e12, 1),
+        "note": "torch.mm (hipBLASLt) on the same shapes with one weight, no bias, rotation or residual"}
+    out["note"] = (f"bf16 [N][{c}] rows of the bench pack (N={n_tokens}, {s} samples), one weight matrix per "
+                   f"modality; bytes = activations read and written once plus the weights of one modality")
     return out
 
 
@@ -361,6 +446,8 @@ def main():
         roof["frac_measured"] = round(roof["achieved"] / probe["tflops"], 4)
     if args.flow:
         result["flow"] = flow_timing(mf, workloads, w, samples, packres, N, dev)
+    if args.block:
+        result["block"] = block_timing(mf, workloads, w, packres, N, max_pos, dev)
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

@@ -30,7 +30,8 @@ namespace {
 
 constexpr int kPT = 256;     // token rows per projection tile
 constexpr int kFT = 256;     // output features per projection tile
-constexpr int kKS = 64;      // reduction slice per pipeline step (one 128-byte LDS row)
+constexpr int kKS = 32;      // reduction slice per pipeline step (one 64-byte LDS row)
+constexpr int kStages = 4;   // LDS stages; copies run three steps ahead
 constexpr int kPWaves = 8;   // 4 x 2 waves, each 64 tokens x 128 features
 constexpr int kXcds = 8;     // workgroups are dealt round-robin to the XCDs
 
@@ -93,17 +94,40 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per token row; lane l holds the 8-element chunks l, l + 64, ...
-// (coalesced 1 KB per load across the wave).  C = 512 cpl, cpl <= kMaxCpl.
-constexpr int kMaxCpl = 16;
+// One wave per token row, four rows per workgroup; lane l holds the 8-element
+// chunks l, l + 64, ... of its row (coalesced 1 KB per load across the wave).
+// The (1 + scale, shift) vectors of the first row's (sample, modality) are
+// staged in LDS once per workgroup; a row of another piece (rows are in
+// packed order, so rarely) reads its own from global memory.  C = 512 cpl,
+// cpl <= kMaxCpl.
+constexpr int kAdaMaxC = 8192;
+template <int kMaxCpl>
 __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__ x, const float* __restrict__ shift,
                                                     const float* __restrict__ scale, const int* __restrict__ cp,
                                                     int m, int per, int n_tokens, int channels, float eps,
                                                     uint16_t* __restrict__ h) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n_tokens) return;
+  extern __shared__ float mod_lds[];  // [2][channels]: 1 + scale, shift
+  const int row0 = blockIdx.x * 4;
+  const int row = row0 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int cpl = channels / 512;
+  auto group_of = [&](int r) {
+    const int i = piece_of_row(cp, m, r);
+    return i < 0 ? -1 : (i / per) * 2 + (i % per == 0 ? 0 : 1);
+  };
+  const int g0 = group_of(row0);
+  if (g0 >= 0) {
+    const float* sc = scale + static_cast<size_t>(g0) * channels;
+    const float* sh = shift + static_cast<size_t>(g0) * channels;
+    for (int e = threadIdx.x * 4; e < channels; e += 256 * 4) {
+      const float4 s4 = *reinterpret_cast<const float4*>(sc + e);
+      const float4 b4 = *reinterpret_cast<const float4*>(sh + e);
+      *reinterpret_cast<float4*>(mod_lds + e) = make_float4(1.0f + s4.x, 1.0f + s4.y, 1.0f + s4.z, 1.0f + s4.w);
+      *reinterpret_cast<float4*>(mod_lds + channels + e) = b4;
+    }
+  }
+  __syncthreads();
+  if (row >= n_tokens) return;
   const uint16_t* xr = x + static_cast<size_t>(row) * channels;
   float v[kMaxCpl][8];
   float sum = 0.f;
@@ -126,31 +150,46 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__
       }
     }
   const float rstd = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(channels) + eps);
-  const int i = piece_of_row(cp, m, row);
-  const float* sh = nullptr;
-  const float* sc = nullptr;
-  if (i >= 0) {
-    const size_t off = (static_cast<size_t>(i / per) * 2 + (i % per == 0 ? 0 : 1)) * channels;
-    sh = shift + off;
-    sc = scale + off;
-  }
+  const int g = group_of(row);  // wave-uniform
   uint16_t* hr = h + static_cast<size_t>(row) * channels;
 #pragma unroll
   for (int c = 0; c < kMaxCpl; ++c)
     if (c < cpl) {
       const int e = (c * 64 + lane) * 8;
-      float o[8];
-      if (sh != nullptr) {
-        const float4 s0 = *reinterpret_cast<const float4*>(sc + e), s1 = *reinterpret_cast<const float4*>(sc + e + 4);
-        const float4 b0 = *reinterpret_cast<const float4*>(sh + e), b1 = *reinterpret_cast<const float4*>(sh + e + 4);
-        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float s1[8], b[8];
+      if (g == g0 && g >= 0) {
+        const float4* ls = reinterpret_cast<const float4*>(mod_lds + e);
+        const float4* lb = reinterpret_cast<const float4*>(mod_lds + channels + e);
+        const float4 s0 = ls[0], s4 = ls[1], b0 = lb[0], b4 = lb[1];
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s4.x, s4.y, s4.z, s4.w};
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = v[c][j] * rstd * (1.0f + sv[j]) + bv[j];
+        for (int j = 0; j < 8; ++j) {
+          s1[j] = sv[j];
+          b[j] = bv[j];
+        }
+      } else if (g >= 0) {
+        const float* sc = scale + static_cast<size_t>(g) * channels + e;
+        const float* sh = shift + static_cast<size_t>(g) * channels + e;
+        const float4 s0 = *reinterpret_cast<const float4*>(sc), s4 = *reinterpret_cast<const float4*>(sc + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(sh), b4 = *reinterpret_cast<const float4*>(sh + 4);
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s4.x, s4.y, s4.z, s4.w};
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          s1[j] = 1.0f + sv[j];
+          b[j] = bv[j];
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = v[c][j] * rstd;
+        for (int j = 0; j < 8; ++j) {
+          s1[j] = 1.0f;
+          b[j] = 0.0f;
+        }
       }
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = v[c][j] * rstd * s1[j] + b[j];
       store8<uint16_t>(hr + e, o);
     }
 }
@@ -180,6 +219,11 @@ struct ProjArgs {
 
 enum { kEpiQkvRope = 0, kEpiGatedResidual = 1 };
 
+// Feature tiles per scheduling window: 4 when they divide the tile count.
+__host__ __device__ __forceinline__ int window_cols(int n_ntiles) {
+  return n_ntiles % 4 == 0 ? 4 : n_ntiles % 2 == 0 ? 2 : 1;
+}
+
 // out = act W^T (+ b) over one 256-token x 256-feature tile.  MFMA A operand
 // = weight rows (features), B operand = token rows, so the accumulator holds
 // the transposed tile: lane element e of block (mb, nb) is feature
@@ -187,19 +231,30 @@ enum { kEpiQkvRope = 0, kEpiGatedResidual = 1 };
 // consecutive features per lane group, the rotary pairs inside one lane.
 template <int D, int kEpi>
 __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
-  constexpr int kTileBytes = 256 * kKS * 2;  // 256 rows of 128 bytes
+  constexpr int kTileBytes = 256 * kKS * 2;  // 256 rows of 64 bytes
+  // Four stages of a token tile and a weight tile, as separate objects so
+  // the compiler can tell the stage being read from stages being filled.
   __shared__ __attribute__((aligned(16))) char smemA0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char smemA1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemA2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemA3[kTileBytes];
   __shared__ __attribute__((aligned(16))) char smemB0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char smemB1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemB2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemB3[kTileBytes];
 
-  // Workgroups are dealt to the XCDs round-robin.  Blocks b, b + 8, b + 16,
-  // ... (one XCD) share a token tile and sweep the feature tiles, so the
-  // token rows are fetched into that XCD's L2 once per slice.
+  // Workgroups are dealt to the XCDs round-robin, so blocks b, b + 8, b + 16,
+  // ... run together on one XCD.  Each run of 32 such blocks is a window of
+  // (32 / nw) token tiles x nw feature tiles: the XCD's L2 then serves 12
+  // distinct tiles (8 + 4 with nw = 4) to 32 workgroups, not 33 with one
+  // token tile and 32 feature tiles.
   const int b = blockIdx.x;
-  const int grp = b / (kXcds * a.n_ntiles), within = b % (kXcds * a.n_ntiles);
-  const int nt = within / kXcds;
-  const int mt = grp * kXcds + within % kXcds;
+  const int nw = window_cols(a.n_ntiles), mw = 32 / nw;
+  const int x = b % kXcds, r = b / kXcds;
+  const int win = (r / 32) * kXcds + x, p = r % 32;
+  const int n_ntg = a.n_ntiles / nw;
+  const int nt = (win % n_ntg) * nw + p / mw;
+  const int mt = (win / n_ntg) * mw + p % mw;
   const int total = a.tstart[a.n_pieces];
   if (mt >= total) return;
   int lo = 0, hi = a.n_pieces;  // piece p: tstart[p] <= mt < tstart[p + 1]
@@ -224,20 +279,27 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
   const int wm = wave >> 1;  // token rows 64 wm .. + 64
   const int wn = wave & 1;   // features 128 wn .. + 128
 
-  const TileCopy<kKS, 256, kPWaves> copy(wave, lane, static_cast<unsigned>(a.k) * 2u);
-  lds_char* const sA[2] = {(lds_char*)smemA0, (lds_char*)smemA1};
-  lds_char* const sB[2] = {(lds_char*)smemB0, (lds_char*)smemB1};
+  using Copy = TileCopy<kKS, 256, kPWaves>;
+  constexpr int kCopiesPerStage = 2 * Copy::kCopies;  // token and weight tile, per wave
+  const Copy copy(wave, lane, static_cast<unsigned>(a.k) * 2u);
+  lds_char* const sA[kStages] = {(lds_char*)smemA0, (lds_char*)smemA1, (lds_char*)smemA2, (lds_char*)smemA3};
+  lds_char* const sB[kStages] = {(lds_char*)smemB0, (lds_char*)smemB1, (lds_char*)smemB2, (lds_char*)smemB3};
+  const int nsteps = a.k / kKS;  // a multiple of 8 (k is a multiple of 256)
+  // Stage ks lives in buffer ks % 4.  Every step issues the copies of stage
+  // ks + 3 (past the end: the last slice again, into a buffer no later step
+  // reads), so the wait for stage ks + 1 keeps a fixed count in flight.
   auto load_stage = [&](int ks, int buf) {
+    ks = min(ks, nsteps - 1);
     copy(a.act + ks * kKS, m0, mend, sA[buf]);
     copy(w + ks * kKS, n0, a.n_out, sB[buf]);
   };
 
-  // Row fragments: the chunk swizzle of Tile<64> depends on (row / 2) % 8,
+  // Row fragments: the chunk swizzle of Tile<32> depends on (row / 2) % 4,
   // the same for every 32-row block, so one offset per reduction step kk.
   const int r32 = lane & 31;
-  int off[4];
+  int off[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) off[kk] = Tile<kKS>::off(r32, 2 * kk + hh);
+  for (int kk = 0; kk < 2; ++kk) off[kk] = Tile<kKS>::off(r32, 2 * kk + hh);
   auto frag = [&](const lds_char* t, int row0, int kk) {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(t + off[kk] + row0 * (kKS * 2));
   };
@@ -250,14 +312,13 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 
-  const int nsteps = a.k / kKS;
   auto step = [&](int ks, auto buf_tag) {
     constexpr int bf = decltype(buf_tag)::value;
-    if (ks + 1 < nsteps) load_stage(ks + 1, 1 - bf);
+    load_stage(ks + 3, (bf + 3) % kStages);
     const lds_char* A = sA[bf];
     const lds_char* B = sB[bf];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2; ++kk) {
       bf16x8 tf[2], wf[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) tf[mb] = frag(A, 64 * wm + 32 * mb, kk);
@@ -268,20 +329,27 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma32(wf[nb], tf[mb], acc[mb][nb]);
     }
-    wait_vmem();
-    __syncthreads();
+    // Stage ks + 1 has landed once only the two newest stages' copies are
+    // outstanding (copies complete in issue order).
+    wait_vmem_keep<2 * kCopiesPerStage>();
+    barrier_keep_loads();
   };
   load_stage(0, 0);
-  wait_vmem();
-  __syncthreads();
+  load_stage(1, 1);
+  load_stage(2, 2);
+  wait_vmem_keep<2 * kCopiesPerStage>();
+  barrier_keep_loads();
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  int ks = 0;
-  for (; ks + 2 <= nsteps; ks += 2) {
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  for (int ks = 0; ks < nsteps; ks += 4) {
     step(ks, B0{});
     step(ks + 1, B1{});
+    step(ks + 2, B2{});
+    step(ks + 3, B3{});
   }
-  if (ks < nsteps) step(ks, B0{});
+  wait_vmem();  // the trailing copies land before the workgroup's LDS is released
 
   // ---- epilogue
   const int C = a.n_out / (kEpi == kEpiQkvRope ? 3 : 1);
@@ -327,8 +395,9 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
 
 template <int D, int kEpi>
 hipError_t launch_proj_t(const ProjArgs& a, int mtiles_max, hipStream_t stream) {
-  const long long groups = (mtiles_max + kXcds - 1) / kXcds;
-  const long long blocks = groups * kXcds * a.n_ntiles;
+  const int nw = window_cols(a.n_ntiles), mw = 32 / nw;
+  const long long wins = static_cast<long long>((mtiles_max + mw - 1) / mw) * (a.n_ntiles / nw);
+  const long long blocks = (wins + kXcds - 1) / kXcds * kXcds * 32;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((proj_kernel<D, kEpi>), dim3(static_cast<unsigned>(blocks)), dim3(kPWaves * 64), 0, stream, a);
@@ -349,10 +418,22 @@ hipError_t launch_piece_tiles(const int* cu_pieces, int n_pieces, int n_tokens, 
 hipError_t launch_adaln(const void* x, const float* shift, const float* scale, const int* cu_pieces, int n_samples,
                         int frames, int n_tokens, int channels, float eps, void* h, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
+  if (channels > kAdaMaxC) return hipErrorInvalidValue;
   const int per = frames + 1;
-  hipLaunchKernelGGL(adaln_kernel, dim3(static_cast<unsigned>((n_tokens + 3) / 4)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(x), shift, scale, cu_pieces, per * n_samples, per, n_tokens,
-                     channels, eps, static_cast<uint16_t*>(h));
+  const dim3 grid(static_cast<unsigned>((n_tokens + 3) / 4));
+  const size_t lds = 2 * static_cast<size_t>(channels) * sizeof(float);
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  uint16_t* hs = static_cast<uint16_t*>(h);
+  const int cpl = channels / 512;
+  if (cpl <= 4)
+    hipLaunchKernelGGL((adaln_kernel<4>), grid, dim3(256), lds, stream, xs, shift, scale, cu_pieces,
+                       per * n_samples, per, n_tokens, channels, eps, hs);
+  else if (cpl <= 6)
+    hipLaunchKernelGGL((adaln_kernel<6>), grid, dim3(256), lds, stream, xs, shift, scale, cu_pieces,
+                       per * n_samples, per, n_tokens, channels, eps, hs);
+  else
+    hipLaunchKernelGGL((adaln_kernel<16>), grid, dim3(256), lds, stream, xs, shift, scale, cu_pieces,
+                       per * n_samples, per, n_tokens, channels, eps, hs);
   return hipGetLastError();
 }
 

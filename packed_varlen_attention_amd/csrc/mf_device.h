@@ -85,8 +85,11 @@ struct Tile {
   __device__ static __forceinline__ int swz(int row) {
     if constexpr (D == 128) {
       return ((row & 3) << 2) | ((row >> 2) & 3);
-    } else {
+    } else if constexpr (D == 64) {
       return (row >> 1) & 7;
+    } else {
+      static_assert(D == 32, "tiles of 32, 64 or 128 bf16 per row");
+      return (row >> 1) & 3;  // 64-byte rows: 8 consecutive rows cover all banks
     }
   }
   __device__ static __forceinline__ int off(int row, int chunk) {
