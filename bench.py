@@ -44,7 +44,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mixed50k", choices=["mixed50k", "cfg1024", "stress", "edit50k"],
+    ap.add_argument("--workload", default="mixed50k", choices=["mixed50k", "cfg1024", "stress", "edit50k", "captions"],
                     help="bench line workload (mixed50k is the metric's; others for exploration; edit50k runs "
                          "the editing path with frame-aware 3D RoPE)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU timing")
@@ -291,7 +291,7 @@ def main():
 
     torch.cuda.set_device(0)
     w = {"mixed50k": lambda: workloads.mixed50k(backward=True), "cfg1024": workloads.cfg1024,
-         "stress": workloads.stress, "edit50k": workloads.edit50k}[args.workload]()
+         "stress": workloads.stress, "edit50k": workloads.edit50k, "captions": workloads.captions}[args.workload]()
     samples = list(w.samples)
     H, D = w.n_heads, w.head_dim
     dev = torch.device("cuda", 0)
@@ -418,7 +418,9 @@ def main():
                          "stress": "long/ragged stress pack (2048^2 + two 4:1 panoramas + 64 thumbnails): "
                                    "pack + fwd + bwd",
                          "edit50k": "editing training pack [text | source | target], frame-aware 3D RoPE, "
-                                    "50,000-token budget, seed 6: pack + fwd(LSE) + bwd"}[args.workload],
+                                    "50,000-token budget, seed 6: pack + fwd(LSE) + bwd",
+                         "captions": "1500 text-only segments of 16-120 tokens (multi-segment tiles), seed 8: "
+                                     "pack + fwd(LSE) + bwd"}[args.workload],
             "n_tokens": N, "segments": n_packed, "heads": H, "head_dim": D, "max_seqlen": max_seqlen,
             "sum_L2": sum_l2, "gather_row_bytes": ROW_BYTES,
         },

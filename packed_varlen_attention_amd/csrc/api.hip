@@ -63,8 +63,11 @@ struct AttnWorkspace {
 AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
                              int32_t max_pos, int32_t dtype, bool backward) {
   AttnWorkspace w;
-  // schedules (order, tile prefix): one for the forward; dkdv's and dq's for the backward
-  w.sched = (backward ? 2 : 1) * (2 * static_cast<size_t>(n_segments > 0 ? n_segments : 0) + 1) * sizeof(int32_t);
+  // schedules (order, tile prefix): one for the forward; dkdv's and dq's for
+  // the backward; then the virtual segments (offsets, first segment) that
+  // merge runs of tiny segments into multi-segment tiles
+  const size_t nseg = static_cast<size_t>(n_segments > 0 ? n_segments : 0);
+  w.sched = ((backward ? 2 : 1) * (2 * nseg + 1) + 2 * (nseg + 1)) * sizeof(int32_t);
   const size_t tensor_bf16 = static_cast<size_t>(n_tokens) * n_heads * head_dim * 2;
   // rotary table, sized for the wider (3-axis) layout so one size serves both
   w.tab = static_cast<size_t>(max_pos > 0 ? max_pos : 0) * mf::rope_table_width(head_dim, 3) * sizeof(float2);
@@ -305,7 +308,7 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
     });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
-  mf::AttnArgs a;
+  mf::AttnArgs a = {};
   a.cu_seqlens = cu_seqlens;
   a.n_segments = n_segments;
   a.max_seqlen = max_seqlen;
@@ -320,8 +323,22 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
   a.order = reinterpret_cast<int*>(ws + w.sched_off);
   a.pt = a.order + n_segments;
+  // Multi-segment tiles for runs of tiny segments, when they can hold half of
+  // the tokens at all (that needs a mean segment length of at most 256).
+  const bool merge = static_cast<long long>(n_tokens) <= 2LL * mf::kTinySegment * n_segments;
+  int* vcu = const_cast<int*>(a.pt) + n_segments + 1;
+  int* vfirst = vcu + n_segments + 1;
+  if (merge) {
+    a.cu_seqlens = vcu;
+    a.rcu = cu_seqlens;
+    a.vfirst = vfirst;
+  }
   e = tr.run("attn_sched", [&] {
-    return mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kFwdTile, const_cast<int*>(a.order),
+    if (merge) {
+      hipError_t r = mf::launch_merge_tiny(cu_seqlens, n_segments, n_tokens, vcu, vfirst, s);
+      if (r != hipSuccess) return r;
+    }
+    return mf::launch_sched(a.cu_seqlens, n_segments, n_tokens, mf::kFwdTile, const_cast<int*>(a.order),
                             const_cast<int*>(a.pt), s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
@@ -393,7 +410,7 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
     });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
-  mf::AttnArgs a;
+  mf::AttnArgs a = {};
   a.cu_seqlens = cu_seqlens;
   a.n_segments = n_segments;
   a.max_seqlen = max_seqlen;
@@ -412,11 +429,27 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
   mf::AttnArgs aq = a;
   aq.order = a.pt + n_segments + 1;
   aq.pt = aq.order + n_segments;
+  // dq takes multi-segment tiles like the forward; dkdv keeps one tile per
+  // segment (its 128-key x 32-query steps already fit tiny segments: a shared
+  // tile measured slower).
+  const bool merge = static_cast<long long>(n_tokens) <= 2LL * mf::kTinySegment * n_segments;
+  int* vcu = const_cast<int*>(aq.pt) + n_segments + 1;
+  int* vfirst = vcu + n_segments + 1;
+  if (merge) {
+    aq.cu_seqlens = vcu;
+    aq.rcu = cu_seqlens;
+    aq.vfirst = vfirst;
+  }
   e = tr.run("attn_sched", [&] {
-    hipError_t r = mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kDkdvTile, const_cast<int*>(a.order),
-                                    const_cast<int*>(a.pt), s);
+    hipError_t r = hipSuccess;
+    if (merge) {
+      r = mf::launch_merge_tiny(cu_seqlens, n_segments, n_tokens, vcu, vfirst, s);
+      if (r != hipSuccess) return r;
+    }
+    r = mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kDkdvTile, const_cast<int*>(a.order),
+                         const_cast<int*>(a.pt), s);
     if (r != hipSuccess) return r;
-    return mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kDqTile, const_cast<int*>(aq.order),
+    return mf::launch_sched(aq.cu_seqlens, n_segments, n_tokens, mf::kDqTile, const_cast<int*>(aq.order),
                             const_cast<int*>(aq.pt), s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;

@@ -200,14 +200,14 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   }
 }
 
-template <int D, typename TOut>
+template <int D, typename TOut, bool kMulti>
 __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     const uint16_t* __restrict__ dob, const TOut* __restrict__ o, const TOut* __restrict__ dout,
     const float* __restrict__ lse, float* __restrict__ lse2, float* __restrict__ delta,
     TOut* __restrict__ dq, const int* __restrict__ cu, const int* __restrict__ order, const int* __restrict__ pt,
     int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax, const float2* __restrict__ tab,
-    int max_pos, float scale, float scale_log2) {
+    int max_pos, float scale, float scale_log2, const int* __restrict__ rcu, const int* __restrict__ vfirst) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int kRowBytes = D * 2;
@@ -236,6 +236,13 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
   const int hh = lane >> 5;
   const int qi = qbase + wave * 32 + (lane & 31);
   const bool qok = qi < L;
+  // A multi-segment tile is left to the kMulti instance, where a query meets
+  // only the keys of its own segment, [qlo, qhi) in tile rows.
+  const int f0 = vfirst != nullptr ? vfirst[it.seg] : it.seg;
+  const int f1 = vfirst != nullptr ? vfirst[it.seg + 1] : it.seg + 1;
+  if ((f1 - f0 > 1) != kMulti) return;
+  int qlo = 0, qhi = L;
+  if constexpr (kMulti) member_bounds(rcu, f0, f1, s0, s1, min(qi, L - 1), qlo, qhi);
   const long long qrow = (static_cast<long long>(s0) + min(qi, L - 1)) * heads + head;
 
   bf16x8 qf[NKK], df[NKK];
@@ -342,9 +349,12 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
         sacc = mfma32(ka, qf[kk], sacc);
         dpacc = mfma32(va, df[kk], dpacc);
       }
-      if (k0 + kKT > L) {  // only the segment's last tile holds keys past its end: exp2(-inf) = 0
+      if (kMulti || k0 + kKT > L) {  // keys outside the query's segment (or past its end): exp2(-inf) = 0
 #pragma unroll
-        for (int g = 0; g < 2; ++g) mask_rows8(sacc, g, L - (k0 + 32 * kb + 16 * g + 8 * hh), -INFINITY);
+        for (int g = 0; g < 2; ++g) {
+          const int r0 = k0 + 32 * kb + 16 * g + 8 * hh;
+          mask_rows8_range(sacc, g, qlo - r0, qhi - r0, -INFINITY);
+        }
       }
       float p[16];
 #pragma unroll
@@ -414,12 +424,20 @@ hipError_t launch_dq_t(const AttnArgs& a, const void* qr, const void* kr, const 
                        hipStream_t stream) {
   const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kQT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((dq_kernel<D, TOut>), dim3(static_cast<unsigned>(blocks)), dim3(kDqWaves * 64), 0, stream,
+  hipLaunchKernelGGL((dq_kernel<D, TOut, false>), dim3(static_cast<unsigned>(blocks)), dim3(kDqWaves * 64), 0, stream,
                      static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
                      static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob),
                      static_cast<const TOut*>(o), static_cast<const TOut*>(dout), lse, lse2, delta,
                      static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     a.pos, a.nax, a.tab, a.max_pos, a.scale, a.scale * kLog2e);
+                     a.pos, a.nax, a.tab, a.max_pos, a.scale, a.scale * kLog2e, a.rcu, a.vfirst);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.vfirst == nullptr) return e;
+  hipLaunchKernelGGL((dq_kernel<D, TOut, true>), dim3(static_cast<unsigned>(blocks)), dim3(kDqWaves * 64), 0, stream,
+                     static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
+                     static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob),
+                     static_cast<const TOut*>(o), static_cast<const TOut*>(dout), lse, lse2, delta,
+                     static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
+                     a.pos, a.nax, a.tab, a.max_pos, a.scale, a.scale * kLog2e, a.rcu, a.vfirst);
   return hipGetLastError();
 }
 

@@ -43,12 +43,13 @@ __device__ __forceinline__ void load_q8(const T* p, bool ok, float (&x)[8]) {
   }
 }
 
-template <int D, typename TIn>
+template <int D, typename TIn, bool kMulti>
 __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     const TIn* __restrict__ q, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     TIn* __restrict__ o, float* __restrict__ lse, const int* __restrict__ cu, const int* __restrict__ order,
     const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax,
-    const float2* __restrict__ tab, int max_pos, float scale_log2) {
+    const float2* __restrict__ tab, int max_pos, float scale_log2, const int* __restrict__ rcu,
+    const int* __restrict__ vfirst) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;                   // 16-byte chunks per row
@@ -80,6 +81,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   const int hh = lane >> 5;
   const int qi = qbase + wave * 32 + (lane & 31);
   const bool qok = qi < L;
+  // A multi-segment tile (several tiny segments, at most 255 tokens) is left
+  // to the kMulti instance, where a query meets only the keys of its own
+  // segment; the ordinary instance carries none of that code.
+  const int f0 = vfirst != nullptr ? vfirst[it.seg] : it.seg;
+  const int f1 = vfirst != nullptr ? vfirst[it.seg + 1] : it.seg + 1;
+  if ((f1 - f0 > 1) != kMulti) return;
   const long long qrow = (static_cast<long long>(s0) + qi) * heads + head;
 
   // Q fragments (B operand of S^T = K Q^T): Q[q][16kk + 8h .. +8], rotated.
@@ -163,7 +170,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     return __builtin_bit_cast(bf16x8, r);
   };
 
-  float m_run = -INFINITY;  // running max, log2 units, same in both lane halves
+  // Running max, log2 units, same in both lane halves.  It starts finite, so
+  // a key tile that a multi-segment tile masks entirely for this query leaves
+  // it (and the sums) untouched instead of producing -inf - (-inf).
+  float m_run = -1e30f;
   float l_run = 0.f;        // this lane half's partial row sum
   f32x16 oacc[NDB];
 #pragma unroll
@@ -202,12 +212,24 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     // reads.
     load_rows(kseg, min(k0 + 3 * kKT, last_k0), sKb[b]);
     load_rows(vseg, min(k0 + 2 * kKT, last_k0), sVb[(b + 2) % 3]);
-    if (k0 + kKT > L) {  // only the segment's last tile holds keys past its end
+    if (kMulti || k0 + kKT > L) {  // keys past the segment's end, or outside the query's segment
+      if constexpr (kMulti) {
+        int qlo, qhi;
+        member_bounds(rcu, f0, f1, s0, s1, min(qi, L - 1), qlo, qhi);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (k0 + kb * 32 + acc_row(i, hh) >= L) scur[kb][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + acc_row(i, hh);
+            if (key < qlo || key >= qhi) scur[kb][i] = -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (k0 + kb * 32 + acc_row(i, hh) >= L) scur[kb][i] = -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -289,10 +311,18 @@ hipError_t launch_fwd_t(const AttnArgs& a, const void* q, const void* kr, const 
                         hipStream_t stream) {
   const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kQT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
+  // The ordinary tiles, then (with merged tiny segments) the multi-segment
+  // ones; each launch's blocks exit at once on the other kind of item.
+  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, false>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
                      static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
                      static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e);
+                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.vfirst == nullptr) return e;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, true>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
+                     static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
+                     static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
+                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst);
   return hipGetLastError();
 }
 

@@ -64,16 +64,35 @@ __device__ __forceinline__ int acc_row(int i, int h) { return 16 * (i >> 3) + 8 
 
 // Masks the 8 accumulator elements of group g (elements 8g .. 8g + 7, the
 // rows acc_row(8g + c, h) = 16g + 8h + c of a 32-row block): element c is set
-// to `fill` unless c < valid.  Built from bit tests instead of compares, so
+// to `fill` unless lo <= c < hi.  Built from bit tests instead of compares, so
 // it holds no lane masks in scalar registers.
-__device__ __forceinline__ void mask_rows8(f32x16& acc, int g, int valid, float fill) {
-  const unsigned keep_bits = (1u << min(max(valid, 0), 8)) - 1u;  // bit c: element c is kept
+__device__ __forceinline__ void mask_rows8_range(f32x16& acc, int g, int lo, int hi, float fill) {
+  const unsigned keep_bits = ((1u << min(max(hi, 0), 8)) - 1u) & ~((1u << min(max(lo, 0), 8)) - 1u);
   const int fill_bits = __float_as_int(fill);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const int keep = static_cast<int>(keep_bits << (31 - c)) >> 31;  // 0 or -1
     acc[8 * g + c] = __int_as_float((__float_as_int(acc[8 * g + c]) & keep) | (fill_bits & ~keep));
   }
+}
+
+__device__ __forceinline__ void mask_rows8(f32x16& acc, int g, int valid, float fill) {
+  mask_rows8_range(acc, g, 0, valid, fill);
+}
+
+// For a virtual segment [s0, s1) made of real segments f0 .. f1 - 1 (cu:
+// their offsets), the bounds [lo, hi) relative to s0 of the real segment that
+// holds token s0 + t: a row of a multi-segment tile meets only these rows.
+__device__ __forceinline__ void member_bounds(const int* __restrict__ cu, int f0, int f1, int s0, int s1, int t,
+                                              int& lo, int& hi) {
+  const int tok = s0 + t;
+  int a = f0, b = f1;
+  while (b - a > 1) {
+    const int mid = (a + b) >> 1;
+    if (cu[mid] <= tok) a = mid; else b = mid;
+  }
+  lo = min(max(cu[a], s0), s1) - s0;
+  hi = min(max(cu[a + 1], s0 + lo), s1) - s0;
 }
 
 // A [rows][D] bf16 tile in LDS, rows of D*2 bytes, 16-byte chunks XOR-swizzled

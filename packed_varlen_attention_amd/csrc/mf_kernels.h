@@ -33,6 +33,12 @@ hipError_t launch_rope_apply(const void* src, int src_dtype, void* dst, int dst_
 // Longest-first schedule of (segment, tile) work; see sched.hip.
 hipError_t launch_sched(const int* cu_seqlens, int n_segments, int n_tokens, int tile, int* order, int* pt,
                         hipStream_t stream);
+// Virtual segments: runs of tiny segments (at most kTinySegment tokens)
+// merged for multi-segment tiles (see sched.hip); vcu and vfirst hold
+// n_segments + 1 ints each.
+constexpr int kTinySegment = 128;
+hipError_t launch_merge_tiny(const int* cu_seqlens, int n_segments, int n_tokens, int* vcu, int* vfirst,
+                             hipStream_t stream);
 // Blocks to launch for a schedule with the given tile size (an upper bound).
 long long sched_grid(int n_tokens, int n_segments, int heads, int tile);
 
@@ -55,6 +61,11 @@ struct AttnArgs {
   float scale;
   const int* order;  // schedule: segments longest first
   const int* pt;     // schedule: tile prefix in that order
+  // Multi-segment tiles: cu_seqlens above holds the virtual segments; rcu is
+  // the caller's cu_seqlens and vfirst[v] the first real segment of virtual
+  // segment v (both nullptr: every virtual segment is one real segment).
+  const int* rcu;
+  const int* vfirst;
 };
 
 // q: caller's (rotated in-kernel), kr/vb: bf16 [N][H][D] (kr already rotated).

@@ -89,6 +89,93 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* __restrict__
   if (threadIdx.x == 0) pt[n_seg] = sCarry;
 }
 
+// Multi-segment tiles.  Tiny segments (at most kTinyLen tokens) that follow
+// one another in the stream and start in the same kTinyLen-token window of it
+// form one virtual segment, which the attention kernels cover with a single
+// tile and a per-lane block-diagonal mask.  Such a group spans at most
+// 2 kTinyLen - 1 tokens (its last member starts inside the window and is at
+// most kTinyLen long); every other segment is a virtual segment of its own.
+// vcu[v] = first token of virtual segment v and vfirst[v] = its first
+// segment; entries from the last virtual segment to n_seg hold the end and
+// n_seg (zero-length virtual segments), so n_seg + 1 entries always suffice
+// and the virtual count never exceeds n_seg.  Merging pays only when tiny
+// segments carry most of the work: a shared tile runs in a launch of its own,
+// while unmerged tiny tiles fill the idle tail of the long segments' launch.
+// So groups form only when tiny segments hold at least half of the tokens;
+// otherwise every segment is its own virtual segment.
+constexpr int kTinyLen = kTinySegment;
+
+__global__ __launch_bounds__(kThreads) void merge_kernel(const int* __restrict__ cu, int n_seg, int n_tokens,
+                                                         int* __restrict__ vcu, int* __restrict__ vfirst) {
+  __shared__ int sWave[kThreads / 64];
+  __shared__ int sCarry;
+  __shared__ int sTiny;
+  if (threadIdx.x == 0) {
+    sCarry = 0;
+    sTiny = 0;
+  }
+  __syncthreads();
+  auto start_of = [&](int s) { return min(max(cu[s], 0), n_tokens); };
+  auto len_of = [&](int s) {
+    const int a = start_of(s);
+    return min(max(cu[s + 1], a), n_tokens) - a;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int tiny = 0;  // tokens in tiny segments
+  for (int s = threadIdx.x; s < n_seg; s += kThreads) {
+    const int l = len_of(s);
+    if (l <= kTinyLen) tiny += l;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) tiny += __shfl_xor(tiny, d, 64);
+  if (lane == 0) atomicAdd(&sTiny, tiny);
+  __syncthreads();
+  const bool merge = 2LL * sTiny >= n_tokens && n_tokens > 0;
+  for (int base = 0; base < n_seg; base += kThreads) {
+    const int s = base + threadIdx.x;
+    int f = 0;  // 1: segment s starts a virtual segment
+    if (s < n_seg) {
+      f = 1;
+      if (merge && s > 0 && len_of(s) <= kTinyLen && len_of(s - 1) <= kTinyLen && cu[s - 1] <= cu[s] &&
+          start_of(s) / kTinyLen == start_of(s - 1) / kTinyLen)
+        f = 0;
+    }
+    int x = f;  // inclusive scan over the block
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) sWave[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int w = lane < kThreads / 64 ? sWave[lane] : 0;
+#pragma unroll
+      for (int d = 1; d < kThreads / 64; d <<= 1) {
+        const int y = __shfl_up(w, d, 64);
+        if (lane >= d) w += y;
+      }
+      if (lane < kThreads / 64) sWave[lane] = w;
+    }
+    __syncthreads();
+    const int incl = x + (wave > 0 ? sWave[wave - 1] : 0) + sCarry;
+    if (s < n_seg && f) {
+      vcu[incl - 1] = start_of(s);
+      vfirst[incl - 1] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x == kThreads - 1) sCarry = incl;
+    __syncthreads();
+  }
+  const int n_v = sCarry;
+  const int end = n_seg > 0 ? min(max(cu[n_seg], start_of(n_seg - 1)), n_tokens) : 0;
+  for (int v = n_v + threadIdx.x; v <= n_seg; v += kThreads) {
+    vcu[v] = end;
+    vfirst[v] = n_seg;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_sched(const int* cu_seqlens, int n_segments, int n_tokens, int tile, int* order, int* pt,
@@ -102,6 +189,12 @@ long long sched_grid(int n_tokens, int n_segments, int heads, int tile) {
   const long long per_xcd_heads = (heads + 7) / 8;
   const long long tiles_bound = (static_cast<long long>(n_tokens) + tile - 1) / tile + n_segments;
   return 8LL * per_xcd_heads * tiles_bound;
+}
+
+hipError_t launch_merge_tiny(const int* cu_seqlens, int n_segments, int n_tokens, int* vcu, int* vfirst,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel, dim3(1), dim3(kThreads), 0, stream, cu_seqlens, n_segments, n_tokens, vcu, vfirst);
+  return hipGetLastError();
 }
 
 }  // namespace mf

@@ -94,6 +94,37 @@ def assert_close_large_values(got, ref, label: str, rel_large: float = 1.5e-2, r
     assert rel <= rel_rms_max, f"{label}: relative rms {rel} > {rel_rms_max}"
 
 
+# The attention kernels cover runs of tiny segments with one multi-segment
+# tile (the library's stated rule): when tiny segments (at most TINY_LEN
+# tokens) hold at least half of the pack's tokens, consecutive tiny segments
+# whose first tokens lie in the same TINY_LEN-token window of the stream
+# share a tile.  A merged segment meets its keys on other tile boundaries
+# than when it runs alone, so its outputs equal a standalone run's only up to
+# rounding; every other segment's outputs are bitwise the same.
+TINY_LEN = 128
+
+
+def merged_segments(cu) -> set:
+    cu = [int(x) for x in cu]
+    n = len(cu) - 1
+    tokens = cu[-1] - cu[0] if n else 0
+    tiny = sum(cu[s + 1] - cu[s] for s in range(n) if cu[s + 1] - cu[s] <= TINY_LEN)
+    if n == 0 or 2 * tiny < tokens or tokens > 2 * TINY_LEN * n:
+        return set()
+    first = []  # index of the first segment of each group
+    for s in range(n):
+        if s > 0 and cu[s + 1] - cu[s] <= TINY_LEN and cu[s] - cu[s - 1] <= TINY_LEN and \
+                cu[s] // TINY_LEN == cu[s - 1] // TINY_LEN:
+            continue
+        first.append(s)
+    first.append(n)
+    out = set()
+    for a, b in zip(first[:-1], first[1:]):
+        if b - a > 1:
+            out.update(range(a, b))
+    return out
+
+
 class Case:
     """A packed workload with inputs on host (as exact float32 values) and GPU."""
 

@@ -9,7 +9,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import THETA, Case, assert_close, assert_close_large_values, assert_close_scaled, host_f64, note
+from gpu_util import (THETA, Case, assert_close, assert_close_large_values, assert_close_scaled, host_f64,
+                      merged_segments, note)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +72,9 @@ def test_deterministic_and_segment_local():
     b = _run(c)
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
-    # per-segment runs give bitwise the same gradients
+    # per-segment runs give bitwise the same gradients (a segment sharing a
+    # multi-segment tile, see gpu_util.merged_segments, up to rounding)
+    merged = merged_segments(c.cu)
     for s in (0, 2, 3):
         lo, hi = int(c.cu[s]), int(c.cu[s + 1])
         cu1 = torch.tensor([0, hi - lo], dtype=torch.int32).cuda()
@@ -81,8 +84,11 @@ def test_deterministic_and_segment_local():
         o1, l1 = mf.attn_fwd(sl[0], sl[1], sl[2], cu1, hi - lo, p1, THETA, c.max_pos)
         g = mf.attn_bwd(sl[0], sl[1], sl[2], o1, l1, sl[3], cu1, hi - lo, p1, THETA, c.max_pos)
         torch.cuda.synchronize()
-        for x, y in zip(g, a):
-            assert torch.equal(x.view(torch.int16), y[lo:hi].view(torch.int16))
+        for x, y, name in zip(g, a, ("dQ", "dK", "dV")):
+            if s in merged:
+                assert_close_scaled(host_f64(x), host_f64(y[lo:hi]), f"{name} segment {s} (multi-segment tile)")
+            else:
+                assert torch.equal(x.view(torch.int16), y[lo:hi].view(torch.int16))
 
 
 def test_gradient_sums_match_invariants():

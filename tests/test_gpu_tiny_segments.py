@@ -1,0 +1,140 @@
+"""Multi-segment tiles: runs of tiny segments (captions, thumbnails, 1-token
+unconditional texts) share one attention tile with a block-diagonal mask.
+
+Parity against the fp64 oracle at the attention tests' bars on layouts that
+are all tiny segments, tiny runs between long segments, lengths at the
+128-token threshold, many 1-token and zero-length segments, and the stress
+pack; the layouts are checked to produce multi-segment tiles
+(gpu_util.merged_segments states the rule).  Isolation inside a shared tile
+is exact: outlier keys and values in one member change no bit of any other
+member's outputs or gradients, since masked scores are exactly -inf and
+their weights exactly 0.  Packs whose tiny segments hold under half of the
+tokens (the stress pack) are not merged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (THETA, Case, assert_close, assert_close_large_values, assert_close_scaled, host_f64,
+                      merged_segments, note)
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-2
+
+
+def _mf():
+    import packed_varlen_attention_amd as mf
+    return mf
+
+
+def _layouts():
+    rng = np.random.default_rng(90)
+    all_tiny = [(int(rng.integers(0, 40)), int(rng.integers(0, 5)), int(rng.integers(0, 9))) for _ in range(60)]
+    mixed = []  # long segments between runs of tiny ones, tiny ones holding over half of the tokens
+    for _ in range(5):
+        mixed.append((int(rng.integers(20, 60)), int(rng.integers(10, 13)), int(rng.integers(10, 13))))
+        mixed += [(int(rng.integers(0, 30)), int(rng.integers(1, 4)), int(rng.integers(1, 10)))
+                  for _ in range(int(rng.integers(8, 14)))]
+    threshold = [(127, 0, 0), (128, 0, 0), (0, 1, 1), (129, 0, 0), (1, 0, 0), (126, 1, 1), (1, 1, 1), (0, 0, 0),
+                 (0, 8, 16), (64, 0, 0), (1, 0, 0)]
+    ones = [(1, 0, 0)] * 60 + [(0, 0, 0)] * 5 + [(0, 1, 1)] * 40 + [(2, 0, 0)] * 30 + [(1, 1, 2)] * 20 + [(1, 0, 0)] * 30
+    return {"all_tiny": all_tiny, "mixed": mixed, "threshold": threshold, "ones": ones}
+
+
+LAYOUTS = _layouts()
+
+
+@pytest.mark.parametrize("name", sorted(LAYOUTS))
+@pytest.mark.parametrize("d", [128, 64])
+def test_forward_and_backward_against_oracle(name, d):
+    mf = _mf()
+    c = Case(LAYOUTS[name], 1 << 20, 3, d, "bf16", seed=91, with_dout=True)
+    merged = merged_segments(c.cu)
+    assert merged, "layout must produce multi-segment tiles"
+    note(f"tiny segments {name} D={d} {c.describe()} merged={len(merged)}")
+    o, lse = mf.attn_fwd(c.tq, c.tk, c.tv, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    dq, dk, dv = mf.attn_bwd(c.tq, c.tk, c.tv, o, lse, c.tdo, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_fwd(c.q, c.k, c.v, c.cu, c.pos, THETA)
+    assert_close(host_f64(o)[: c.n], ro, O_MAX, O_MEAN, "O")
+    assert_close(host_f64(lse)[:, : c.n], rl, LSE_MAX, LSE_MAX, "LSE")
+    rq, rk, rv = oracle.attn_bwd(c.q, c.k, c.v, c.do, c.cu, c.pos, THETA)
+    # 1-token and very short segments have large per-element gradients (one key holds all the weight); the
+    # magnitude-aware bar applies the fixed 2e-2 to |ref| <= 4 and a relative bar above
+    assert_close_large_values(host_f64(dq), rq, "dQ")
+    assert_close_large_values(host_f64(dk), rk, "dK")
+    assert_close_large_values(host_f64(dv), rv, "dV")
+
+
+def test_members_of_a_shared_tile_are_isolated_bitwise():
+    mf = _mf()
+    c = Case(LAYOUTS["mixed"], 1 << 20, 2, 128, "bf16", seed=92, with_dout=True)
+    merged = sorted(merged_segments(c.cu))
+    victim = merged[len(merged) // 2]
+    a, b = int(c.cu[victim]), int(c.cu[victim + 1])
+    while b == a:  # a member with tokens
+        victim += 1
+        a, b = int(c.cu[victim]), int(c.cu[victim + 1])
+    note(f"isolation victim={victim} rows [{a}, {b})")
+
+    def run(k, v):
+        o, lse = mf.attn_fwd(c.tq, k, v, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+        g = mf.attn_bwd(c.tq, k, v, o, lse, c.tdo, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+        torch.cuda.synchronize()
+        return (o, lse) + tuple(g)
+
+    base = run(c.tk, c.tv)
+    k2, v2 = c.tk.clone(), c.tv.clone()
+    k2[a:b] = 30.0
+    v2[a:b] = -30.0
+    alt = run(k2, v2)
+    for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"), base, alt):
+        if name == "LSE":
+            assert torch.equal(x[:, :a], y[:, :a]) and torch.equal(x[:, b:c.n], y[:, b:c.n]), name
+        else:
+            assert torch.equal(x[:a].view(torch.int16), y[:a].view(torch.int16)), name
+            assert torch.equal(x[b:c.n].view(torch.int16), y[b:c.n].view(torch.int16)), name
+    assert not torch.equal(base[0][a:b].view(torch.int16), alt[0][a:b].view(torch.int16))
+
+
+def test_stress_pack_thumbnails_stay_in_the_long_segments_launch():
+    """The stress pack (a 2048^2 image, both 4:1 panoramas, 64 thumbnails of 80 tokens): tiny segments hold 17%
+    of its tokens, below the half that merging needs, so the thumbnails keep tiles of their own, which fill the
+    long segments' tail; sampled rows of every kind of segment against the oracle."""
+    mf = _mf()
+    w = workloads.stress()
+    c = Case(w.samples, w.budget, 4, w.head_dim, "bf16", w.seed)
+    assert not merged_segments(c.cu)
+    note(f"stress thumbnails {c.describe()}")
+    o, lse = mf.attn_fwd(c.tq, c.tk, c.tv, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    torch.cuda.synchronize()
+    rows = []
+    for s in list(range(0, len(c.cu) - 1, 5)) + [0, 1, 2]:
+        a, b = int(c.cu[s]), int(c.cu[s + 1])
+        if b > a:
+            rows += sorted({a, b - 1, (a + b) // 2})
+    pairs = [(int(t), h) for t in sorted(set(rows)) for h in range(c.heads)]
+    ref_o, ref_l = oracle.attn_fwd_rows(c.q, c.k, c.v, c.cu, c.pos, pairs, THETA)
+    t = torch.tensor([r[0] for r in pairs]).cuda()
+    hd = torch.tensor([r[1] for r in pairs]).cuda()
+    assert_close(host_f64(o[t, hd]), ref_o, O_MAX, O_MEAN, "O sampled")
+    assert_close(host_f64(lse[hd, t]), ref_l, LSE_MAX, LSE_MAX, "LSE sampled")
+
+
+def test_single_token_members_closed_form():
+    """A 1-token segment attends only to itself: O = V, dV = dO exactly, and dQ = dK = 0 up to the rounding
+    of dP - Delta (both dot(dO, V), summed in different orders)."""
+    mf = _mf()
+    c = Case([(1, 0, 0)] * 150 + [(0, 0, 0)] * 5 + [(0, 1, 1)] * 40, 1 << 20, 3, 128, "bf16", seed=93,
+             with_dout=True)
+    assert len(merged_segments(c.cu)) == len(c.cu) - 1
+    note(f"single-token members {c.describe()}")
+    o, lse = mf.attn_fwd(c.tq, c.tk, c.tv, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    dq, dk, dv = mf.attn_bwd(c.tq, c.tk, c.tv, o, lse, c.tdo, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    torch.cuda.synchronize()
+    assert torch.equal(o[: c.n].view(torch.int16), c.tv[: c.n].view(torch.int16))
+    assert torch.equal(dv[: c.n].view(torch.int16), c.tdo[: c.n].view(torch.int16))
+    assert float(dq[: c.n].float().abs().max()) < 1e-4 and float(dk[: c.n].float().abs().max()) < 1e-4

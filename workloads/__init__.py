@@ -173,6 +173,15 @@ def stress() -> Workload:
                     head_dim=128, dtype="bf16", seed=4)
 
 
+def captions(seed: int = 8, n: int = 1500) -> Workload:
+    """A pack of short text segments only (the prompts of a training batch as
+    the text side sees them): 1500 captions of 16-120 tokens, ~100k tokens.
+    Tiny segments hold all of its work, the case for multi-segment tiles."""
+    rng = np.random.default_rng([seed, STREAM_SHAPES])
+    samples: List[Sample] = [(int(rng.integers(16, 121)), 0, 0) for _ in range(n)]
+    return Workload("captions", tuple(samples), budget=1 << 20, n_heads=24, head_dim=128, dtype="bf16", seed=seed)
+
+
 def all_workloads() -> List[Workload]:
     return [tiny(), cfg1024(), mixed50k(), stress(), mixed50k(backward=True)]
 
