@@ -112,8 +112,12 @@ def cpu_baseline(w, samples, q, k, v, do, threads: int, min_seconds: float = 10.
 
     avail = len(os.sched_getaffinity(0))
     use = max(1, min(threads, avail))
-    p = oracle.pack(samples, w.budget)
-    pos = oracle.positions(samples, p["n_packed"])
+    if w.editing:
+        p = oracle.pack_edit(samples, w.budget)
+        pos = oracle.positions_edit(samples, p["n_packed"])
+    else:
+        p = oracle.pack(samples, w.budget)
+        pos = oracle.positions(samples, p["n_packed"])
     cu = p["cu_seqlens"]
     sum_l2 = float(np.sum(np.diff(cu).astype(np.float64) ** 2))
     secs = 0.0
@@ -137,7 +141,7 @@ def cpu_baseline(w, samples, q, k, v, do, threads: int, min_seconds: float = 10.
     }
 
 
-def flow_timing(mf, workloads, w, samples, packres, n_tokens: int, dev, reps: int = 20) -> dict:
+def flow_timing(mf, workloads, w, samples, packres, n_tokens: int, dev, reps: int = 20, cpu: bool = False) -> dict:
     """Mean per-launch time and algorithmic GB/s of the rectified-flow and CFG passes."""
     import numpy as np
     import torch
@@ -192,10 +196,30 @@ def flow_timing(mf, workloads, w, samples, packres, n_tokens: int, dev, reps: in
                                                    out=gv, trace=tr), 3 * cond_img * row)
     out["note"] = (f"latents [N][{c}] bf16 on the bench pack (N={n_tokens}, {noised} noised rows); CFG on the "
                    f"1024^2 packed-CFG pack ({gn} tokens, {len(g.samples) // 2} pairs)")
+    for name in ("rf_noise", "rf_loss", "cfg_combine"):
+        out[name]["roofline"] = {"bound": "hbm", "achieved": out[name]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(out[name]["gbs"] / PEAK_HBM_GBS, 4)}
+    if cpu:
+        # the oracle (test infrastructure, never the product path): the loss over the whole pack
+        from oracle import flow as oflow
+        f64 = lambda x: x.float().cpu().numpy().astype(np.float64)  # noqa: E731
+        vz, zz, ez = f64(v), f64(z), f64(eps)
+        cpn = cp.cpu().numpy()
+        t0 = time.perf_counter()
+        reps_cpu = 0
+        while time.perf_counter() - t0 < 2.0:
+            oflow.rf_loss(vz, zz, ez, cpn, s, frames, 1.0)
+            reps_cpu += 1
+        secs = (time.perf_counter() - t0) / reps_cpu
+        nb = out["rf_loss"]["bytes"]
+        out["cpu_baseline"] = {"value": round(nb / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"fp64 numpy oracle rf_loss over the whole pack, {reps_cpu} runs in "
+                                         f"{secs * reps_cpu:.1f} s (same algorithmic bytes as the kernel)"}
     return out
 
 
-def block_timing(mf, workloads, w, packres, n_tokens: int, max_pos: int, dev, reps: int = 10) -> dict:
+def block_timing(mf, workloads, w, packres, n_tokens: int, max_pos: int, dev, reps: int = 10,
+                 cpu: bool = False) -> dict:
     """Per-launch time and rate of the sub-block chain kernels on the bench pack, plus (for context only) the
     library GEMM of the same shapes without an epilogue."""
     import numpy as np
@@ -267,13 +291,67 @@ def block_timing(mf, workloads, w, packres, n_tokens: int, max_pos: int, dev, re
     wq_t = wq[1].t().contiguous()
     wo_t = wo[1].t().contiguous()
     mq, mo = lib_ms(h, wq_t), lib_ms(o, wo_t)
+    for name, bound in (("adaln", "hbm"), ("qkv_rope", "mfma"), ("out_gated", "mfma")):
+        e = out[name]
+        if bound == "hbm":
+            out[name]["roofline"] = {"bound": "hbm", "achieved": e["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                     "frac": round(e["gbs"] / PEAK_HBM_GBS, 4)}
+        else:
+            out[name]["roofline"] = {"bound": "mfma", "achieved": e["tflops"], "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(e["tflops"] / PEAK_BF16_TFLOPS, 4)}
     out["library_gemm_context"] = {
         "qkv_ms": round(mq, 4), "qkv_tflops": round(2 * n_tokens * c * 3 * c / (mq * 1e-3) / 1e12, 1),
         "out_ms": round(mo, 4), "out_tflops": round(2 * n_tokens * c * c / (mo * 1e-3) / 1e12, 1),
         "note": "torch.mm (hipBLASLt) on the same shapes with one weight, no bias, rotation or residual"}
     out["note"] = (f"bf16 [N][{c}] rows of the bench pack (N={n_tokens}, {s} samples), one weight matrix per "
                    f"modality; bytes = activations read and written once plus the weights of one modality")
+    if cpu:
+        out["cpu_baseline"] = block_cpu_baseline(w, d, packres, heads, hd, frames)
     return out
+
+
+def block_cpu_baseline(w, d, packres, heads: int, hd: int, frames: int, min_seconds: float = 8.0) -> dict:
+    """Time the oracle (test infrastructure, never the product path) on a bounded sample of the block chain:
+    adaLN, QKV projection with the rotation and the gated output projection over 128-row slices of the pack's
+    image pieces (largest first) until about ``min_seconds`` of CPU work; reported as the projections' FLOP
+    rate."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import block
+    import workloads
+
+    cp = packres.cu_pieces.cpu().numpy()
+    s = int(packres.counts[0].item())
+    per = frames + 1
+    pieces = sorted(((int(cp[i + 1] - cp[i]), i) for i in range(per * s) if i % per != 0), reverse=True)
+    pos = packres.pos.cpu().numpy()
+    c = heads * hd
+    f64 = lambda x: workloads.bf16_bits_to_f32(x).astype(np.float64)  # noqa: E731
+    w_q = (f64(d["w_qkv0"]), f64(d["w_qkv1"]))
+    w_o = (f64(d["w_o0"]), f64(d["w_o1"]))
+    secs, rows = 0.0, 0
+    with threadpool_limits(limits=max(1, min(16, len(os.sched_getaffinity(0))))):
+        nthreads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        for length, piece in pieces:  # image pieces, largest first, in slices of 128 rows
+            sample, a0 = piece // per, int(cp[piece])
+            for r0 in range(0, length - 127, 128):
+                if secs >= min_seconds:
+                    break
+                sl = slice(a0 + r0, a0 + r0 + 128)
+                cu = [0, 0, 128]  # one sample: no text rows, 128 image rows
+                x = f64(d["x"][sl])
+                t0 = time.perf_counter()
+                h = block.adaln_modulate(x, d["shift"][sample:sample + 1], d["scale"][sample:sample + 1], cu, 1, 1)
+                block.qkv_rope(h, w_q, (d["b_qkv0"], d["b_qkv1"]), cu, 1, 1, pos[sl], heads, hd, w.theta)
+                block.out_gated_residual(f64(d["o"][sl]), x, w_o, (d["b_o0"], d["b_o1"]),
+                                         d["gate"][sample:sample + 1], cu, 1, 1)
+                secs += time.perf_counter() - t0
+                rows += 128
+    flops = 2.0 * rows * c * 4 * c  # QKV (3C outputs) + output projection (C outputs)
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(nthreads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle: adaLN + QKV projection with RoPE + gated output projection over {rows} "
+                      f"image rows (128-row slices, largest pieces first), {secs:.1f} s"}
 
 
 def main():
@@ -447,9 +525,9 @@ def main():
         roof["peak_measured"] = round(probe["tflops"], 1)
         roof["frac_measured"] = round(roof["achieved"] / probe["tflops"], 4)
     if args.flow:
-        result["flow"] = flow_timing(mf, workloads, w, samples, packres, N, dev)
+        result["flow"] = flow_timing(mf, workloads, w, samples, packres, N, dev, cpu=not args.no_cpu_baseline)
     if args.block:
-        result["block"] = block_timing(mf, workloads, w, packres, N, max_pos, dev)
+        result["block"] = block_timing(mf, workloads, w, packres, N, max_pos, dev, cpu=not args.no_cpu_baseline)
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -462,7 +540,7 @@ def main():
         c1.record()
         torch.cuda.synchronize()
         result["copy_1GiB_gbs"] = round(2 * (1 << 30) * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
-    if not args.no_cpu_baseline and args.workload == "mixed50k":
+    if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, samples, q, k, v, do, args.cpu_threads)
     print(json.dumps(result), flush=True)
 
