@@ -31,6 +31,11 @@ Readings taken where the pages are silent:
   token's position exactly as the attention path rotates them, v is not;
 * gated residual: y = x + gate (o W_o^T + b_o) with the modality's W_o [C][C],
   b_o [C] and the sample's gate for that modality.
+
+The backward functions give the gradient of a scalar loss with respect to
+every input of each chain from the gradient of its output (weights and
+biases summed over the rows of their modality, modulation vectors over the
+rows of their sample and modality).
 """
 from __future__ import annotations
 
@@ -112,3 +117,82 @@ def out_gated_residual(o: np.ndarray, x: np.ndarray, w: Tuple[np.ndarray, np.nda
     for a, e, s, m in row_groups(cu_pieces, n_samples, frames):
         y[a:e] = x[a:e] + gate[s, m] * linear(o[a:e], w[m], b[m])
     return y
+
+
+# ---------------------------------------------------------------------------
+# Backward of the chains (gradients of a scalar loss with respect to every
+# input, given the gradient of the chain's output).  The rotation is
+# orthogonal, so its gradient is the inverse rotation.
+# ---------------------------------------------------------------------------
+
+def adaln_modulate_bwd(dh: np.ndarray, x: np.ndarray, shift: np.ndarray, scale: np.ndarray,
+                       cu_pieces: Sequence[int], n_samples: int, frames: int, eps: float = 1e-6):
+    """(dx [N][C], dshift [S][2][C], dscale [S][2][C]) for h = LN(x) (1 + scale[s][m]) + shift[s][m]."""
+    dh = np.asarray(dh, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    scale = np.asarray(scale, dtype=np.float64)
+    dx = np.zeros_like(x)
+    dshift = np.zeros(np.shape(shift), dtype=np.float64)
+    dscale = np.zeros(np.shape(scale), dtype=np.float64)
+    for a, b, s, m in row_groups(cu_pieces, n_samples, frames):
+        if b == a:
+            continue
+        xs = x[a:b]
+        mean = xs.mean(axis=-1, keepdims=True)
+        var = ((xs - mean) ** 2).mean(axis=-1, keepdims=True)
+        rstd = 1.0 / np.sqrt(var + eps)
+        xhat = (xs - mean) * rstd
+        g = dh[a:b]
+        dshift[s, m] += g.sum(axis=0)
+        dscale[s, m] += (g * xhat).sum(axis=0)
+        dxhat = g * (1.0 + scale[s, m])
+        dx[a:b] = rstd * (dxhat - dxhat.mean(axis=-1, keepdims=True)
+                          - xhat * (dxhat * xhat).mean(axis=-1, keepdims=True))
+    return dx, dshift, dscale
+
+
+def qkv_rope_bwd(dq: np.ndarray, dk: np.ndarray, dv: np.ndarray, h: np.ndarray,
+                 w: Tuple[np.ndarray, np.ndarray], cu_pieces: Sequence[int], n_samples: int, frames: int,
+                 pos: Optional[np.ndarray], theta: float = 10000.0):
+    """(dh [N][C], (dW_text, dW_image) [3C][C], (db_text, db_image) [3C]) given the gradients of the rotated
+    q, k and of v ([N][H][D] each)."""
+    h = np.asarray(h, dtype=np.float64)
+    n, c = h.shape
+    dq = np.asarray(dq, dtype=np.float64)
+    dk = np.asarray(dk, dtype=np.float64)
+    if pos is not None:
+        dq = rope_axes(dq, pos, theta, inverse=True)
+        dk = rope_axes(dk, pos, theta, inverse=True)
+    g = np.concatenate([dq.reshape(n, c), dk.reshape(n, c), np.asarray(dv, dtype=np.float64).reshape(n, c)], axis=1)
+    dh = np.zeros_like(h)
+    dw = [np.zeros((3 * c, c)), np.zeros((3 * c, c))]
+    db = [np.zeros(3 * c), np.zeros(3 * c)]
+    for a, e, s, m in row_groups(cu_pieces, n_samples, frames):
+        dh[a:e] = g[a:e] @ np.asarray(w[m], dtype=np.float64)
+        dw[m] += g[a:e].T @ h[a:e]
+        db[m] += g[a:e].sum(axis=0)
+    return dh, tuple(dw), tuple(db)
+
+
+def out_gated_residual_bwd(dy: np.ndarray, o: np.ndarray, x: np.ndarray, w: Tuple[np.ndarray, np.ndarray],
+                           b: Tuple[Optional[np.ndarray], Optional[np.ndarray]], gate: np.ndarray,
+                           cu_pieces: Sequence[int], n_samples: int, frames: int):
+    """(dx, do [N][C], (dW_text, dW_image) [C][C], (db_text, db_image) [C], dgate [S][2][C]) for
+    y = x + gate[s][m] (o W_m^T + b_m)."""
+    dy = np.asarray(dy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64).reshape(x.shape[0], -1)
+    gate = np.asarray(gate, dtype=np.float64)
+    c = x.shape[1]
+    do = np.zeros_like(o)
+    dw = [np.zeros((c, o.shape[1])), np.zeros((c, o.shape[1]))]
+    db = [np.zeros(c), np.zeros(c)]
+    dgate = np.zeros_like(gate)
+    for a, e, s, m in row_groups(cu_pieces, n_samples, frames):
+        u = gate[s, m] * dy[a:e]
+        proj = linear(o[a:e], w[m], b[m])
+        do[a:e] = u @ np.asarray(w[m], dtype=np.float64)
+        dw[m] += u.T @ o[a:e]
+        db[m] += u.sum(axis=0)
+        dgate[s, m] += (dy[a:e] * proj).sum(axis=0)
+    return dy.copy(), do, tuple(dw), tuple(db), dgate
