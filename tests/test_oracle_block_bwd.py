@@ -54,8 +54,7 @@ def test_adaln_bwd_closed_forms():
     rng = np.random.default_rng(43)
     x = rng.standard_normal((14, 8))
     z = np.zeros((2, 2, 8))
-    # a gradient that is constant along a row, or proportional to the normalised row, is removed by the
-    # normalisation: LN is invariant to shifting and rescaling its input row
+    # LN is invariant to shifting its input row: a gradient constant along a row is removed exactly
     dy_const = np.repeat(rng.standard_normal((14, 1)), 8, axis=1)
     dx, dsh, _ = block.adaln_modulate_bwd(dy_const, x, z, z, CU, 2, 1)
     np.testing.assert_allclose(dx, 0.0, atol=1e-12)
