@@ -71,7 +71,7 @@ typedef int32_t mf_status;
 #define MF_BF16 0
 #define MF_F32 1
 
-#define MF_ABI_VERSION 3
+#define MF_ABI_VERSION 4
 
 /* One sample descriptor: text tokens, then a grid_h x grid_w latent grid. */
 typedef struct mf_sample {
@@ -420,14 +420,112 @@ mf_status mf_qkv_rope(const void* h, const void* w_text, const void* w_image, co
  * token's sample s and modality m (W_o,m bf16 [channels][channels], b_o,m
  * float[channels] or NULL).  o is the attention output ([N][H][D] is
  * [N][channels]); y may be x (in place) but must not overlap o.
+ * proj       bf16 [n_tokens][channels], out, or NULL: o W_o,m^T + b_o,m
+ *            before the gate, which mf_out_gated_residual_bwd needs for the
+ *            gate's gradient.
  * workspace  >= mf_block_workspace_size(n_samples, frames, 64, 0) bytes,
  *            256-byte aligned.
  */
 mf_status mf_out_gated_residual(const void* o, const void* x, const void* w_text, const void* w_image,
-                                const float* b_text, const float* b_image, const float* gate, void* y,
+                                const float* b_text, const float* b_image, const float* gate, void* y, void* proj,
                                 const int32_t* cu_pieces, int32_t n_samples, int32_t frames,
                                 int32_t n_tokens, int32_t channels, void* workspace,
                                 size_t workspace_bytes, void* stream, mf_trace* trace);
+
+/*
+ * Backward of the three chains: the gradient of a scalar loss with respect to
+ * every input of a chain, given the gradient of its output (the chain rule
+ * through the forward definitions above).  Sums over rows -- weight, bias and
+ * modulation gradients -- are deterministic: partial sums over fixed blocks of
+ * rows, then added in a fixed order, so repeated calls give identical bits.
+ * Weight and bias gradients are float [out][in] / float[out] per modality and
+ * are OVERWRITTEN (not accumulated); modulation gradients are float
+ * [n_samples][2][channels].  A modality without tokens gets zero gradients.
+ * Rows outside every piece take no part in the sums.
+ *
+ * The weight gradient gathers each modality's rows into token-contiguous
+ * operands in the workspace, so n_tokens is at most 2^23 - 512 for
+ * mf_qkv_rope_bwd and mf_out_gated_residual_bwd, and channels at most 16384.
+ */
+
+/* Bytes of workspace of mf_adaln_modulate_bwd (0 for unsupported sizes). */
+size_t mf_adaln_modulate_bwd_workspace_size(int32_t n_samples, int32_t frames, int32_t n_tokens,
+                                            int32_t channels);
+
+/*
+ * mf_adaln_modulate_bwd -- backward of mf_adaln_modulate:
+ *   dx = dres + rstd (g - mean(g) - xhat mean(g xhat)),  g = dh (1 + scale[s][m]),
+ *   dshift[s][m] = sum of dh, dscale[s][m] = sum of dh xhat over the rows of
+ *   sample s, modality m (xhat = LN(x), statistics recomputed from x as the
+ *   forward computes them).
+ * dh, x      bf16 [n_tokens][channels], in.
+ * scale      the forward's float [n_samples][2][channels], in.
+ * dres       bf16 [n_tokens][channels] or NULL: a gradient added to dx (the
+ *            residual branch of x), in.  dx may alias dres, not dh or x.
+ * dx         bf16 [n_tokens][channels], out.
+ * dshift, dscale  float [n_samples][2][channels], out.
+ * channels a multiple of 512, at most 8192.
+ */
+mf_status mf_adaln_modulate_bwd(const void* dh, const void* x, const float* scale, const void* dres, void* dx,
+                                float* dshift, float* dscale, const int32_t* cu_pieces, int32_t n_samples,
+                                int32_t frames, int32_t n_tokens, int32_t channels, float eps, void* workspace,
+                                size_t workspace_bytes, void* stream, mf_trace* trace);
+
+/* Bytes of workspace of mf_qkv_rope_bwd; max_pos 0 when pos will be NULL (0
+ * for unsupported sizes). */
+size_t mf_qkv_rope_bwd_workspace_size(int32_t n_samples, int32_t frames, int32_t n_tokens, int32_t n_heads,
+                                      int32_t head_dim, int32_t max_pos);
+
+/*
+ * mf_qkv_rope_bwd -- backward of mf_qkv_rope.  With G = [dq' | dk' | dv]
+ * ([n_tokens][3 channels], dq' and dk' the inverse rotation of dq and dk by
+ * pos, or dq and dk themselves when pos is NULL):
+ *   dh = G W_m per token of modality m, dW_m = G_m^T h_m, db_m = column sums
+ *   of G_m, where _m takes modality m's rows.
+ * dq, dk, dv bf16 [n_tokens][n_heads][head_dim], in: gradients of the
+ *            projection's outputs as mf_qkv_rope wrote them (rotated q, k).
+ * h          bf16 [n_tokens][channels], in: the forward's input.
+ * w_text, w_image  the forward's weights, bf16 [3 channels][channels], in.
+ * dh         bf16 [n_tokens][channels], out (must not overlap the inputs).
+ * dw_text, dw_image  float [3 channels][channels], out.
+ * db_text, db_image  float [3 channels], out, or NULL to skip.
+ * pos, nax, theta, max_pos  as given to mf_qkv_rope.
+ */
+mf_status mf_qkv_rope_bwd(const void* dq, const void* dk, const void* dv, const void* h, const void* w_text,
+                          const void* w_image, void* dh, float* dw_text, float* dw_image, float* db_text,
+                          float* db_image, const int32_t* cu_pieces, int32_t n_samples, int32_t frames,
+                          const int32_t* pos, int32_t nax, double theta, int32_t max_pos, int32_t n_tokens,
+                          int32_t n_heads, int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream,
+                          mf_trace* trace);
+
+/* Bytes of workspace of mf_out_gated_residual_bwd (0 for unsupported sizes). */
+size_t mf_out_gated_residual_bwd_workspace_size(int32_t n_samples, int32_t frames, int32_t n_tokens,
+                                                int32_t channels);
+
+/*
+ * mf_out_gated_residual_bwd -- backward of mf_out_gated_residual.  With
+ * u = gate[s][m] dy per token of sample s, modality m:
+ *   d_o = u W_o,m, dW_o,m = u_m^T o_m, db_o,m = column sums of u_m,
+ *   dgate[s][m] = sum of dy proj over the rows of sample s, modality m.
+ * The gradient with respect to x is dy itself (the residual path); no call
+ * is needed for it.
+ * dy         bf16 [n_tokens][channels], in.
+ * o          the forward's attention output, bf16 [n_tokens][channels], in.
+ * proj       the forward's pre-gate projection (mf_out_gated_residual's
+ *            proj output), bf16 [n_tokens][channels], in.
+ * w_text, w_image  the forward's weights, bf16 [channels][channels], in.
+ * gate       float [n_samples][2][channels], in.
+ * d_o        bf16 [n_tokens][channels], out (must not overlap the inputs).
+ * dw_text, dw_image  float [channels][channels], out.
+ * db_text, db_image  float [channels], out, or NULL to skip.
+ * dgate      float [n_samples][2][channels], out.
+ */
+mf_status mf_out_gated_residual_bwd(const void* dy, const void* o, const void* proj, const void* w_text,
+                                    const void* w_image, const float* gate, void* d_o, float* dw_text,
+                                    float* dw_image, float* db_text, float* db_image, float* dgate,
+                                    const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
+                                    int32_t channels, void* workspace, size_t workspace_bytes, void* stream,
+                                    mf_trace* trace);
 
 /*
  * mf_mfma_probe -- measurement helper, not a step of the path: the sustained

@@ -155,7 +155,8 @@ def qkv_rope_bwd(dq: np.ndarray, dk: np.ndarray, dv: np.ndarray, h: np.ndarray,
                  w: Tuple[np.ndarray, np.ndarray], cu_pieces: Sequence[int], n_samples: int, frames: int,
                  pos: Optional[np.ndarray], theta: float = 10000.0):
     """(dh [N][C], (dW_text, dW_image) [3C][C], (db_text, db_image) [3C]) given the gradients of the rotated
-    q, k and of v ([N][H][D] each)."""
+    q, k and of v ([N][H][D] each).  The output features may also be a subset of heads (w then holds their rows):
+    dW and db of those rows come out exact, dh does not."""
     h = np.asarray(h, dtype=np.float64)
     n, c = h.shape
     dq = np.asarray(dq, dtype=np.float64)
@@ -163,10 +164,12 @@ def qkv_rope_bwd(dq: np.ndarray, dk: np.ndarray, dv: np.ndarray, h: np.ndarray,
     if pos is not None:
         dq = rope_axes(dq, pos, theta, inverse=True)
         dk = rope_axes(dk, pos, theta, inverse=True)
-    g = np.concatenate([dq.reshape(n, c), dk.reshape(n, c), np.asarray(dv, dtype=np.float64).reshape(n, c)], axis=1)
+    g = np.concatenate([dq.reshape(n, -1), dk.reshape(n, -1), np.asarray(dv, dtype=np.float64).reshape(n, -1)],
+                       axis=1)
+    f = g.shape[1]  # 3 C for the block's projection; any width for a slice of its output features
     dh = np.zeros_like(h)
-    dw = [np.zeros((3 * c, c)), np.zeros((3 * c, c))]
-    db = [np.zeros(3 * c), np.zeros(3 * c)]
+    dw = [np.zeros((f, c)), np.zeros((f, c))]
+    db = [np.zeros(f), np.zeros(f)]
     for a, e, s, m in row_groups(cu_pieces, n_samples, frames):
         dh[a:e] = g[a:e] @ np.asarray(w[m], dtype=np.float64)
         dw[m] += g[a:e].T @ h[a:e]

@@ -11,11 +11,13 @@ from ._binding import (  # noqa: F401
     mf_rope3d_apply, mf_rope3d_workspace_size,
     mf_rope2d_apply, mf_rope2d_workspace_size, mf_varlen_attn_bwd, mf_varlen_attn_fwd,
     mf_varlen_attn_workspace_size, status_string, mf_adaln_modulate, mf_block_workspace_size, mf_out_gated_residual,
-    mf_qkv_rope,
+    mf_qkv_rope, mf_adaln_modulate_bwd, mf_adaln_modulate_bwd_workspace_size, mf_out_gated_residual_bwd,
+    mf_out_gated_residual_bwd_workspace_size, mf_qkv_rope_bwd, mf_qkv_rope_bwd_workspace_size,
 )
 from .api import (  # noqa: F401
     PROBE_VECTORS, PackResult, attn_bwd, attn_fwd, cfg_combine, mfma_probe, pack, pack_edit, rf_loss, rf_noise,
-    rope2d_apply, rope3d_apply, adaln_modulate, block_workspace, out_gated_residual, qkv_rope,
+    rope2d_apply, rope3d_apply, adaln_modulate, block_workspace, out_gated_residual, qkv_rope, adaln_modulate_bwd,
+    out_gated_residual_bwd, qkv_rope_bwd,
 )
 
 load_library()

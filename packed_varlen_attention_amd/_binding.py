@@ -31,6 +31,8 @@ EXPORTED = (
     "mf_varlen_attn_bwd", "mf_mfma_probe", "mf_pack_edit", "mf_rope3d_workspace_size", "mf_rope3d_apply",
     "mf_varlen_attn3d_fwd", "mf_varlen_attn3d_bwd", "mf_rf_noise", "mf_rf_loss_workspace_size", "mf_rf_loss",
     "mf_cfg_combine", "mf_block_workspace_size", "mf_adaln_modulate", "mf_qkv_rope", "mf_out_gated_residual",
+    "mf_adaln_modulate_bwd_workspace_size", "mf_adaln_modulate_bwd", "mf_qkv_rope_bwd_workspace_size",
+    "mf_qkv_rope_bwd", "mf_out_gated_residual_bwd_workspace_size", "mf_out_gated_residual_bwd",
 )
 
 
@@ -148,8 +150,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mf_qkv_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _dbl, _i32,
                                 _i32, _i32, _i32, _vp, _sz, _vp, _vp]
     lib.mf_out_gated_residual.restype = _i32
-    lib.mf_out_gated_residual.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp,
+    lib.mf_out_gated_residual.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                          _vp, _sz, _vp, _vp]
+    lib.mf_adaln_modulate_bwd_workspace_size.restype = _sz
+    lib.mf_adaln_modulate_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
+    lib.mf_adaln_modulate_bwd.restype = _i32
+    lib.mf_adaln_modulate_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp,
                                           _sz, _vp, _vp]
+    lib.mf_qkv_rope_bwd_workspace_size.restype = _sz
+    lib.mf_qkv_rope_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+    lib.mf_qkv_rope_bwd.restype = _i32
+    lib.mf_qkv_rope_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32,
+                                    _dbl, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp]
+    lib.mf_out_gated_residual_bwd_workspace_size.restype = _sz
+    lib.mf_out_gated_residual_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
+    lib.mf_out_gated_residual_bwd.restype = _i32
+    lib.mf_out_gated_residual_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                              _i32, _i32, _i32, _vp, _sz, _vp, _vp]
     _lib = lib
     return lib
 
@@ -363,10 +380,61 @@ def mf_qkv_rope(h, w_text, w_image, b_text, b_image, q, k, v, cu_pieces, n_sampl
            "mf_qkv_rope")
 
 
-def mf_out_gated_residual(o, x, w_text, w_image, b_text, b_image, gate, y, cu_pieces, n_samples: int, frames: int,
-                          workspace, stream=None, trace=None) -> None:
+def mf_out_gated_residual(o, x, w_text, w_image, b_text, b_image, gate, y, proj, cu_pieces, n_samples: int,
+                          frames: int, workspace, stream=None, trace=None) -> None:
     n, c = x.shape
     _check(lib().mf_out_gated_residual(_ptr(o), _ptr(x), _ptr(w_text), _ptr(w_image), _ptr(b_text), _ptr(b_image),
-                                       _ptr(gate), _ptr(y), _ptr(cu_pieces), int(n_samples), int(frames), int(n),
-                                       int(c), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
-                                       _stream(stream), _trace(trace)), "mf_out_gated_residual")
+                                       _ptr(gate), _ptr(y), _ptr(proj), _ptr(cu_pieces), int(n_samples), int(frames),
+                                       int(n), int(c), _ptr(workspace),
+                                       int(workspace.numel() * workspace.element_size()), _stream(stream),
+                                       _trace(trace)), "mf_out_gated_residual")
+
+
+def _nbytes(t) -> int:
+    return int(t.numel() * t.element_size())
+
+
+def mf_adaln_modulate_bwd_workspace_size(n_samples: int, frames: int, n_tokens: int, channels: int) -> int:
+    return int(lib().mf_adaln_modulate_bwd_workspace_size(int(n_samples), int(frames), int(n_tokens), int(channels)))
+
+
+def mf_adaln_modulate_bwd(dh, x, scale, dres, dx, dshift, dscale, cu_pieces, n_samples: int, frames: int, eps: float,
+                          workspace, stream=None, trace=None) -> None:
+    n, c = x.shape
+    _check(lib().mf_adaln_modulate_bwd(_ptr(dh), _ptr(x), _ptr(scale), _ptr(dres), _ptr(dx), _ptr(dshift),
+                                       _ptr(dscale), _ptr(cu_pieces), int(n_samples), int(frames), int(n), int(c),
+                                       float(eps), _ptr(workspace), _nbytes(workspace), _stream(stream),
+                                       _trace(trace)), "mf_adaln_modulate_bwd")
+
+
+def mf_qkv_rope_bwd_workspace_size(n_samples: int, frames: int, n_tokens: int, n_heads: int, head_dim: int,
+                                   max_pos: int) -> int:
+    return int(lib().mf_qkv_rope_bwd_workspace_size(int(n_samples), int(frames), int(n_tokens), int(n_heads),
+                                                    int(head_dim), int(max_pos)))
+
+
+def mf_qkv_rope_bwd(dq, dk, dv, h, w_text, w_image, dh, dw_text, dw_image, db_text, db_image, cu_pieces,
+                    n_samples: int, frames: int, pos, theta: float, max_pos: int, workspace, stream=None,
+                    trace=None) -> None:
+    n, heads, d = dq.shape
+    nax = int(pos.shape[-1]) if pos is not None else 2
+    _check(lib().mf_qkv_rope_bwd(_ptr(dq), _ptr(dk), _ptr(dv), _ptr(h), _ptr(w_text), _ptr(w_image), _ptr(dh),
+                                 _ptr(dw_text), _ptr(dw_image), _ptr(db_text), _ptr(db_image), _ptr(cu_pieces),
+                                 int(n_samples), int(frames), _ptr(pos), nax, float(theta), int(max_pos), int(n),
+                                 int(heads), int(d), _ptr(workspace), _nbytes(workspace), _stream(stream),
+                                 _trace(trace)), "mf_qkv_rope_bwd")
+
+
+def mf_out_gated_residual_bwd_workspace_size(n_samples: int, frames: int, n_tokens: int, channels: int) -> int:
+    return int(lib().mf_out_gated_residual_bwd_workspace_size(int(n_samples), int(frames), int(n_tokens),
+                                                              int(channels)))
+
+
+def mf_out_gated_residual_bwd(dy, o, proj, w_text, w_image, gate, d_o, dw_text, dw_image, db_text, db_image, dgate,
+                              cu_pieces, n_samples: int, frames: int, workspace, stream=None, trace=None) -> None:
+    n, c = dy.shape
+    _check(lib().mf_out_gated_residual_bwd(_ptr(dy), _ptr(o), _ptr(proj), _ptr(w_text), _ptr(w_image), _ptr(gate),
+                                           _ptr(d_o), _ptr(dw_text), _ptr(dw_image), _ptr(db_text), _ptr(db_image),
+                                           _ptr(dgate), _ptr(cu_pieces), int(n_samples), int(frames), int(n), int(c),
+                                           _ptr(workspace), _nbytes(workspace), _stream(stream), _trace(trace)),
+           "mf_out_gated_residual_bwd")

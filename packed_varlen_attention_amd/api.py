@@ -207,11 +207,72 @@ def qkv_rope(h: torch.Tensor, w: Tuple[torch.Tensor, torch.Tensor],
 def out_gated_residual(o: torch.Tensor, x: torch.Tensor, w: Tuple[torch.Tensor, torch.Tensor],
                        b: Tuple[Optional[torch.Tensor], Optional[torch.Tensor]], gate: torch.Tensor,
                        cu_pieces: torch.Tensor, n_samples: int, frames: int = 1, out: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, stream=None, trace=None) -> torch.Tensor:
-    """y = x + gate[s][m] (o W_o,m^T + b_o,m); out may be x."""
+                       proj: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                       trace=None) -> torch.Tensor:
+    """y = x + gate[s][m] (o W_o,m^T + b_o,m); out may be x.  proj, if given ([N][C] bf16), receives the
+    pre-gate projection the backward needs."""
     y = torch.empty_like(x) if out is None else out
     if workspace is None:
         workspace = block_workspace(n_samples, frames, 64, 0, x.device)
-    B.mf_out_gated_residual(o, x, w[0], w[1], b[0], b[1], gate, y, cu_pieces, n_samples, frames, workspace, stream,
-                            trace)
+    B.mf_out_gated_residual(o, x, w[0], w[1], b[0], b[1], gate, y, proj, cu_pieces, n_samples, frames, workspace,
+                            stream, trace)
     return y
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    if nbytes == 0:
+        raise B.MFError(B.MF_ERR_UNSUPPORTED, "sizes not supported by the backward")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def adaln_modulate_bwd(dh: torch.Tensor, x: torch.Tensor, scale: torch.Tensor, cu_pieces: torch.Tensor,
+                       n_samples: int, frames: int = 1, eps: float = 1e-6, dres: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None, trace=None):
+    """(dx bf16 [N][C], dshift, dscale float [S][2][C]) for h = LN(x) (1 + scale) + shift; dres, if given, is
+    added to dx."""
+    n, c = x.shape
+    dx = torch.empty_like(x)
+    dshift = torch.empty((n_samples, 2, c), dtype=torch.float32, device=x.device)
+    dscale = torch.empty_like(dshift)
+    if workspace is None:
+        workspace = _workspace(B.mf_adaln_modulate_bwd_workspace_size(n_samples, frames, n, c), x.device)
+    B.mf_adaln_modulate_bwd(dh, x, scale, dres, dx, dshift, dscale, cu_pieces, n_samples, frames, eps, workspace,
+                            stream, trace)
+    return dx, dshift, dscale
+
+
+def qkv_rope_bwd(dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, h: torch.Tensor,
+                 w: Tuple[torch.Tensor, torch.Tensor], cu_pieces: torch.Tensor, n_samples: int, frames: int,
+                 pos: Optional[torch.Tensor], theta: float = 10000.0, max_pos: int = 1, bias: bool = True,
+                 workspace: Optional[torch.Tensor] = None, stream=None, trace=None):
+    """(dh bf16 [N][C], (dW_text, dW_image) float [3C][C], (db_text, db_image) float [3C] or None) given the
+    gradients of the rotated q, k and of v."""
+    n, heads, d = dq.shape
+    c = heads * d
+    dh = torch.empty((n, c), dtype=h.dtype, device=h.device)
+    dw = tuple(torch.empty((3 * c, c), dtype=torch.float32, device=h.device) for _ in range(2))
+    db = tuple(torch.empty(3 * c, dtype=torch.float32, device=h.device) for _ in range(2)) if bias else (None, None)
+    if workspace is None:
+        mp = max_pos if pos is not None else 0
+        workspace = _workspace(B.mf_qkv_rope_bwd_workspace_size(n_samples, frames, n, heads, d, mp), h.device)
+    B.mf_qkv_rope_bwd(dq, dk, dv, h, w[0], w[1], dh, dw[0], dw[1], db[0], db[1], cu_pieces, n_samples, frames, pos,
+                      theta, max_pos, workspace, stream, trace)
+    return dh, dw, db
+
+
+def out_gated_residual_bwd(dy: torch.Tensor, o: torch.Tensor, proj: torch.Tensor,
+                           w: Tuple[torch.Tensor, torch.Tensor], gate: torch.Tensor, cu_pieces: torch.Tensor,
+                           n_samples: int, frames: int = 1, bias: bool = True,
+                           workspace: Optional[torch.Tensor] = None, stream=None, trace=None):
+    """(d_o bf16 [N][C], (dW_text, dW_image) float [C][C], (db_text, db_image) float [C] or None, dgate float
+    [S][2][C]); the gradient with respect to x is dy itself."""
+    n, c = dy.shape
+    d_o = torch.empty_like(dy)
+    dw = tuple(torch.empty((c, c), dtype=torch.float32, device=dy.device) for _ in range(2))
+    db = tuple(torch.empty(c, dtype=torch.float32, device=dy.device) for _ in range(2)) if bias else (None, None)
+    dgate = torch.empty((n_samples, 2, c), dtype=torch.float32, device=dy.device)
+    if workspace is None:
+        workspace = _workspace(B.mf_out_gated_residual_bwd_workspace_size(n_samples, frames, n, c), dy.device)
+    B.mf_out_gated_residual_bwd(dy, o.reshape(n, c), proj, w[0], w[1], gate, d_o, dw[0], dw[1], db[0], db[1], dgate,
+                                cu_pieces, n_samples, frames, workspace, stream, trace)
+    return d_o, dw, db, dgate

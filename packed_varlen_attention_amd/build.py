@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmf.so")
 SOURCES = ["api.hip", "pack.hip", "rope.hip", "sched.hip", "attn_fwd.hip", "attn_bwd.hip", "flow.hip", "block.hip",
-           "probe.hip"]
+           "block_bwd.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

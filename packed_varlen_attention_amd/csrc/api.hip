@@ -604,13 +604,17 @@ size_t block_tiles_bytes(int32_t n_samples, int32_t frames) {
   return align_up((static_cast<size_t>(n_samples) * (frames + 1) + 1) * sizeof(int32_t));
 }
 
-mf_status check_block_common(const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
-                             int32_t channels) {
-  if (cu_pieces == nullptr || n_samples < 0 || n_tokens < 0 || (frames != 1 && frames != 2))
-    return MF_ERR_INVALID_ARG;
+mf_status check_block_sizes(int32_t n_samples, int32_t frames, int32_t n_tokens, int32_t channels) {
+  if (n_samples < 0 || n_tokens < 0 || (frames != 1 && frames != 2)) return MF_ERR_INVALID_ARG;
   if (static_cast<long long>(n_samples) * (frames + 1) >= 0x7fffffffLL) return MF_ERR_INVALID_ARG;
   if (channels < 256 || channels % 256 != 0 || channels > 65535 * 128) return MF_ERR_UNSUPPORTED;
   return MF_OK;
+}
+
+mf_status check_block_common(const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
+                             int32_t channels) {
+  if (cu_pieces == nullptr) return MF_ERR_INVALID_ARG;
+  return check_block_sizes(n_samples, frames, n_tokens, channels);
 }
 
 bool aligned16_or_null(const void* p) { return p == nullptr || aligned16(p); }
@@ -691,7 +695,7 @@ mf_status mf_qkv_rope(const void* h, const void* w_text, const void* w_image, co
 }
 
 mf_status mf_out_gated_residual(const void* o, const void* x, const void* w_text, const void* w_image,
-                                const float* b_text, const float* b_image, const float* gate, void* y,
+                                const float* b_text, const float* b_image, const float* gate, void* y, void* proj,
                                 const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
                                 int32_t channels, void* workspace, size_t workspace_bytes, void* stream,
                                 mf_trace* trace) {
@@ -702,7 +706,7 @@ mf_status mf_out_gated_residual(const void* o, const void* x, const void* w_text
   if (o == nullptr || x == nullptr || y == nullptr || w_text == nullptr || w_image == nullptr)
     return MF_ERR_INVALID_ARG;
   if (!aligned16(o) || !aligned16(x) || !aligned16(y) || !aligned16(w_text) || !aligned16(w_image) ||
-      !aligned16_or_null(b_text) || !aligned16_or_null(b_image))
+      !aligned16_or_null(b_text) || !aligned16_or_null(b_image) || !aligned16_or_null(proj))
     return MF_ERR_INVALID_ARG;
   if (n_samples > 0 && (gate == nullptr || !aligned16(gate))) return MF_ERR_INVALID_ARG;
   const size_t need = mf_block_workspace_size(n_samples, frames, 64, 0);
@@ -716,8 +720,317 @@ mf_status mf_out_gated_residual(const void* o, const void* x, const void* w_text
   if (e != hipSuccess) return MF_ERR_HIP;
   return from_hip(tr.run("out_gated", [&] {
     return mf::launch_out_gated(o, x, w_text, w_image, b_text, b_image, gate, cu_pieces, tstart, n_samples, frames,
-                                n_tokens, channels, y, s);
+                                n_tokens, channels, y, proj, s);
   }));
+}
+
+}  // extern "C"
+
+// Backward of the chains.  Workspace parts in order, each 256-byte aligned.
+
+namespace {
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  }
+};
+
+// Largest token count whose gathered operands keep a row pitch below 2^24 bytes.
+constexpr int32_t kBwdMaxTokens = (1 << 23) - 512;
+// Largest channel count of the projections' backward (transpose grids).
+constexpr int32_t kBwdMaxChannels = 16384;
+
+struct BlockBwdWorkspace {
+  size_t tstart = 0, col0 = 0, kr = 0, stats = 0, part = 0;  // common
+  size_t tab = 0, dqk = 0, u = 0, wt = 0, at = 0, bt = 0, bpart = 0, split = 0;
+  long long pitch = 0;
+  int splits = 1;
+  size_t total = 0;
+};
+
+// kind 0: adaln; 1: qkv projection (rotation when max_pos > 0); 2: output projection.
+BlockBwdWorkspace block_bwd_layout(int kind, int32_t n_samples, int32_t frames, int32_t n_tokens, int32_t channels,
+                                   int32_t head_dim, int32_t max_pos) {
+  BlockBwdWorkspace w;
+  Carve c;
+  const size_t n_pieces = static_cast<size_t>(n_samples) * (frames + 1);
+  const size_t n = static_cast<size_t>(n_tokens), ch = static_cast<size_t>(channels);
+  const size_t sub_rows = 4 * static_cast<size_t>(mf::block_mtiles_bound(n_tokens, static_cast<int>(n_pieces)));
+  w.tstart = c.take((n_pieces + 1) * sizeof(int32_t));
+  if (kind == 0) {
+    w.stats = c.take(n * 2 * sizeof(float));
+    w.part = c.take(sub_rows * 2 * ch * sizeof(float));
+    w.total = c.off;
+    return w;
+  }
+  const size_t out_rows = kind == 1 ? 3 * ch : ch;  // gradient features of the projection's output
+  w.pitch = mf::block_bwd_cols(n_tokens);
+  w.splits = mf::block_bwd_splits(n_tokens, static_cast<int>(out_rows), channels);
+  w.col0 = c.take((n_pieces + 2) * sizeof(int32_t));
+  w.kr = c.take(2 * sizeof(int32_t));
+  if (kind == 1 && max_pos > 0) {
+    w.tab = c.take(static_cast<size_t>(max_pos) * mf::rope_table_width(head_dim, 3) * sizeof(float2));
+    w.dqk = c.take(2 * n * ch * 2);
+  }
+  if (kind == 2) {
+    w.u = c.take(n * ch * 2);
+    w.part = c.take(sub_rows * ch * sizeof(float));
+  }
+  w.wt = c.take(2 * out_rows * ch * 2);
+  w.at = c.take(out_rows * static_cast<size_t>(w.pitch) * 2);
+  w.bt = c.take(ch * static_cast<size_t>(w.pitch) * 2);
+  w.bpart = c.take(static_cast<size_t>(w.pitch / 64) * out_rows * sizeof(float));
+  if (w.splits > 1) w.split = c.take(static_cast<size_t>(w.splits) * 2 * out_rows * ch * sizeof(float));
+  w.total = c.off;
+  return w;
+}
+
+mf_status check_workspace(const void* workspace, size_t workspace_bytes, size_t need) {
+  if (workspace_bytes < need) return MF_ERR_WORKSPACE;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
+  return MF_OK;
+}
+
+bool aligned4_or_null(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t mf_adaln_modulate_bwd_workspace_size(int32_t n_samples, int32_t frames, int32_t n_tokens, int32_t channels) {
+  if (check_block_sizes(n_samples, frames, n_tokens, channels) != MF_OK) return 0;
+  if (channels % 512 != 0 || channels > mf::kAdaBwdMaxC) return 0;
+  return block_bwd_layout(0, n_samples, frames, n_tokens, channels, 64, 0).total;
+}
+
+size_t mf_qkv_rope_bwd_workspace_size(int32_t n_samples, int32_t frames, int32_t n_tokens, int32_t n_heads,
+                                      int32_t head_dim, int32_t max_pos) {
+  if ((head_dim != 64 && head_dim != 128) || n_heads < 1 || n_heads > 65535 || n_tokens > kBwdMaxTokens) return 0;
+  if (n_heads * head_dim > kBwdMaxChannels) return 0;
+  if (check_block_sizes(n_samples, frames, n_tokens, n_heads * head_dim) != MF_OK) return 0;
+  return block_bwd_layout(1, n_samples, frames, n_tokens, n_heads * head_dim, head_dim, max_pos > 0 ? max_pos : 0)
+      .total;
+}
+
+size_t mf_out_gated_residual_bwd_workspace_size(int32_t n_samples, int32_t frames, int32_t n_tokens,
+                                                int32_t channels) {
+  if (n_tokens > kBwdMaxTokens || channels > kBwdMaxChannels) return 0;
+  if (check_block_sizes(n_samples, frames, n_tokens, channels) != MF_OK) return 0;
+  return block_bwd_layout(2, n_samples, frames, n_tokens, channels, 64, 0).total;
+}
+
+mf_status mf_adaln_modulate_bwd(const void* dh, const void* x, const float* scale, const void* dres, void* dx,
+                                float* dshift, float* dscale, const int32_t* cu_pieces, int32_t n_samples,
+                                int32_t frames, int32_t n_tokens, int32_t channels, float eps, void* workspace,
+                                size_t workspace_bytes, void* stream, mf_trace* trace) {
+  mf_status st = check_block_common(cu_pieces, n_samples, frames, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (channels % 512 != 0 || channels > mf::kAdaBwdMaxC) return MF_ERR_UNSUPPORTED;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (!(eps > 0.0f) || isinf(eps)) return MF_ERR_INVALID_ARG;
+  if (n_samples > 0 && (scale == nullptr || dshift == nullptr || dscale == nullptr || !aligned16(scale) ||
+                        !aligned16(dshift) || !aligned16(dscale)))
+    return MF_ERR_INVALID_ARG;
+  if (n_tokens > 0 && (dh == nullptr || x == nullptr || dx == nullptr || !aligned16(dh) || !aligned16(x) ||
+                       !aligned16(dx) || !aligned16_or_null(dres)))
+    return MF_ERR_INVALID_ARG;
+  const BlockBwdWorkspace w = block_bwd_layout(0, n_samples, frames, n_tokens, channels, 64, 0);
+  if ((st = check_workspace(workspace, workspace_bytes, w.total)) != MF_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int* tstart = reinterpret_cast<int*>(ws + w.tstart);
+  float* part = reinterpret_cast<float*>(ws + w.part);
+  const int n_pieces = (frames + 1) * n_samples;
+  Tracer tr(trace, s);
+  hipError_t e = tr.run("piece_tiles", [&] { return mf::launch_piece_tiles(cu_pieces, n_pieces, n_tokens, tstart, s); });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  e = tr.run("adaln_bwd", [&] {
+    return mf::launch_adaln_bwd(dh, x, scale, dres, cu_pieces, tstart, n_samples, frames, n_tokens, channels, eps, dx,
+                                reinterpret_cast<float2*>(ws + w.stats), part, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  const long long stride = 2LL * channels;
+  e = tr.run("group_sum", [&] {
+    hipError_t r = mf::launch_group_sum(part, stride, 0, channels, tstart, n_samples, frames, n_tokens, dshift, s);
+    if (r != hipSuccess) return r;
+    return mf::launch_group_sum(part, stride, channels, channels, tstart, n_samples, frames, n_tokens, dscale, s);
+  });
+  return from_hip(e);
+}
+
+mf_status mf_qkv_rope_bwd(const void* dq, const void* dk, const void* dv, const void* h, const void* w_text,
+                          const void* w_image, void* dh, float* dw_text, float* dw_image, float* db_text,
+                          float* db_image, const int32_t* cu_pieces, int32_t n_samples, int32_t frames,
+                          const int32_t* pos, int32_t nax, double theta, int32_t max_pos, int32_t n_tokens,
+                          int32_t n_heads, int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream,
+                          mf_trace* trace) {
+  if (head_dim != 64 && head_dim != 128) return MF_ERR_UNSUPPORTED;
+  if (n_heads < 1 || n_heads > 65535) return MF_ERR_INVALID_ARG;
+  const int32_t channels = n_heads * head_dim;
+  mf_status st = check_block_common(cu_pieces, n_samples, frames, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (n_tokens > kBwdMaxTokens || channels > kBwdMaxChannels) return MF_ERR_UNSUPPORTED;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (pos != nullptr) {
+    if (nax != 2 && nax != 3) return MF_ERR_INVALID_ARG;
+    if (max_pos < 1 || !(theta > 0.0) || isinf(theta)) return MF_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(pos) & (nax == 2 ? 7u : 3u)) != 0) return MF_ERR_INVALID_ARG;
+  }
+  if (w_text == nullptr || w_image == nullptr || dw_text == nullptr || dw_image == nullptr || !aligned16(w_text) ||
+      !aligned16(w_image) || !aligned16(dw_text) || !aligned16(dw_image) || !aligned4_or_null(db_text) ||
+      !aligned4_or_null(db_image))
+    return MF_ERR_INVALID_ARG;
+  if (n_tokens > 0 && (dq == nullptr || dk == nullptr || dv == nullptr || h == nullptr || dh == nullptr ||
+                       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(h) || !aligned16(dh)))
+    return MF_ERR_INVALID_ARG;
+  const BlockBwdWorkspace w =
+      block_bwd_layout(1, n_samples, frames, n_tokens, channels, head_dim, pos != nullptr ? max_pos : 0);
+  if ((st = check_workspace(workspace, workspace_bytes, w.total)) != MF_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int* tstart = reinterpret_cast<int*>(ws + w.tstart);
+  int* col0 = reinterpret_cast<int*>(ws + w.col0);
+  int* kr = reinterpret_cast<int*>(ws + w.kr);
+  const int n_pieces = (frames + 1) * n_samples;
+  const size_t nc = static_cast<size_t>(n_tokens) * channels;
+  Tracer tr(trace, s);
+  hipError_t e = tr.run("piece_tiles", [&] { return mf::launch_piece_tiles(cu_pieces, n_pieces, n_tokens, tstart, s); });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  e = tr.run("modality_cols",
+             [&] { return mf::launch_modality_cols(cu_pieces, n_samples, frames, n_tokens, col0, kr, s); });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  const void* g[3] = {dq, dk, dv};
+  if (pos != nullptr && n_tokens > 0) {
+    // gradients with respect to the un-rotated projections: the inverse rotation
+    float2* tab = reinterpret_cast<float2*>(ws + w.tab);
+    uint16_t* dqk = reinterpret_cast<uint16_t*>(ws + w.dqk);
+    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, nax, theta, s); });
+    if (e != hipSuccess) return MF_ERR_HIP;
+    e = tr.run("rope_inverse", [&] {
+      hipError_t r = mf::launch_rope_apply(dq, mf::kDtypeBf16, dqk, mf::kDtypeBf16, pos, nax, tab, max_pos, n_tokens,
+                                           n_heads, head_dim, true, true, s);
+      if (r != hipSuccess) return r;
+      return mf::launch_rope_apply(dk, mf::kDtypeBf16, dqk + nc, mf::kDtypeBf16, pos, nax, tab, max_pos, n_tokens,
+                                   n_heads, head_dim, true, true, s);
+    });
+    if (e != hipSuccess) return MF_ERR_HIP;
+    g[0] = dqk;
+    g[1] = dqk + nc;
+  }
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + w.wt);
+  const size_t wsz = static_cast<size_t>(3) * channels * channels;
+  e = tr.run("transpose_w", [&] {
+    hipError_t r = mf::launch_transpose(w_text, 3 * channels, channels, wt, s);
+    if (r != hipSuccess) return r;
+    return mf::launch_transpose(w_image, 3 * channels, channels, wt + wsz, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  if (n_tokens > 0) {
+    e = tr.run("dgrad", [&] {
+      return mf::launch_dgrad(g, 3, channels, wt, wt + wsz, cu_pieces, tstart, n_samples, frames, n_tokens, channels,
+                              dh, s);
+    });
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
+  float* bpart = reinterpret_cast<float*>(ws + w.bpart);
+  e = tr.run("gather_t", [&] {
+    hipError_t r = mf::launch_gather_t(g, 3, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.at,
+                                       w.pitch, bpart, s);
+    if (r != hipSuccess) return r;
+    const void* hs[1] = {h};
+    return mf::launch_gather_t(hs, 1, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.bt, w.pitch,
+                               nullptr, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  e = tr.run("wgrad", [&] {
+    return mf::launch_wgrad(ws + w.at, ws + w.bt, w.pitch, 3 * channels, channels, kr, w.splits,
+                            reinterpret_cast<float*>(ws + w.split), dw_text, dw_image, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  return from_hip(tr.run("bias_sum", [&] { return mf::launch_bias_sum(bpart, 3 * channels, kr, w.pitch, db_text, db_image, s); }));
+}
+
+mf_status mf_out_gated_residual_bwd(const void* dy, const void* o, const void* proj, const void* w_text,
+                                    const void* w_image, const float* gate, void* d_o, float* dw_text,
+                                    float* dw_image, float* db_text, float* db_image, float* dgate,
+                                    const int32_t* cu_pieces, int32_t n_samples, int32_t frames, int32_t n_tokens,
+                                    int32_t channels, void* workspace, size_t workspace_bytes, void* stream,
+                                    mf_trace* trace) {
+  mf_status st = check_block_common(cu_pieces, n_samples, frames, n_tokens, channels);
+  if (st != MF_OK) return st;
+  if (n_tokens > kBwdMaxTokens || channels > kBwdMaxChannels) return MF_ERR_UNSUPPORTED;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (w_text == nullptr || w_image == nullptr || dw_text == nullptr || dw_image == nullptr || !aligned16(w_text) ||
+      !aligned16(w_image) || !aligned16(dw_text) || !aligned16(dw_image) || !aligned4_or_null(db_text) ||
+      !aligned4_or_null(db_image))
+    return MF_ERR_INVALID_ARG;
+  if (n_samples > 0 && (gate == nullptr || dgate == nullptr || !aligned16(gate) || !aligned16(dgate)))
+    return MF_ERR_INVALID_ARG;
+  if (n_tokens > 0 && (dy == nullptr || o == nullptr || proj == nullptr || d_o == nullptr || !aligned16(dy) ||
+                       !aligned16(o) || !aligned16(proj) || !aligned16(d_o)))
+    return MF_ERR_INVALID_ARG;
+  const BlockBwdWorkspace w = block_bwd_layout(2, n_samples, frames, n_tokens, channels, 64, 0);
+  if ((st = check_workspace(workspace, workspace_bytes, w.total)) != MF_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int* tstart = reinterpret_cast<int*>(ws + w.tstart);
+  int* col0 = reinterpret_cast<int*>(ws + w.col0);
+  int* kr = reinterpret_cast<int*>(ws + w.kr);
+  void* u = ws + w.u;
+  float* gpart = reinterpret_cast<float*>(ws + w.part);
+  const int n_pieces = (frames + 1) * n_samples;
+  Tracer tr(trace, s);
+  hipError_t e = tr.run("piece_tiles", [&] { return mf::launch_piece_tiles(cu_pieces, n_pieces, n_tokens, tstart, s); });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  e = tr.run("modality_cols",
+             [&] { return mf::launch_modality_cols(cu_pieces, n_samples, frames, n_tokens, col0, kr, s); });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  if (n_tokens > 0) {
+    e = tr.run("gate_bwd", [&] {
+      return mf::launch_gate_bwd(dy, proj, gate, cu_pieces, tstart, n_samples, frames, n_tokens, channels, u, gpart,
+                                 s);
+    });
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
+  e = tr.run("group_sum",
+             [&] { return mf::launch_group_sum(gpart, channels, 0, channels, tstart, n_samples, frames, n_tokens, dgate, s); });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + w.wt);
+  const size_t wsz = static_cast<size_t>(channels) * channels;
+  e = tr.run("transpose_w", [&] {
+    hipError_t r = mf::launch_transpose(w_text, channels, channels, wt, s);
+    if (r != hipSuccess) return r;
+    return mf::launch_transpose(w_image, channels, channels, wt + wsz, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  const void* us[1] = {u};
+  if (n_tokens > 0) {
+    e = tr.run("dgrad", [&] {
+      return mf::launch_dgrad(us, 1, channels, wt, wt + wsz, cu_pieces, tstart, n_samples, frames, n_tokens, channels,
+                              d_o, s);
+    });
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
+  float* bpart = reinterpret_cast<float*>(ws + w.bpart);
+  e = tr.run("gather_t", [&] {
+    hipError_t r = mf::launch_gather_t(us, 1, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.at,
+                                       w.pitch, bpart, s);
+    if (r != hipSuccess) return r;
+    const void* os[1] = {o};
+    return mf::launch_gather_t(os, 1, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.bt, w.pitch,
+                               nullptr, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  e = tr.run("wgrad", [&] {
+    return mf::launch_wgrad(ws + w.at, ws + w.bt, w.pitch, channels, channels, kr, w.splits,
+                            reinterpret_cast<float*>(ws + w.split), dw_text, dw_image, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  return from_hip(tr.run("bias_sum", [&] { return mf::launch_bias_sum(bpart, channels, kr, w.pitch, db_text, db_image, s); }));
 }
 
 }  // extern "C"

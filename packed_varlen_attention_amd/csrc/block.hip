@@ -21,27 +21,13 @@
 //   out:    y = x + gate[s][m] (o W_o,m^T + b_o,m).
 // The projections tile the token rows per piece, so a tile never mixes
 // modalities and takes one weight matrix.
+#include "block_gemm.h"
 #include "mf_device.h"
 #include "mf_kernels.h"
 
 namespace mf {
 
 namespace {
-
-constexpr int kPT = 256;     // token rows per projection tile
-constexpr int kFT = 256;     // output features per projection tile
-constexpr int kKS = 32;      // reduction slice per pipeline step (one 64-byte LDS row)
-constexpr int kStages = 4;   // LDS stages; copies run three steps ahead
-constexpr int kPWaves = 8;   // 4 x 2 waves, each 64 tokens x 128 features
-constexpr int kXcds = 8;     // workgroups are dealt round-robin to the XCDs
-
-// Rows of piece i, clamped to [0, n_tokens] (cu_pieces is device data the
-// host cannot check; a malformed one yields empty pieces, never a read past
-// the tensors).
-__device__ __forceinline__ void piece_rows(const int* __restrict__ cp, int i, int n_tokens, int& a, int& e) {
-  a = min(max(cp[i], 0), n_tokens);
-  e = min(max(cp[i + 1], a), n_tokens);
-}
 
 // tstart[p] = sum over pieces q < p of ceil(len_q / kPT); tstart[m] = total.
 __global__ __launch_bounds__(1024) void piece_tiles_kernel(const int* __restrict__ cp, int m, int n_tokens,
@@ -215,14 +201,10 @@ struct ProjArgs {
   const uint16_t* x;
   const float* gate;  // [S][2][n_out]
   uint16_t* y;
+  uint16_t* proj;  // o W^T + b before the gate, for the backward; or nullptr
 };
 
 enum { kEpiQkvRope = 0, kEpiGatedResidual = 1 };
-
-// Feature tiles per scheduling window: 4 when they divide the tile count.
-__host__ __device__ __forceinline__ int window_cols(int n_ntiles) {
-  return n_ntiles % 4 == 0 ? 4 : n_ntiles % 2 == 0 ? 2 : 1;
-}
 
 // out = act W^T (+ b) over one 256-token x 256-feature tile.  MFMA A operand
 // = weight rows (features), B operand = token rows, so the accumulator holds
@@ -231,38 +213,12 @@ __host__ __device__ __forceinline__ int window_cols(int n_ntiles) {
 // consecutive features per lane group, the rotary pairs inside one lane.
 template <int D, int kEpi>
 __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
-  constexpr int kTileBytes = 256 * kKS * 2;  // 256 rows of 64 bytes
-  // Four stages of a token tile and a weight tile, as separate objects so
-  // the compiler can tell the stage being read from stages being filled.
-  __shared__ __attribute__((aligned(16))) char smemA0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char smemA1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char smemA2[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char smemA3[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char smemB0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char smemB1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char smemB2[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char smemB3[kTileBytes];
-
-  // Workgroups are dealt to the XCDs round-robin, so blocks b, b + 8, b + 16,
-  // ... run together on one XCD.  Each run of 32 such blocks is a window of
-  // (32 / nw) token tiles x nw feature tiles: the XCD's L2 then serves 12
-  // distinct tiles (8 + 4 with nw = 4) to 32 workgroups, not 33 with one
-  // token tile and 32 feature tiles.
   const int b = blockIdx.x;
-  const int nw = window_cols(a.n_ntiles), mw = 32 / nw;
-  const int x = b % kXcds, r = b / kXcds;
-  const int win = (r / 32) * kXcds + x, p = r % 32;
-  const int n_ntg = a.n_ntiles / nw;
-  const int nt = (win % n_ntg) * nw + p / mw;
-  const int mt = (win / n_ntg) * mw + p % mw;
+  int mt, nt;
+  window_tile(b, a.n_ntiles, mt, nt);
   const int total = a.tstart[a.n_pieces];
   if (mt >= total) return;
-  int lo = 0, hi = a.n_pieces;  // piece p: tstart[p] <= mt < tstart[p + 1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.tstart[mid] <= mt) lo = mid; else hi = mid;
-  }
-  const int piece = lo;
+  const int piece = piece_of_tile(a.tstart, a.n_pieces, mt);
   int pa, mend;
   piece_rows(a.cp, piece, a.n_tokens, pa, mend);
   const int m0 = pa + (mt - a.tstart[piece]) * kPT;
@@ -276,80 +232,19 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5;
+  const int r32 = lane & 31;
   const int wm = wave >> 1;  // token rows 64 wm .. + 64
   const int wn = wave & 1;   // features 128 wn .. + 128
 
-  using Copy = TileCopy<kKS, 256, kPWaves>;
-  constexpr int kCopiesPerStage = 2 * Copy::kCopies;  // token and weight tile, per wave
-  const Copy copy(wave, lane, static_cast<unsigned>(a.k) * 2u);
-  lds_char* const sA[kStages] = {(lds_char*)smemA0, (lds_char*)smemA1, (lds_char*)smemA2, (lds_char*)smemA3};
-  lds_char* const sB[kStages] = {(lds_char*)smemB0, (lds_char*)smemB1, (lds_char*)smemB2, (lds_char*)smemB3};
-  const int nsteps = a.k / kKS;  // a multiple of 8 (k is a multiple of 256)
-  // Stage ks lives in buffer ks % 4.  Every step issues the copies of stage
-  // ks + 3 (past the end: the last slice again, into a buffer no later step
-  // reads), so the wait for stage ks + 1 keeps a fixed count in flight.
-  auto load_stage = [&](int ks, int buf) {
-    ks = min(ks, nsteps - 1);
-    copy(a.act + ks * kKS, m0, mend, sA[buf]);
-    copy(w + ks * kKS, n0, a.n_out, sB[buf]);
+  const TileCopy256 copy(wave, lane, static_cast<unsigned>(a.k) * 2u);
+  auto load = [&](int ks, lds_char* tA, lds_char* tB) {
+    copy(a.act + ks * kKS, m0, mend, tA);
+    copy(w + ks * kKS, n0, a.n_out, tB);
   };
-
-  // Row fragments: the chunk swizzle of Tile<32> depends on (row / 2) % 4,
-  // the same for every 32-row block, so one offset per reduction step kk.
-  const int r32 = lane & 31;
-  int off[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) off[kk] = Tile<kKS>::off(r32, 2 * kk + hh);
-  auto frag = [&](const lds_char* t, int row0, int kk) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(t + off[kk] + row0 * (kKS * 2));
-  };
-
   f32x16 acc[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-
-  auto step = [&](int ks, auto buf_tag) {
-    constexpr int bf = decltype(buf_tag)::value;
-    load_stage(ks + 3, (bf + 3) % kStages);
-    const lds_char* A = sA[bf];
-    const lds_char* B = sB[bf];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 tf[2], wf[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) tf[mb] = frag(A, 64 * wm + 32 * mb, kk);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) wf[nb] = frag(B, 128 * wn + 32 * nb, kk);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma32(wf[nb], tf[mb], acc[mb][nb]);
-    }
-    // Stage ks + 1 has landed once only the two newest stages' copies are
-    // outstanding (copies complete in issue order).
-    wait_vmem_keep<2 * kCopiesPerStage>();
-    barrier_keep_loads();
-  };
-  load_stage(0, 0);
-  load_stage(1, 1);
-  load_stage(2, 2);
-  wait_vmem_keep<2 * kCopiesPerStage>();
-  barrier_keep_loads();
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
-  using B3 = std::integral_constant<int, 3>;
-  for (int ks = 0; ks < nsteps; ks += 4) {
-    step(ks, B0{});
-    step(ks + 1, B1{});
-    step(ks + 2, B2{});
-    step(ks + 3, B3{});
-  }
-  wait_vmem();  // the trailing copies land before the workgroup's LDS is released
+  zero_acc(acc);
+  // k is a multiple of 256, so the slice count a multiple of 8
+  tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc);
 
   // ---- epilogue
   const int C = a.n_out / (kEpi == kEpiQkvRope ? 3 : 1);
@@ -383,6 +278,8 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
           r[2] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] & 0xffffu));
           r[3] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] >> 16));
           const float4 gv = *reinterpret_cast<const float4*>(gate + c);
+          if (a.proj != nullptr)
+            store4<uint16_t>(a.proj + static_cast<size_t>(tok) * C + c, xv[0], xv[1], xv[2], xv[3]);
           xv[0] = r[0] + gv.x * xv[0];
           xv[1] = r[1] + gv.y * xv[1];
           xv[2] = r[2] + gv.z * xv[2];
@@ -395,18 +292,16 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
 
 template <int D, int kEpi>
 hipError_t launch_proj_t(const ProjArgs& a, int mtiles_max, hipStream_t stream) {
-  const int nw = window_cols(a.n_ntiles), mw = 32 / nw;
-  const long long wins = static_cast<long long>((mtiles_max + mw - 1) / mw) * (a.n_ntiles / nw);
-  const long long blocks = (wins + kXcds - 1) / kXcds * kXcds * 32;
+  const long long blocks = window_blocks(mtiles_max, a.n_ntiles);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((proj_kernel<D, kEpi>), dim3(static_cast<unsigned>(blocks)), dim3(kPWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
-int mtiles_bound(int n_tokens, int n_pieces) { return (n_tokens + kPT - 1) / kPT + n_pieces; }
-
 }  // namespace
+
+int block_mtiles_bound(int n_tokens, int n_pieces) { return (n_tokens + kPT - 1) / kPT + n_pieces; }
 
 int block_tile_rows() { return kPT; }
 
@@ -463,7 +358,7 @@ hipError_t launch_qkv_rope(const void* h, const void* w_text, const void* w_imag
   a.nax = nax;
   a.tab = tab;
   a.max_pos = max_pos;
-  const int mt = mtiles_bound(n_tokens, a.n_pieces);
+  const int mt = block_mtiles_bound(n_tokens, a.n_pieces);
   return head_dim == 128 ? launch_proj_t<128, kEpiQkvRope>(a, mt, stream)
                          : launch_proj_t<64, kEpiQkvRope>(a, mt, stream);
 }
@@ -471,7 +366,7 @@ hipError_t launch_qkv_rope(const void* h, const void* w_text, const void* w_imag
 hipError_t launch_out_gated(const void* o, const void* x, const void* w_text, const void* w_image,
                             const float* b_text, const float* b_image, const float* gate, const int* cu_pieces,
                             const int* tstart, int n_samples, int frames, int n_tokens, int channels, void* y,
-                            hipStream_t stream) {
+                            void* proj, hipStream_t stream) {
   ProjArgs a = {};
   a.act = static_cast<const uint16_t*>(o);
   a.w0 = static_cast<const uint16_t*>(w_text);
@@ -489,7 +384,8 @@ hipError_t launch_out_gated(const void* o, const void* x, const void* w_text, co
   a.x = static_cast<const uint16_t*>(x);
   a.gate = gate;
   a.y = static_cast<uint16_t*>(y);
-  return launch_proj_t<128, kEpiGatedResidual>(a, mtiles_bound(n_tokens, a.n_pieces), stream);
+  a.proj = static_cast<uint16_t*>(proj);
+  return launch_proj_t<128, kEpiGatedResidual>(a, block_mtiles_bound(n_tokens, a.n_pieces), stream);
 }
 
 }  // namespace mf

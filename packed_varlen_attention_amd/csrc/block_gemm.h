@@ -1,0 +1,160 @@
+// The 256 x 256 tile matrix product shared by the attention sub-block's
+// projections (forward and backward), and the row tiling of the packed
+// stream by pieces.
+//
+// Rows are tokens in packed order; cu_pieces splits them into pieces of
+// frames + 1 per sample (the first piece of a sample is its text, the others
+// image grids).  A projection tiles each piece's rows separately, so a tile
+// never mixes modalities and takes one weight matrix.
+#pragma once
+
+#include "mf_device.h"
+
+namespace mf {
+namespace {
+
+constexpr int kPT = 256;     // token rows per projection tile
+constexpr int kFT = 256;     // output features per projection tile
+constexpr int kKS = 32;      // reduction slice per pipeline step (one 64-byte LDS row)
+constexpr int kStages = 4;   // LDS stages; copies run three steps ahead
+constexpr int kPWaves = 8;   // 4 x 2 waves, each 64 tokens x 128 features
+constexpr int kXcds = 8;     // workgroups are dealt round-robin to the XCDs
+
+using TileCopy256 = TileCopy<kKS, 256, kPWaves>;
+
+// Rows of piece i, clamped to [0, n_tokens] (cu_pieces is device data the
+// host cannot check; a malformed one yields empty pieces, never a read past
+// the tensors).
+__device__ __forceinline__ void piece_rows(const int* __restrict__ cp, int i, int n_tokens, int& a, int& e) {
+  a = min(max(cp[i], 0), n_tokens);
+  e = min(max(cp[i + 1], a), n_tokens);
+}
+
+// Index p with tstart[p] <= t < tstart[p + 1] among the m pieces (tstart is
+// non-decreasing and t < tstart[m]).
+__device__ __forceinline__ int piece_of_tile(const int* __restrict__ tstart, int m, int t) {
+  int lo = 0, hi = m;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tstart[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Feature tiles per scheduling window: 4 when they divide the tile count.
+__host__ __device__ __forceinline__ int window_cols(int n_ntiles) {
+  return n_ntiles % 4 == 0 ? 4 : n_ntiles % 2 == 0 ? 2 : 1;
+}
+
+// Workgroups are dealt to the XCDs round-robin, so blocks b, b + 8, b + 16,
+// ... run together on one XCD.  Each run of 32 such blocks is a window of
+// (32 / nw) row tiles x nw feature tiles: the XCD's L2 then serves 12
+// distinct operand tiles (8 + 4 with nw = 4) to 32 workgroups, not 33 with
+// one row tile and 32 feature tiles.
+__device__ __forceinline__ void window_tile(int b, int n_ntiles, int& mt, int& nt) {
+  const int nw = window_cols(n_ntiles), mw = 32 / nw;
+  const int x = b % kXcds, r = b / kXcds;
+  const int win = (r / 32) * kXcds + x, p = r % 32;
+  const int n_ntg = n_ntiles / nw;
+  nt = (win % n_ntg) * nw + p / mw;
+  mt = (win / n_ntg) * mw + p % mw;
+}
+
+// Blocks of a window grid covering mtiles x n_ntiles tiles (a multiple of
+// 8 x 32, so the XCD of a block is the same in every such grid).
+__host__ inline long long window_blocks(int mtiles, int n_ntiles) {
+  const int nw = window_cols(n_ntiles), mw = 32 / nw;
+  const long long wins = static_cast<long long>((mtiles + mw - 1) / mw) * (n_ntiles / nw);
+  return (wins + kXcds - 1) / kXcds * kXcds * 32;
+}
+
+// acc += the product of one 256-row tile R (the MFMA B operand, "token"
+// rows) and one 256-row tile W (the A operand, "feature" rows) over nsteps
+// 32-wide reduction slices (nsteps a positive multiple of 4).
+// load(ks, r_tile, w_tile) issues this wave's copies of slice ks of both
+// tiles, kCopies in all.  The accumulator holds the transposed tile: lane
+// element e of block (mb, nb) is feature 128 wn + 32 nb + 8 (e/4) + 4 (lane/32)
+// + e%4 of row 64 wm + 32 mb + lane%32 -- four consecutive features per lane.
+template <int kCopies, class Load>
+__device__ __forceinline__ void tile_gemm(int nsteps, int wm, int wn, int lane, const Load& load,
+                                          f32x16 (&acc)[2][4]) {
+  constexpr int kTileBytes = 256 * kKS * 2;  // 256 rows of 64 bytes
+  // Four stages of a row tile and a feature tile, as separate objects so the
+  // compiler can tell the stage being read from stages being filled.
+  __shared__ __attribute__((aligned(16))) char smemA0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemA1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemA2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemA3[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemB0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemB1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemB2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smemB3[kTileBytes];
+  lds_char* const sA[kStages] = {(lds_char*)smemA0, (lds_char*)smemA1, (lds_char*)smemA2, (lds_char*)smemA3};
+  lds_char* const sB[kStages] = {(lds_char*)smemB0, (lds_char*)smemB1, (lds_char*)smemB2, (lds_char*)smemB3};
+  const int hh = lane >> 5;
+  // Stage ks lives in buffer ks % 4.  Every step issues the copies of stage
+  // ks + 3 (past the end: the last slice again, into a buffer no later step
+  // reads), so the wait for stage ks + 1 keeps a fixed count in flight.
+  auto load_stage = [&](int ks, int buf) { load(min(ks, nsteps - 1), sA[buf], sB[buf]); };
+
+  // Row fragments: the chunk swizzle of Tile<32> depends on (row / 2) % 4,
+  // the same for every 32-row block, so one offset per reduction step kk.
+  const int r32 = lane & 31;
+  int off[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) off[kk] = Tile<kKS>::off(r32, 2 * kk + hh);
+  auto frag = [&](const lds_char* t, int row0, int kk) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(t + off[kk] + row0 * (kKS * 2));
+  };
+
+  auto step = [&](int ks, auto buf_tag) {
+    constexpr int bf = decltype(buf_tag)::value;
+    load_stage(ks + 3, (bf + 3) % kStages);
+    const lds_char* A = sA[bf];
+    const lds_char* B = sB[bf];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 tf[2], wf[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) tf[mb] = frag(A, 64 * wm + 32 * mb, kk);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) wf[nb] = frag(B, 128 * wn + 32 * nb, kk);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma32(wf[nb], tf[mb], acc[mb][nb]);
+    }
+    // Stage ks + 1 has landed once only the two newest stages' copies are
+    // outstanding (copies complete in issue order).
+    wait_vmem_keep<2 * kCopies>();
+    barrier_keep_loads();
+  };
+  load_stage(0, 0);
+  load_stage(1, 1);
+  load_stage(2, 2);
+  wait_vmem_keep<2 * kCopies>();
+  barrier_keep_loads();
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  for (int ks = 0; ks < nsteps; ks += 4) {
+    step(ks, B0{});
+    step(ks + 1, B1{});
+    step(ks + 2, B2{});
+    step(ks + 3, B3{});
+  }
+  wait_vmem();  // the trailing copies land before the workgroup's LDS is released
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][4]) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+}
+
+}  // namespace
+}  // namespace mf

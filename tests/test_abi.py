@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     import packed_varlen_attention_amd as m
-    assert m.abi_version() == 3
+    assert m.abi_version() == 4
     for code in (0, -1, -2, -3, -4):
         assert len(m.status_string(code)) > 0
     assert m.status_string(7) == "unknown status"
@@ -238,13 +238,101 @@ def test_block_argument_errors(lib):
     assert qkv(wsb=ws - 1) == -3
     assert qkv(ws=FAKE + 16) == -1
     assert qkv(n=0, h=None, q=None) == 0        # empty: nothing to launch
-    # mf_out_gated_residual(o, x, wt, wi, bt, bi, gate, y, cu, n_samples, frames, n, C, ws, wsb, stream, trace)
+    # mf_out_gated_residual(o, x, wt, wi, bt, bi, gate, y, proj, cu, n_samples, frames, n, C, ws, wsb, stream, trace)
     wso = lib.mf_block_workspace_size(2, 1, 64, 0)
-    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 2, 1, 8, 3000, FAKE, wso,
-                                     None, None) == -2
-    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, 2, 1, 8, 3072, FAKE, wso,
-                                     None, None) == -1  # gate
-    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 2, 1, 8, 3072, FAKE, 4,
-                                     None, None) == -3
-    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE + 2, FAKE, 2, 1, 8, 3072, FAKE,
-                                     wso, None, None) == -1
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, 2, 1, 8, 3000, FAKE,
+                                     wso, None, None) == -2
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, FAKE, 2, 1, 8, 3072, FAKE,
+                                     wso, None, None) == -1  # gate
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, 2, 1, 8, 3072, FAKE,
+                                     4, None, None) == -3
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE + 2, None, FAKE, 2, 1, 8, 3072,
+                                     FAKE, wso, None, None) == -1
+    assert lib.mf_out_gated_residual(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE + 8, FAKE, 2, 1, 8, 3072,
+                                     FAKE, wso, None, None) == -1  # proj misaligned
+
+
+def test_block_bwd_workspace_sizes(lib):
+    # adaLN: tile table, (mean, rstd) per row, then 2 C floats per 64-row block (4 per projection tile bound)
+    # S = 2, frames 1, N = 1000, C = 3072: 5 ints -> 256; 8000 -> 8192; 4 (4 + 4) blocks x 24 KiB = 786 432
+    assert lib.mf_adaln_modulate_bwd_workspace_size(2, 1, 1000, 3072) == 256 + 8192 + 786432
+    assert lib.mf_adaln_modulate_bwd_workspace_size(2, 1, 1000, 768) == 0      # C % 512
+    assert lib.mf_adaln_modulate_bwd_workspace_size(2, 3, 1000, 3072) == 0     # frames
+    # QKV projection, no rotation, N = 1000, 24 x 128: tile table, columns, counts (3 x 256), transposed
+    # weights 2 x 9216 x 3072 bf16, gathered operands [9216][1280] and [3072][1280] bf16 (1280 = 1024 + 256
+    # token columns), bias block sums 20 x 9216 floats; one split (no split partials)
+    qkv = 768 + 2 * 9216 * 3072 * 2 + 9216 * 1280 * 2 + 3072 * 1280 * 2 + 20 * 9216 * 4
+    assert lib.mf_qkv_rope_bwd_workspace_size(2, 1, 1000, 24, 128, 0) == qkv
+    # with rotation: the 3-axis table (5 D / 16 pairs per position) and the inverse-rotated dq, dk
+    assert lib.mf_qkv_rope_bwd_workspace_size(2, 1, 1000, 24, 128, 640) == qkv + 640 * 40 * 8 + 2 * 1000 * 3072 * 2
+    assert lib.mf_qkv_rope_bwd_workspace_size(2, 1, 1000, 24, 96, 0) == 0      # head_dim
+    assert lib.mf_qkv_rope_bwd_workspace_size(2, 1, 1 << 23, 24, 128, 0) == 0  # too many tokens for the pitch
+    assert lib.mf_qkv_rope_bwd_workspace_size(2, 1, 1000, 256, 128, 0) == 0   # channels > 16384
+    # output projection, N = 50000, C = 3072: u [N][C] bf16, 4 (196 + 4) dgate blocks x 3072 floats,
+    # transposed weights, gathered operands of 50176 + 256 = 50432 columns, 788 bias blocks, and 4 token
+    # splits (144 output tiles per modality) of fp32 partials [4][2][3072][3072]
+    out = (768 + 50000 * 3072 * 2 + 800 * 3072 * 4 + 2 * 3072 * 3072 * 2 + 2 * 3072 * 50432 * 2 + 788 * 3072 * 4
+           + 4 * 2 * 3072 * 3072 * 4)
+    assert lib.mf_out_gated_residual_bwd_workspace_size(2, 1, 50000, 3072) == out
+    assert lib.mf_out_gated_residual_bwd_workspace_size(2, 1, 50000, 3000) == 0
+
+
+def test_block_bwd_argument_errors(lib):
+    ws = lib.mf_qkv_rope_bwd_workspace_size(2, 1, 8, 24, 128, 64)
+    # mf_adaln_modulate_bwd(dh, x, scale, dres, dx, dshift, dscale, cu, S, frames, n, C, eps, ws, wsb, stream, trace)
+    wsa = lib.mf_adaln_modulate_bwd_workspace_size(2, 1, 8, 3072)
+
+    def ada(**kw):
+        a = dict(dh=FAKE, x=FAKE, sc=FAKE, dres=None, dx=FAKE, dsh=FAKE, dsc=FAKE, cu=FAKE, ns=2, fr=1, n=8, C=3072,
+                 eps=1e-6, ws=FAKE, wsb=wsa)
+        a.update(kw)
+        return lib.mf_adaln_modulate_bwd(a["dh"], a["x"], a["sc"], a["dres"], a["dx"], a["dsh"], a["dsc"], a["cu"],
+                                         a["ns"], a["fr"], a["n"], a["C"], a["eps"], a["ws"], a["wsb"], None, None)
+    assert ada(C=768) == -2
+    assert ada(C=16384) == -2
+    assert ada(eps=0.0) == -1
+    assert ada(dsc=None) == -1
+    assert ada(dres=FAKE + 8) == -1
+    assert ada(dh=FAKE + 2) == -1
+    assert ada(cu=None) == -1
+    assert ada(wsb=wsa - 1) == -3
+    assert ada(ws=FAKE + 16) == -1
+
+    # mf_qkv_rope_bwd(dq, dk, dv, h, wt, wi, dh, dwt, dwi, dbt, dbi, cu, S, frames, pos, nax, theta, max_pos, n, H,
+    #                 D, ws, wsb, stream, trace)
+    def qkv(**kw):
+        a = dict(dq=FAKE, dk=FAKE, dv=FAKE, h=FAKE, wt=FAKE, wi=FAKE, dh=FAKE, dwt=FAKE, dwi=FAKE, dbt=None, dbi=None,
+                 cu=FAKE, ns=2, fr=1, pos=FAKE, nax=2, theta=10000.0, max_pos=64, n=8, H=24, D=128, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return lib.mf_qkv_rope_bwd(a["dq"], a["dk"], a["dv"], a["h"], a["wt"], a["wi"], a["dh"], a["dwt"], a["dwi"],
+                                   a["dbt"], a["dbi"], a["cu"], a["ns"], a["fr"], a["pos"], a["nax"], a["theta"],
+                                   a["max_pos"], a["n"], a["H"], a["D"], a["ws"], a["wsb"], None, None)
+    assert qkv(D=96) == -2
+    assert qkv(H=256) == -2                     # channels 32768 > 16384
+    assert qkv(H=0) == -1
+    assert qkv(nax=4) == -1
+    assert qkv(max_pos=0) == -1
+    assert qkv(dwt=None) == -1
+    assert qkv(dwi=FAKE + 4) == -1
+    assert qkv(dbt=FAKE + 2) == -1              # float alignment
+    assert qkv(dq=FAKE + 8) == -1
+    assert qkv(wsb=ws - 1) == -3
+    assert qkv(n=1 << 23) == -2                 # too many tokens
+    # mf_out_gated_residual_bwd(dy, o, proj, wt, wi, gate, d_o, dwt, dwi, dbt, dbi, dgate, cu, S, frames, n, C, ws,
+    #                           wsb, stream, trace)
+    wso = lib.mf_out_gated_residual_bwd_workspace_size(2, 1, 8, 3072)
+
+    def out(**kw):
+        a = dict(dy=FAKE, o=FAKE, proj=FAKE, wt=FAKE, wi=FAKE, gate=FAKE, do=FAKE, dwt=FAKE, dwi=FAKE, dbt=None,
+                 dbi=None, dg=FAKE, cu=FAKE, ns=2, fr=1, n=8, C=3072, ws=FAKE, wsb=wso)
+        a.update(kw)
+        return lib.mf_out_gated_residual_bwd(a["dy"], a["o"], a["proj"], a["wt"], a["wi"], a["gate"], a["do"],
+                                             a["dwt"], a["dwi"], a["dbt"], a["dbi"], a["dg"], a["cu"], a["ns"],
+                                             a["fr"], a["n"], a["C"], a["ws"], a["wsb"], None, None)
+    assert out(C=3000) == -2
+    assert out(proj=None) == -1                 # the forward's pre-gate projection is required
+    assert out(dg=None) == -1
+    assert out(gate=FAKE + 4) == -1
+    assert out(fr=0) == -1
+    assert out(wsb=wso - 1) == -3
+    assert out(ws=FAKE + 16) == -1

@@ -47,6 +47,7 @@ STREAM_BQKV = 26     # + modality
 STREAM_WO = 28       # + modality
 STREAM_BO = 30       # + modality
 STREAM_O = 32
+STREAM_GRAD = 33    # + 0 dy / dh, + 1 dq, + 2 dk, + 3 dv
 
 Sample = Tuple[int, int, int]  # (text_len, grid_h, grid_w)
 
@@ -263,3 +264,13 @@ def block_inputs(seed: int, n_tokens: int, n_samples: int, channels: int, dtype:
         out[f"w_o{m}"] = normal(seed, STREAM_WO + m, (c, c), dtype, w_scale)
         out[f"b_o{m}"] = normal(seed, STREAM_BO + m, (c,), "f32", 0.02)
     return out
+
+
+def block_grads(seed: int, n_tokens: int, channels: int, dtype: str = "bf16"):
+    """Seeded output gradients for the sub-block chains' backward: dy (of the
+    gated residual, also used as dh of the adaptive norm) and dq, dk, dv (of
+    the QKV projection), each [N][C] ~ N(0, 1)."""
+    c = int(channels)
+    return {name: normal(seed, STREAM_GRAD + i, (n_tokens, c), dtype)
+            for i, name in enumerate(("dy", "dq", "dk", "dv"))}
+
