@@ -305,8 +305,86 @@ def block_timing(mf, workloads, w, packres, n_tokens: int, max_pos: int, dev, re
         "note": "torch.mm (hipBLASLt) on the same shapes with one weight, no bias, rotation or residual"}
     out["note"] = (f"bf16 [N][{c}] rows of the bench pack (N={n_tokens}, {s} samples), one weight matrix per "
                    f"modality; bytes = activations read and written once plus the weights of one modality")
+    out["backward"] = block_bwd_timing(mf, workloads, w, d, packres, n_tokens, max_pos, dev, x, o, h, wq, bo, wo,
+                                       gate, scale, reps)
     if cpu:
         out["cpu_baseline"] = block_cpu_baseline(w, d, packres, heads, hd, frames)
+        out["backward"]["cpu_baseline"] = block_bwd_cpu_baseline(w, d, packres, heads, hd, frames)
+    return out
+
+
+def block_bwd_timing(mf, workloads, w, d, packres, n_tokens: int, max_pos: int, dev, x, o, h, wq, bo, wo, gate,
+                     scale, reps: int) -> dict:
+    """Per-stage time of the three backward calls on the bench pack.  FLOPs of a projection's backward:
+    2 N F C for the activation gradient (dgrad) and again for the weight gradient (wgrad), F = 3C (QKV) or C
+    (output); bytes of the memory-bound stages: operands read and written once."""
+    import numpy as np
+    import torch
+
+    heads, hd = w.n_heads, w.head_dim
+    c = heads * hd
+    frames = 2 if w.editing else 1
+    s = int(packres.counts[0].item())
+    cp = packres.cu_pieces
+    pos = packres.pos[:n_tokens]
+    g = workloads.block_grads(w.seed + 101, n_tokens, c)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    dy = bf(g["dy"])
+    dq, dk, dv = (bf(g[k]).view(n_tokens, heads, hd) for k in ("dq", "dk", "dv"))
+    proj = torch.empty_like(x)
+    mf.out_gated_residual(o, x, wo, bo, gate, cp, s, frames, proj=proj)
+    ws_a = torch.empty(mf.mf_adaln_modulate_bwd_workspace_size(s, frames, n_tokens, c), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(mf.mf_qkv_rope_bwd_workspace_size(s, frames, n_tokens, heads, hd, max_pos), dtype=torch.uint8,
+                       device=dev)
+    ws_o = torch.empty(mf.mf_out_gated_residual_bwd_workspace_size(s, frames, n_tokens, c), dtype=torch.uint8,
+                       device=dev)
+    out = {}
+
+    def staged(name, fn):
+        tr = mf.KernelTrace(16)
+        fn(None)
+        torch.cuda.synchronize()
+        acc = {}
+        for _ in range(reps):
+            fn(tr)
+            torch.cuda.synchronize()
+            for nm, ms in tr.results():
+                acc[nm] = acc.get(nm, 0.0) + ms
+        st = {nm: round(v / reps, 4) for nm, v in acc.items()}
+        out[name] = {"ms": round(sum(st.values()), 4), "stages_ms": st}
+
+    staged("adaln_bwd", lambda tr: mf.adaln_modulate_bwd(dy, x, scale, cp, s, frames, workspace=ws_a, trace=tr))
+    staged("qkv_rope_bwd", lambda tr: mf.qkv_rope_bwd(dq, dk, dv, h, wq, cp, s, frames, pos, w.theta, max_pos,
+                                                      workspace=ws_q, trace=tr))
+    staged("out_gated_bwd", lambda tr: mf.out_gated_residual_bwd(dy, o, proj, wo, gate, cp, s, frames, workspace=ws_o,
+                                                                 trace=tr))
+    nc2 = n_tokens * c * 2  # bytes of one bf16 [N][C] tensor
+    for name, f in (("qkv_rope_bwd", 3 * c), ("out_gated_bwd", c)):
+        st = out[name]["stages_ms"]
+        flops = 2.0 * n_tokens * f * c
+        out[name]["flops_per_gemm"] = flops
+        for stage in ("dgrad", "wgrad"):
+            t = st[stage]
+            tf = flops / (t * 1e-3) / 1e12
+            out[name][stage] = {"ms": t, "tflops": round(tf, 1),
+                                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                                             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+        # the gather-transposes move the gradient and the layer input once each way
+        t = st["gather_t"]
+        gb = 2 * (f + c) * n_tokens * 2 / (t * 1e-3) / 1e9
+        out[name]["gather_t"] = {"ms": t, "gbs": round(gb, 1), "frac_hbm": round(gb / PEAK_HBM_GBS, 4)}
+    # adaLN backward: rows read x and dh and write dx; the column sums read x and dh again
+    t = out["adaln_bwd"]["stages_ms"]["adaln_bwd"]
+    gb = 5 * nc2 / (t * 1e-3) / 1e9
+    out["adaln_bwd"]["roofline"] = {"bound": "hbm", "achieved": round(gb, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(gb / PEAK_HBM_GBS, 4), "bytes": 5 * nc2}
+    total = sum(out[k]["ms"] for k in ("adaln_bwd", "qkv_rope_bwd", "out_gated_bwd"))
+    out["total_ms"] = round(total, 4)
+    out["note"] = ("backward of the three chains on the bench pack, QKV with the inverse rotation; stage times from "
+                   "HIP events around each launch (stages_ms), rates from the FLOPs and bytes stated in the fields")
     return out
 
 
@@ -352,6 +430,55 @@ def block_cpu_baseline(w, d, packres, heads: int, hd: int, frames: int, min_seco
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(nthreads), "kind": "oracle",
             "sample": f"fp64 numpy oracle: adaLN + QKV projection with RoPE + gated output projection over {rows} "
                       f"image rows (128-row slices, largest pieces first), {secs:.1f} s"}
+
+
+def block_bwd_cpu_baseline(w, d, packres, heads: int, hd: int, frames: int, min_seconds: float = 8.0) -> dict:
+    """Time the oracle's backward of the block chain (test infrastructure, never the product path) on a bounded
+    sample: adaLN, QKV projection with the inverse rotation and gated output projection backward over 128-row
+    slices of the pack's image pieces (largest first) until about ``min_seconds`` of CPU work; reported as the
+    projections' FLOP rate (activation and weight gradients)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import block
+    import workloads
+
+    cp = packres.cu_pieces.cpu().numpy()
+    s = int(packres.counts[0].item())
+    per = frames + 1
+    pieces = sorted(((int(cp[i + 1] - cp[i]), i) for i in range(per * s) if i % per != 0), reverse=True)
+    pos = packres.pos.cpu().numpy()
+    c = heads * hd
+    f64 = lambda x: workloads.bf16_bits_to_f32(x).astype(np.float64)  # noqa: E731
+    w_q = (f64(d["w_qkv0"]), f64(d["w_qkv1"]))
+    w_o = (f64(d["w_o0"]), f64(d["w_o1"]))
+    g = workloads.block_grads(w.seed + 102, 128, c)
+    gq, gk, gv, gy = (f64(g[k]) for k in ("dq", "dk", "dv", "dy"))
+    secs, rows = 0.0, 0
+    with threadpool_limits(limits=max(1, min(16, len(os.sched_getaffinity(0))))):
+        nthreads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        for length, piece in pieces:
+            sample, a0 = piece // per, int(cp[piece])
+            for r0 in range(0, length - 127, 128):
+                if secs >= min_seconds:
+                    break
+                sl = slice(a0 + r0, a0 + r0 + 128)
+                cu = [0, 0, 128]
+                x, o = f64(d["x"][sl]), f64(d["o"][sl])
+                sh = (128, heads, hd)
+                t0 = time.perf_counter()
+                block.out_gated_residual_bwd(gy, o, x, w_o, (d["b_o0"], d["b_o1"]), d["gate"][sample:sample + 1],
+                                             cu, 1, 1)
+                block.qkv_rope_bwd(gq.reshape(sh), gk.reshape(sh), gv.reshape(sh), x, w_q, cu, 1, 1, pos[sl],
+                                   w.theta)
+                block.adaln_modulate_bwd(gy, x, d["shift"][sample:sample + 1], d["scale"][sample:sample + 1], cu,
+                                         1, 1)
+                secs += time.perf_counter() - t0
+                rows += 128
+    flops = 2.0 * 2.0 * rows * c * 4 * c  # dgrad + wgrad of QKV (3C outputs) and output projection (C outputs)
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(nthreads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle: gated output projection + QKV projection (inverse RoPE) + adaLN backward "
+                      f"over {rows} image rows (128-row slices, largest pieces first), {secs:.1f} s"}
 
 
 def main():

@@ -748,7 +748,7 @@ struct BlockBwdWorkspace {
   size_t tstart = 0, col0 = 0, kr = 0, stats = 0, part = 0;  // common
   size_t tab = 0, dqk = 0, u = 0, wt = 0, at = 0, bt = 0, bpart = 0, split = 0;
   long long pitch = 0;
-  int splits = 1;
+  int splits = 2;
   size_t total = 0;
 };
 
@@ -784,7 +784,7 @@ BlockBwdWorkspace block_bwd_layout(int kind, int32_t n_samples, int32_t frames, 
   w.at = c.take(out_rows * static_cast<size_t>(w.pitch) * 2);
   w.bt = c.take(ch * static_cast<size_t>(w.pitch) * 2);
   w.bpart = c.take(static_cast<size_t>(w.pitch / 64) * out_rows * sizeof(float));
-  if (w.splits > 1) w.split = c.take(static_cast<size_t>(w.splits) * 2 * out_rows * ch * sizeof(float));
+  if (w.splits > 2) w.split = c.take(static_cast<size_t>(w.splits) * out_rows * ch * sizeof(float));
   w.total = c.off;
   return w;
 }
@@ -951,6 +951,13 @@ mf_status mf_qkv_rope_bwd(const void* dq, const void* dk, const void* dv, const 
                             reinterpret_cast<float*>(ws + w.split), dw_text, dw_image, s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
+  if (w.splits > 2) {
+    e = tr.run("split_sum", [&] {
+      return mf::launch_split_sum(reinterpret_cast<float*>(ws + w.split), w.pitch, 3 * channels, channels, kr,
+                                  w.splits, dw_text, dw_image, s);
+    });
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
   return from_hip(tr.run("bias_sum", [&] { return mf::launch_bias_sum(bpart, 3 * channels, kr, w.pitch, db_text, db_image, s); }));
 }
 
@@ -1030,6 +1037,13 @@ mf_status mf_out_gated_residual_bwd(const void* dy, const void* o, const void* p
                             reinterpret_cast<float*>(ws + w.split), dw_text, dw_image, s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
+  if (w.splits > 2) {
+    e = tr.run("split_sum", [&] {
+      return mf::launch_split_sum(reinterpret_cast<float*>(ws + w.split), w.pitch, channels, channels, kr, w.splits,
+                                  dw_text, dw_image, s);
+    });
+    if (e != hipSuccess) return MF_ERR_HIP;
+  }
   return from_hip(tr.run("bias_sum", [&] { return mf::launch_bias_sum(bpart, channels, kr, w.pitch, db_text, db_image, s); }));
 }
 

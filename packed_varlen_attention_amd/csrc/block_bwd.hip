@@ -453,28 +453,46 @@ __global__ __launch_bounds__(256) void adaln_bwd_cols_kernel(const uint16_t* __r
 }
 
 // out[g][col] = sum over the partial-sum blocks of group g = (sample,
-// modality), in block order; part rows have `stride` floats and the sums
-// start at column `col_off`.  Groups without rows get zeros.
+// modality); part rows have `stride` floats and the sums start at column
+// `col_off`.  Groups without rows get zeros.  256 columns per workgroup: the
+// four waves take every fourth block and their sums are added in wave order
+// (a fixed order, so the result does not depend on timing).
 __global__ __launch_bounds__(256) void group_sum_kernel(const float* __restrict__ part, long long stride,
                                                         int col_off, int ncol, const int* __restrict__ tstart,
                                                         int per, int part_rows, float* __restrict__ out) {
+  __shared__ float4 red[4][64];
   const int g = blockIdx.x;
-  const int col = (blockIdx.y * 256 + threadIdx.x) * 4;
-  if (col >= ncol) return;
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int col = blockIdx.y * 256 + 4 * lane;
   const int s = g / 2, m = g % 2;
   const int p0 = s * per + m, p1 = m ? (s + 1) * per : s * per + 1;
   // blocks past the partial rows exist only for a malformed cu_pieces whose
   // overlapping pieces hold more tiles than the launch covered
   const int lo = min(4 * tstart[p0], part_rows), hi = min(4 * tstart[p1], part_rows);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int r = lo; r < hi; ++r) {
-    const float4 v = *reinterpret_cast<const float4*>(part + static_cast<size_t>(r) * stride + col_off + col);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  if (col < ncol) {
+#pragma unroll 4
+    for (int r = lo + q; r < hi; r += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(part + static_cast<size_t>(r) * stride + col_off + col);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
   }
-  *reinterpret_cast<float4*>(out + static_cast<size_t>(g) * ncol + col) = acc;
+  red[q][lane] = acc;
+  __syncthreads();
+  if (q == 0 && col < ncol) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float4 v = red[w][lane];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(out + static_cast<size_t>(g) * ncol + col) = acc;
+  }
 }
 
 // Modality m's gathered column range [lo, hi) (padded to 256), clamped to
@@ -486,19 +504,28 @@ __device__ __forceinline__ void modality_range(const int* __restrict__ kr, int m
   hi = min(m ? k0p + round256(kr[1]) : k0p, cap);
 }
 
-// db_m[f] = sum of the 64-column block sums of modality m's columns.
+// db_m[f] = sum of the 64-column block sums of modality m's columns.  64
+// features per workgroup; the four waves take every fourth block, added in
+// wave order.
 __global__ __launch_bounds__(256) void bias_sum_kernel(const float* __restrict__ part, int n_feat,
                                                        const int* __restrict__ kr, int cap, float* __restrict__ db0,
                                                        float* __restrict__ db1) {
-  const int f = blockIdx.x * 256 + threadIdx.x;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int f = blockIdx.x * 64 + lane;
   const int m = blockIdx.y;
   float* out = m ? db1 : db0;
-  if (f >= n_feat || out == nullptr) return;
+  if (out == nullptr) return;  // uniform over the workgroup
   int lo, hi;
   modality_range(kr, m, cap, lo, hi);
   float acc = 0.f;
-  for (int b = lo / 64; b < hi / 64; ++b) acc += part[static_cast<size_t>(b) * n_feat + f];
-  out[f] = acc;
+  if (f < n_feat) {
+#pragma unroll 8
+    for (int b = lo / 64 + q; b < hi / 64; b += 4) acc += part[static_cast<size_t>(b) * n_feat + f];
+  }
+  red[q][lane] = acc;
+  __syncthreads();
+  if (q == 0 && f < n_feat) out[f] = ((acc + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
 struct DgradArgs {
@@ -556,49 +583,99 @@ __global__ __launch_bounds__(kPWaves * 64) void dgrad_kernel(DgradArgs a) {
   }
 }
 
+// Token chunks of the weight gradient.  The `pairs` (chunk, modality) work
+// items (at least 2) are shared between the modalities in proportion to their
+// padded token counts, at least one each, and each modality's columns are cut
+// into equal multiples of 256, so every chunk carries about the same work.  A
+// modality with a single chunk has that chunk write dW itself (zeros when the
+// modality has no tokens).  Item p's modality, chunk count and column range:
+struct WgradChunk {
+  int m, t, lo, hi;  // modality, chunks of that modality, columns [lo, hi)
+  bool direct;       // the modality's only chunk: it writes dW itself
+};
+
+__device__ __forceinline__ WgradChunk wgrad_chunk(const int* __restrict__ kr, int cap, int pairs, int p) {
+  const int k0 = min(round256(kr[0]), cap);
+  const int k1 = min(round256(kr[1]), cap - k0);
+  const int t0 = k0 + k1 == 0 ? 1
+                 : min(max(static_cast<int>((static_cast<long long>(pairs) * k0 + (k0 + k1) / 2) / (k0 + k1)), 1),
+                       pairs - 1);
+  WgradChunk c;
+  c.m = p < t0 ? 0 : 1;
+  c.t = c.m ? pairs - t0 : t0;
+  const int i = c.m ? p - t0 : p;
+  const int s = c.m ? k0 : 0, k = c.m ? k1 : k0;
+  const int len = round256((k + c.t - 1) / c.t);
+  c.lo = min(s + i * len, s + k);
+  c.hi = min(s + (i + 1) * len, s + k);
+  c.direct = c.t == 1;
+  return c;
+}
+
 struct WgradArgs {
   const uint16_t* a;  // [n_rows][pitch], gathered and transposed (the output gradient)
   const uint16_t* b;  // [n_cols][pitch] (the layer input)
   long long pitch;    // elements
   int n_rows, n_cols, n_ntiles, mtiles;
   const int* kr;
-  int chunk, n_chunks;  // token columns per split, a multiple of 256
-  long long blocks_per;  // blocks per (split, modality)
-  float* out0;  // one split: dW_text, dW_image [n_rows][n_cols]
+  int pairs;  // (chunk, modality) work items
+  int group;  // consecutive (item, tile) pairs per XCD group: 32, or fewer when there are under 256
+  float* out0;  // dW_text, dW_image [n_rows][n_cols]
   float* out1;
-  float* part;  // several splits: [n_chunks][2][n_rows][n_cols]
+  float* part;  // [pairs][n_rows][n_cols]: chunk sums of modalities with several chunks
 };
 
-// dW[j][i] = sum over modality m's token columns k in this split of
-// A[j][k] B[i][k], one 256 x 256 output tile per workgroup.
+// Output tile t of a mtiles x n_ntiles grid in window-major order: windows of
+// 8 row tiles x nw feature tiles (the last row of windows shorter when
+// mtiles is not a multiple of 8), tiles column-major inside a window.
+__device__ __forceinline__ void window_major_tile(int t, int mtiles, int n_ntiles, int& mt, int& nt) {
+  const int nw = window_cols(n_ntiles), n_ntg = n_ntiles / nw;
+  const int full = (mtiles / 8) * n_ntg;  // windows of 8 x nw tiles
+  if (t < full * 8 * nw) {
+    const int win = t / (8 * nw), pos = t % (8 * nw);
+    mt = (win / n_ntg) * 8 + pos % 8;
+    nt = (win % n_ntg) * nw + pos / 8;
+  } else {
+    const int rem = mtiles % 8, u = t - full * 8 * nw;
+    const int win = u / (rem * nw), pos = u % (rem * nw);
+    mt = (mtiles / 8) * 8 + pos % rem;
+    nt = win * nw + pos / rem;
+  }
+}
+
+// dW[j][i] = sum over one chunk of a modality's token columns k of
+// A[j][k] B[i][k], one 256 x 256 output tile per workgroup.  The (item, tile)
+// pairs are listed item by item, tiles window-major, and cut into groups of
+// 32 (fewer when there are under 256, so all eight XCDs get work); group g
+// runs on XCD g % 8 (blocks are dealt to the XCDs round-robin), so every XCD
+// gets the same share of the work and each group's workgroups read about 12
+// row slabs (one window) through that XCD's L2.
 __global__ __launch_bounds__(kPWaves * 64) void wgrad_kernel(WgradArgs a) {
-  const long long b = blockIdx.x;
-  const int pair = static_cast<int>(b / a.blocks_per);
-  const int local = static_cast<int>(b % a.blocks_per);
-  const int ch = pair / 2, m = pair % 2;
+  const int b = blockIdx.x;
+  const int x = b % kXcds, r = b / kXcds;
+  const long long item = (static_cast<long long>(r / a.group) * kXcds + x) * a.group + r % a.group;
+  const int tiles = a.mtiles * a.n_ntiles;
+  if (item >= static_cast<long long>(tiles) * a.pairs) return;
+  const int p = static_cast<int>(item / tiles);
   int mt, nt;
-  window_tile(local, a.n_ntiles, mt, nt);
-  if (mt >= a.mtiles) return;
-  int lo, hi;
-  modality_range(a.kr, m, static_cast<int>(a.pitch), lo, hi);
-  lo = max(lo, ch * a.chunk);
-  hi = min(hi, (ch + 1) * a.chunk);
-  float* out = a.part != nullptr ? a.part + static_cast<size_t>(ch * 2 + m) * a.n_rows * a.n_cols : (m ? a.out1 : a.out0);
-  if (hi <= lo && a.part != nullptr) return;  // the reduction skips empty splits
+  window_major_tile(static_cast<int>(item % tiles), a.mtiles, a.n_ntiles, mt, nt);
+  const WgradChunk ck = wgrad_chunk(a.kr, static_cast<int>(a.pitch), a.pairs, p);
+  float* out = ck.direct ? (ck.m ? a.out1 : a.out0) : a.part + static_cast<size_t>(p) * a.n_rows * a.n_cols;
   const int m0 = mt * kPT, n0 = nt * kFT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[2][4];
   zero_acc(acc);
-  if (hi > lo) {
+  if (ck.hi > ck.lo) {  // an empty chunk writes zeros, so the reduction can add every chunk
     const TileCopy256 copy(wave, lane, static_cast<unsigned>(a.pitch) * 2u);
+    const long long lo = ck.lo;
     auto load = [&](int ks, lds_char* tA, lds_char* tB) {
       const long long kk = lo + ks * kKS;
       copy(a.a + kk, m0, a.n_rows, tA);
       copy(a.b + kk, n0, a.n_cols, tB);
     };
-    tile_gemm<2 * TileCopy256::kCopies>((hi - lo) / kKS, wm, wn, lane, load, acc);
+    tile_gemm<2 * TileCopy256::kCopies>((ck.hi - ck.lo) / kKS, wm, wn, lane, load, acc);
   }
   const int hh = lane >> 5, r32 = lane & 31;
 #pragma unroll
@@ -615,20 +692,26 @@ __global__ __launch_bounds__(kPWaves * 64) void wgrad_kernel(WgradArgs a) {
   }
 }
 
-// dW_m = sum over the splits that hold modality m's columns, in split order
-// (zeros when the modality has no tokens).
+// dW_m = the sum of modality m's chunk sums in chunk order, for a modality
+// with several chunks (one with a single chunk wrote dW_m itself).
 __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, long long n_elems,
-                                                        const int* __restrict__ kr, int cap, int chunk, int n_chunks,
+                                                        const int* __restrict__ kr, int cap, int pairs,
                                                         float* __restrict__ out0, float* __restrict__ out1) {
   const long long e = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) * 4;
   const int m = blockIdx.y;
   if (e >= n_elems) return;
-  int lo, hi;
-  modality_range(kr, m, cap, lo, hi);
+  int first = -1, t = 0;
+  for (int p = 0; p < pairs; ++p) {
+    const WgradChunk ck = wgrad_chunk(kr, cap, pairs, p);
+    if (ck.m == m) {
+      if (first < 0) first = p;
+      t = ck.t;
+    }
+  }
+  if (t <= 1) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    if (max(lo, ch * chunk) >= min(hi, (ch + 1) * chunk)) continue;
-    const float4 v = *reinterpret_cast<const float4*>(part + static_cast<size_t>(ch * 2 + m) * n_elems + e);
+  for (int i = 0; i < t; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(part + static_cast<size_t>(first + i) * n_elems + e);
     acc.x += v.x;
     acc.y += v.y;
     acc.z += v.z;
@@ -644,12 +727,29 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
 
 int block_bwd_cols(int n_tokens) { return ((n_tokens + 255) / 256) * 256 + 256; }
 
+// (chunk, modality) work items of a weight gradient [n_rows][n_cols].  In the
+// usual pack one modality holds most tokens (image latents) and the other few
+// (captions), so the items are taken as 1 + q: q equal chunks of the large
+// modality plus one of the small.  q in [1, 7] minimises (rounds of
+// one-workgroup-per-CU waves of tiles x q workgroups over the 256 CUs) / q,
+// the time in units of one pass over the large modality's tokens, plus the
+// extra traffic of the chunk sums written and read back when q > 1 (about 2 %
+// of a pass per item at these tile sizes).  Tiny packs keep one chunk per
+// modality.
 int block_bwd_splits(int n_tokens, int n_rows, int n_cols) {
   const int tiles = (n_rows / kPT) * (n_cols / kFT);
-  int n = (512 + tiles - 1) / tiles;  // at least two workgroups per CU for the larger modality
-  n = min(n, 8);
-  n = min(n, max(1, block_bwd_cols(n_tokens) / 2048));  // at least 2048 token columns per split
-  return max(n, 1);
+  if (block_bwd_cols(n_tokens) < 4096) return 2;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int q = 1; q <= 7; ++q) {
+    const long long rounds = (static_cast<long long>(tiles) * q + 255) / 256;
+    const double cost = static_cast<double>(rounds) / q + (q > 1 ? 0.02 * (q + 1) : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = q;
+    }
+  }
+  return best + 1;
 }
 
 hipError_t launch_modality_cols(const int* cu_pieces, int n_samples, int frames, int n_tokens, int* col0, int* kr,
@@ -740,7 +840,7 @@ hipError_t launch_group_sum(const float* part, long long stride, int col_off, in
                             int n_samples, int frames, int n_tokens, float* out, hipStream_t stream) {
   if (n_samples == 0) return hipSuccess;
   const int part_rows = 4 * block_mtiles_bound(n_tokens, (frames + 1) * n_samples);
-  const dim3 grid(static_cast<unsigned>(2 * n_samples), static_cast<unsigned>((ncol / 4 + 255) / 256));
+  const dim3 grid(static_cast<unsigned>(2 * n_samples), static_cast<unsigned>((ncol + 255) / 256));
   hipLaunchKernelGGL(group_sum_kernel, grid, dim3(256), 0, stream, part, stride, col_off, ncol, tstart, frames + 1,
                      part_rows, out);
   return hipGetLastError();
@@ -749,7 +849,7 @@ hipError_t launch_group_sum(const float* part, long long stride, int col_off, in
 hipError_t launch_bias_sum(const float* part, int n_feat, const int* kr, long long pitch, float* db0, float* db1,
                            hipStream_t stream) {
   if (db0 == nullptr && db1 == nullptr) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((n_feat + 255) / 256), 2);
+  const dim3 grid(static_cast<unsigned>((n_feat + 63) / 64), 2);
   hipLaunchKernelGGL(bias_sum_kernel, grid, dim3(256), 0, stream, part, n_feat, kr, static_cast<int>(pitch), db0,
                      db1);
   return hipGetLastError();
@@ -780,7 +880,7 @@ hipError_t launch_dgrad(const void* const* g, int n_src, int kseg, const void* w
 }
 
 hipError_t launch_wgrad(const void* at, const void* bt, long long pitch, int n_rows, int n_cols, const int* kr,
-                        int n_chunks, float* part, float* dw0, float* dw1, hipStream_t stream) {
+                        int pairs, float* part, float* dw0, float* dw1, hipStream_t stream) {
   WgradArgs a = {};
   a.a = static_cast<const uint16_t*>(at);
   a.b = static_cast<const uint16_t*>(bt);
@@ -790,21 +890,26 @@ hipError_t launch_wgrad(const void* at, const void* bt, long long pitch, int n_r
   a.n_ntiles = n_cols / kFT;
   a.mtiles = n_rows / kPT;
   a.kr = kr;
-  a.n_chunks = n_chunks;
-  a.chunk = static_cast<int>(((pitch + n_chunks - 1) / n_chunks + 255) / 256 * 256);
-  a.blocks_per = window_blocks(a.mtiles, a.n_ntiles);
+  a.pairs = pairs;
   a.out0 = dw0;
   a.out1 = dw1;
-  a.part = n_chunks > 1 ? part : nullptr;
-  const long long blocks = a.blocks_per * 2 * n_chunks;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  a.part = part;
+  const long long items = static_cast<long long>(a.mtiles) * a.n_ntiles * pairs;
+  a.group = items >= 32 * kXcds ? 32 : static_cast<int>((items + kXcds - 1) / kXcds);
+  const long long groups = (items + a.group - 1) / a.group;
+  const long long blocks = (groups + kXcds - 1) / kXcds * kXcds * a.group;
+  if (blocks > 0x7fffffffLL || pairs < 2) return hipErrorInvalidValue;
   hipLaunchKernelGGL(wgrad_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kPWaves * 64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n_chunks == 1) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_split_sum(const float* part, long long pitch, int n_rows, int n_cols, const int* kr, int pairs,
+                            float* dw0, float* dw1, hipStream_t stream) {
+  if (pairs <= 2) return hipSuccess;  // one chunk per modality
   const long long n_elems = static_cast<long long>(n_rows) * n_cols;
   const dim3 grid(static_cast<unsigned>((n_elems / 4 + 255) / 256), 2);
-  hipLaunchKernelGGL(split_sum_kernel, grid, dim3(256), 0, stream, part, n_elems, kr, static_cast<int>(pitch), a.chunk,
-                     n_chunks, dw0, dw1);
+  hipLaunchKernelGGL(split_sum_kernel, grid, dim3(256), 0, stream, part, n_elems, kr, static_cast<int>(pitch), pairs,
+                     dw0, dw1);
   return hipGetLastError();
 }
 

@@ -121,7 +121,7 @@ hipError_t launch_out_gated(const void* o, const void* x, const void* w_text, co
 // run over blocks of 64 rows: 4 block_mtiles_bound(n_tokens, n_pieces) rows.
 constexpr int kAdaBwdMaxC = 8192;
 int block_bwd_cols(int n_tokens);
-// Token-column splits of a weight gradient [n_rows][n_cols] (1: no split).
+// (chunk, modality) work items of a weight gradient [n_rows][n_cols], >= 2.
 int block_bwd_splits(int n_tokens, int n_rows, int n_cols);
 hipError_t launch_modality_cols(const int* cu_pieces, int n_samples, int frames, int n_tokens, int* col0, int* kr,
                                 hipStream_t stream);
@@ -149,8 +149,12 @@ hipError_t launch_bias_sum(const float* part, int n_feat, const int* kr, long lo
 hipError_t launch_dgrad(const void* const* g, int n_src, int kseg, const void* wt0, const void* wt1,
                         const int* cu_pieces, const int* tstart, int n_samples, int frames, int n_tokens, int n_out,
                         void* out, hipStream_t stream);
-// dw_m [n_rows][n_cols] = at_m bt_m^T over modality m's token columns; part
-// holds n_chunks 2 n_rows n_cols floats when n_chunks > 1.
+// dw_m [n_rows][n_cols] = at_m bt_m^T over modality m's token columns, cut
+// into `pairs` (chunk, modality) items; chunk sums of a modality with several
+// chunks go to part (pairs n_rows n_cols floats when pairs > 2) and
+// launch_split_sum adds them into dw_m.
 hipError_t launch_wgrad(const void* at, const void* bt, long long pitch, int n_rows, int n_cols, const int* kr,
-                        int n_chunks, float* part, float* dw0, float* dw1, hipStream_t stream);
+                        int pairs, float* part, float* dw0, float* dw1, hipStream_t stream);
+hipError_t launch_split_sum(const float* part, long long pitch, int n_rows, int n_cols, const int* kr, int pairs,
+                            float* dw0, float* dw1, hipStream_t stream);
 }  // namespace mf

@@ -269,10 +269,11 @@ def test_block_bwd_workspace_sizes(lib):
     assert lib.mf_qkv_rope_bwd_workspace_size(2, 1, 1 << 23, 24, 128, 0) == 0  # too many tokens for the pitch
     assert lib.mf_qkv_rope_bwd_workspace_size(2, 1, 1000, 256, 128, 0) == 0   # channels > 16384
     # output projection, N = 50000, C = 3072: u [N][C] bf16, 4 (196 + 4) dgate blocks x 3072 floats,
-    # transposed weights, gathered operands of 50176 + 256 = 50432 columns, 788 bias blocks, and 4 token
-    # splits (144 output tiles per modality) of fp32 partials [4][2][3072][3072]
+    # transposed weights, gathered operands of 50176 + 256 = 50432 columns, 788 bias blocks, and fp32 chunk
+    # sums for 6 (chunk, modality) items [6][3072][3072]: 144 output tiles, 1 + 5 chunks (720 workgroups, 3
+    # rounds of 256 CUs for 1/5 of the tokens each)
     out = (768 + 50000 * 3072 * 2 + 800 * 3072 * 4 + 2 * 3072 * 3072 * 2 + 2 * 3072 * 50432 * 2 + 788 * 3072 * 4
-           + 4 * 2 * 3072 * 3072 * 4)
+           + 6 * 3072 * 3072 * 4)
     assert lib.mf_out_gated_residual_bwd_workspace_size(2, 1, 50000, 3072) == out
     assert lib.mf_out_gated_residual_bwd_workspace_size(2, 1, 50000, 3000) == 0
 

@@ -308,6 +308,57 @@ def test_modality_without_tokens_and_empty_pack():
         assert not bool(t.any())
 
 
+@pytest.mark.parametrize("kind", ["mixed", "image_only", "text_only"])
+def test_weight_gradient_token_chunks(kind):
+    """Packs of ~8k tokens, where the weight gradients cut each modality's tokens into chunks (8 work items for
+    these tile counts) and add the chunk sums in a second pass; with a modality empty, its single chunk writes
+    zeros.  Both projections' weight and bias gradients against the oracle."""
+    mf = _mf()
+    heads, hd, frames = 4, 128, 1
+    c = heads * hd
+    rng = np.random.default_rng(161)
+    if kind == "mixed":
+        samples = [(int(rng.integers(1, 200)), int(rng.integers(4, 40)), int(rng.integers(4, 40))) for _ in range(14)]
+    elif kind == "image_only":
+        samples = [(0, int(rng.integers(8, 50)), int(rng.integers(8, 50))) for _ in range(10)]
+    else:
+        samples = [(int(rng.integers(100, 900)), 0, 0) for _ in range(14)]
+    p, pos, n, s, d, g = _inputs(samples, frames, c, 163)
+    assert mf.mf_qkv_rope_bwd_workspace_size(s, frames, n, heads, hd, 0) > 0
+    note(f"test_weight_gradient_token_chunks {kind} N={n} S={s}")
+    cu = p["cu_pieces"]
+    k = max(_modality_rows(cu, s, frames))
+    dqkv = [dev(g[q], "bf16").view(n, heads, hd) for q in ("dq", "dk", "dv")]
+    w = (d["w_qkv0"], d["w_qkv1"])
+    _, dw, db = mf.qkv_rope_bwd(*dqkv, dev(d["x"], "bf16"), (dev(w[0], "bf16"), dev(w[1], "bf16")), _i32(cu), s,
+                                frames, None)
+    proj = _out_forward(mf, d, p, s, frames, c)
+    _, dwo, dbo, _ = mf.out_gated_residual_bwd(dev(g["dy"], "bf16"), dev(d["o"], "bf16"), proj,
+                                               (dev(d["w_o0"], "bf16"), dev(d["w_o1"], "bf16")), _f32(d["gate"]),
+                                               _i32(cu), s, frames)
+    torch.cuda.synchronize()
+    sh = (n, heads, hd)
+    gq, gk, gv = (_bf(g[q]).reshape(sh) for q in ("dq", "dk", "dv"))
+    wf = (_bf(w[0]), _bf(w[1]))
+    _, rdw, rdb = block.qkv_rope_bwd(gq, gk, gv, _bf(d["x"]), wf, cu, s, frames, None)
+    _, adw, adb = _qkv_abs(gq, gk, gv, _bf(d["x"]), wf, cu, s, frames, None, heads, hd)
+    for m in range(2):
+        _check(_host(dw[m]), rdw[m], (k + 64) * U * adw[m] + 1e-6, f"dW[{m}]", 1e-4)
+        _check(_host(db[m]), rdb[m], (k + 64) * U * adb[m] + 1e-6, f"db[{m}]", 1e-4)
+    wo, bo = (_bf(d["w_o0"]), _bf(d["w_o1"])), (d["b_o0"], d["b_o1"])
+    o, x, dy = _bf(d["o"]), _bf(d["x"]), _bf(g["dy"])
+    _, _, rdw, rdb, _ = block.out_gated_residual_bwd(dy, o, x, wo, bo, d["gate"], cu, s, frames)
+    _, _, adw, adb, _ = block.out_gated_residual_bwd(np.abs(dy), np.abs(o), np.abs(x), (np.abs(wo[0]), np.abs(wo[1])),
+                                                     (np.abs(bo[0]), np.abs(bo[1])), np.abs(d["gate"]), cu, s, frames)
+    for m in range(2):
+        _check(_host(dwo[m]), rdw[m], (2.0 ** -8 + (k + 64) * U) * adw[m] + 1e-6, f"dW_o[{m}]", 2.0 ** -8)
+        _check(_host(dbo[m]), rdb[m], (2.0 ** -8 + (k + 64) * U) * adb[m] + 1e-6, f"db_o[{m}]", 2.0 ** -8)
+    empty = {"image_only": 0, "text_only": 1}.get(kind)
+    if empty is not None:
+        for t in (dw[empty], db[empty], dwo[empty], dbo[empty]):
+            assert not bool(t.any())
+
+
 # ---------------------------------------------------------------------------
 # full size, sampled
 
