@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "block_kernels.h"
 #include "mf_kernels.h"
 
 namespace {

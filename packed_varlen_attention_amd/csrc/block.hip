@@ -23,6 +23,7 @@
 // modalities and takes one weight matrix.
 #include "block_gemm.h"
 #include "mf_device.h"
+#include "block_kernels.h"
 #include "mf_kernels.h"
 
 namespace mf {

@@ -26,6 +26,7 @@
 // the output alone would not fill the chip.
 #include "block_gemm.h"
 #include "mf_device.h"
+#include "block_kernels.h"
 #include "mf_kernels.h"
 
 namespace mf {
