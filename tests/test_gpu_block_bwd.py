@@ -359,6 +359,86 @@ def test_weight_gradient_token_chunks(kind):
             assert not bool(t.any())
 
 
+def _chain_check(got, ref, label, rms_rel=2e-2):
+    """Integration bar for gradients carried through several bf16-rounded stages (h, q, k, v, o, proj, u, d_o,
+    dq, dk, dv): each rounding adds about 2^-8 / sqrt(3) relative RMS, so the composed error stays near 1%; a
+    wrong or dropped term is off by O(100%).  The single chains' tests above carry the tight bars."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    rref = float(np.sqrt((ref ** 2).mean()))
+    rel = float(np.sqrt((err ** 2).mean())) / rref
+    print(f"  {label}: max_abs={float(err.max()):.3e} rms_rel={rel:.2e} max|ref|={float(np.abs(ref).max()):.3e}",
+          flush=True)
+    assert np.isfinite(got).all(), label
+    assert rel <= rms_rel, f"{label}: relative RMS error {rel:.2e} > {rms_rel}"
+    assert float(err.max()) <= 0.2 * float(np.abs(ref).max()), f"{label}: max error {float(err.max()):.3e}"
+
+
+@pytest.mark.parametrize("frames", [1, 2])
+def test_block_backward_chain(frames):
+    """The attention sub-block's backward as a training step runs it: gated output projection -> attention
+    (rotated q, k from the QKV epilogue, so pos = NULL there) -> QKV projection with the inverse rotation ->
+    adaLN, adding the residual path's dy into dx; against the oracle's forward and backward composed in
+    float64 from the same inputs."""
+    mf = _mf()
+    heads, hd = 4, 128
+    c = heads * hd
+    samples = EDIT if frames == 2 else SAMPLES
+    p, pos, n, s, d, g = _inputs(samples, frames, c, 171 + frames)
+    note(f"test_block_backward_chain frames={frames} N={n} C={c}")
+    cu = p["cu_pieces"]
+    tcu, tcs = _i32(cu), _i32(p["cu_seqlens"])
+    max_pos = int(pos.max()) + 1
+    x = dev(d["x"], "bf16")
+    wq = (dev(d["w_qkv0"], "bf16"), dev(d["w_qkv1"], "bf16"))
+    bq = (_f32(d["b_qkv0"]), _f32(d["b_qkv1"]))
+    wo = (dev(d["w_o0"], "bf16"), dev(d["w_o1"], "bf16"))
+    bo = (_f32(d["b_o0"]), _f32(d["b_o1"]))
+    gate, shift, scale = _f32(d["gate"]), _f32(d["shift"]), _f32(d["scale"])
+    # forward
+    h = mf.adaln_modulate(x, shift, scale, tcu, s, frames)
+    q, k, v = mf.qkv_rope(h, wq, bq, tcu, s, frames, _i32(pos), heads, THETA, max_pos)
+    o, lse = mf.attn_fwd(q, k, v, tcs, int(p["max_seqlen"]), None, THETA, max_pos, n_segments=s)
+    proj = torch.empty_like(x)
+    mf.out_gated_residual(o.reshape(n, c), x, wo, bo, gate, tcu, s, frames, proj=proj)
+    # backward
+    dy = dev(g["dy"], "bf16")
+    d_o, dwo, dbo, dgate = mf.out_gated_residual_bwd(dy, o.reshape(n, c), proj, wo, gate, tcu, s, frames)
+    dq, dk, dv = mf.attn_bwd(q, k, v, o, lse, d_o.view(n, heads, hd), tcs, int(p["max_seqlen"]), None, THETA,
+                             max_pos, n_segments=s)
+    dh, dwq, dbq = mf.qkv_rope_bwd(dq, dk, dv, h, wq, tcu, s, frames, _i32(pos), THETA, max_pos)
+    dx, dsh, dsc = mf.adaln_modulate_bwd(dh, x, scale, tcu, s, frames, dres=dy)
+    torch.cuda.synchronize()
+    # oracle, float64 end to end
+    xf = _bf(d["x"])
+    wqf = (_bf(d["w_qkv0"]), _bf(d["w_qkv1"]))
+    wof = (_bf(d["w_o0"]), _bf(d["w_o1"]))
+    bqf, bof = (d["b_qkv0"], d["b_qkv1"]), (d["b_o0"], d["b_o1"])
+    rh = block.adaln_modulate(xf, d["shift"], d["scale"], cu, s, frames)
+    rq, rk, rv = block.qkv_rope(rh, wqf, bqf, cu, s, frames, pos, heads, hd, THETA)
+    ro, _ = oracle.attn_fwd(rq, rk, rv, p["cu_seqlens"], None, THETA)
+    rdy = _bf(g["dy"])
+    _, rdo, rdwo, rdbo, rdg = block.out_gated_residual_bwd(rdy, ro.reshape(n, c), xf, wof, bof, d["gate"], cu, s,
+                                                           frames)
+    rdq, rdk, rdv = oracle.attn_bwd(rq, rk, rv, rdo.reshape(n, heads, hd), p["cu_seqlens"], None, THETA)
+    rdh, rdwq, rdbq = block.qkv_rope_bwd(rdq, rdk, rdv, rh, wqf, cu, s, frames, pos, THETA)
+    rdx, rsh, rsc = block.adaln_modulate_bwd(rdh, xf, d["shift"], d["scale"], cu, s, frames)
+    rdx = rdx + rdy
+    _chain_check(host_f64(d_o), rdo, "d_o")
+    _chain_check(host_f64(dq).reshape(n, c), rdq.reshape(n, c), "dq (rotated)")
+    _chain_check(host_f64(dh), rdh, "dh")
+    _chain_check(host_f64(dx), rdx, "dx")
+    for m in range(2):
+        _chain_check(_host(dwo[m]), rdwo[m], f"dW_o[{m}]")
+        _chain_check(_host(dbo[m]), rdbo[m], f"db_o[{m}]")
+        _chain_check(_host(dwq[m]), rdwq[m], f"dW_qkv[{m}]")
+        _chain_check(_host(dbq[m]), rdbq[m], f"db_qkv[{m}]")
+    _chain_check(_host(dgate), rdg, "dgate")
+    _chain_check(_host(dsh), rsh, "dshift")
+    _chain_check(_host(dsc), rsc, "dscale")
+
+
 # ---------------------------------------------------------------------------
 # full size, sampled
 
