@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5;
   const int r32 = lane & 31;
-  const int wm = wave >> 1;  // token rows 64 wm .. + 64
+  const int wm = wave >> 1;  // token rows kWaveRows wm .. + kWaveRows
   const int wn = wave & 1;   // features 128 wn .. + 128
 
   const TileCopy256 copy(wave, lane, static_cast<unsigned>(a.k) * 2u);
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
     copy(a.act + ks * kKS, m0, mend, tA);
     copy(w + ks * kKS, n0, a.n_out, tB);
   };
-  f32x16 acc[2][4];
+  f32x16 acc[kMB][4];
   zero_acc(acc);
   // k is a multiple of 256, so the slice count a multiple of 8
   tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc);
@@ -255,8 +255,8 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
   const float* gate = nullptr;
   if constexpr (kEpi == kEpiGatedResidual) gate = a.gate + (static_cast<size_t>(sample) * 2 + modality) * C;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int tok = m0 + 64 * wm + 32 * mb + r32;
+  for (int mb = 0; mb < kMB; ++mb) {
+    const int tok = m0 + kWaveRows * wm + 32 * mb + r32;
     if (tok >= mend) continue;
     Pos3 p = {0, 0, 0};
     if (rotate) p = load_pos(a.pos, tok, a.nax);

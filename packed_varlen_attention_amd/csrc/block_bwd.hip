@@ -565,13 +565,13 @@ __global__ __launch_bounds__(kPWaves * 64) void dgrad_kernel(DgradArgs a) {
     copy_g(src, m0, mend, tA);
     copy_w(w + kk, n0, a.n_out, tB);
   };
-  f32x16 acc[2][4];
+  f32x16 acc[kMB][4];
   zero_acc(acc);
   tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc);
   const int hh = lane >> 5, r32 = lane & 31;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int tok = m0 + 64 * wm + 32 * mb + r32;
+  for (int mb = 0; mb < kMB; ++mb) {
+    const int tok = m0 + kWaveRows * wm + 32 * mb + r32;
     if (tok >= mend) continue;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(kPWaves * 64) void wgrad_kernel(WgradArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  f32x16 acc[2][4];
+  f32x16 acc[kMB][4];
   zero_acc(acc);
   if (ck.hi > ck.lo) {  // an empty chunk writes zeros, so the reduction can add every chunk
     const TileCopy256 copy(wave, lane, static_cast<unsigned>(a.pitch) * 2u);
@@ -680,8 +680,8 @@ __global__ __launch_bounds__(kPWaves * 64) void wgrad_kernel(WgradArgs a) {
   }
   const int hh = lane >> 5, r32 = lane & 31;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int row = m0 + 64 * wm + 32 * mb + r32;
+  for (int mb = 0; mb < kMB; ++mb) {
+    const int row = m0 + kWaveRows * wm + 32 * mb + r32;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll

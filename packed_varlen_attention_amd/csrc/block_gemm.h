@@ -17,10 +17,21 @@ constexpr int kPT = 256;     // token rows per projection tile
 constexpr int kFT = 256;     // output features per projection tile
 constexpr int kKS = 32;      // reduction slice per pipeline step (one 64-byte LDS row)
 constexpr int kStages = 4;   // LDS stages; copies run three steps ahead
-constexpr int kPWaves = 8;   // 4 x 2 waves, each 64 tokens x 128 features
+constexpr int kPWaves = 8;   // (kPWaves / 2) x 2 waves, each kWaveRows tokens x 128 features
 constexpr int kXcds = 8;     // workgroups are dealt round-robin to the XCDs
+constexpr int kWaveRows = 256 / (kPWaves / 2);  // token rows per wave
+constexpr int kMB = kWaveRows / 32;              // 32-row MFMA blocks per wave
 
 using TileCopy256 = TileCopy<kKS, 256, kPWaves>;
+
+// Wait until at most N (0..63) of this wave's global loads are outstanding:
+// vmcnt's low four bits sit in bits 3:0 of the immediate, its high two in
+// bits 15:14 (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep_upto63() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Rows of piece i, clamped to [0, n_tokens] (cu_pieces is device data the
 // host cannot check; a malformed one yields empty pieces, never a read past
@@ -74,10 +85,11 @@ __host__ inline long long window_blocks(int mtiles, int n_ntiles) {
 // load(ks, r_tile, w_tile) issues this wave's copies of slice ks of both
 // tiles, kCopies in all.  The accumulator holds the transposed tile: lane
 // element e of block (mb, nb) is feature 128 wn + 32 nb + 8 (e/4) + 4 (lane/32)
-// + e%4 of row 64 wm + 32 mb + lane%32 -- four consecutive features per lane.
+// + e%4 of row kWaveRows wm + 32 mb + lane%32 -- four consecutive features per
+// lane.
 template <int kCopies, class Load>
 __device__ __forceinline__ void tile_gemm(int nsteps, int wm, int wn, int lane, const Load& load,
-                                          f32x16 (&acc)[2][4]) {
+                                          f32x16 (&acc)[kMB][4]) {
   constexpr int kTileBytes = 256 * kKS * 2;  // 256 rows of 64 bytes
   // Four stages of a row tile and a feature tile, as separate objects so the
   // compiler can tell the stage being read from stages being filled.
@@ -114,25 +126,25 @@ __device__ __forceinline__ void tile_gemm(int nsteps, int wm, int wn, int lane, 
     const lds_char* B = sB[bf];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 tf[2], wf[4];
+      bf16x8 tf[kMB], wf[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) tf[mb] = frag(A, 64 * wm + 32 * mb, kk);
+      for (int mb = 0; mb < kMB; ++mb) tf[mb] = frag(A, kWaveRows * wm + 32 * mb, kk);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) wf[nb] = frag(B, 128 * wn + 32 * nb, kk);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma32(wf[nb], tf[mb], acc[mb][nb]);
     }
     // Stage ks + 1 has landed once only the two newest stages' copies are
     // outstanding (copies complete in issue order).
-    wait_vmem_keep<2 * kCopies>();
+    wait_vmem_keep_upto63<2 * kCopies>();
     barrier_keep_loads();
   };
   load_stage(0, 0);
   load_stage(1, 1);
   load_stage(2, 2);
-  wait_vmem_keep<2 * kCopies>();
+  wait_vmem_keep_upto63<2 * kCopies>();
   barrier_keep_loads();
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -147,9 +159,9 @@ __device__ __forceinline__ void tile_gemm(int nsteps, int wm, int wn, int lane, 
   wait_vmem();  // the trailing copies land before the workgroup's LDS is released
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][4]) {
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[kMB][4]) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
