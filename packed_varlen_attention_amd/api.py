@@ -227,11 +227,12 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 def adaln_modulate_bwd(dh: torch.Tensor, x: torch.Tensor, scale: torch.Tensor, cu_pieces: torch.Tensor,
                        n_samples: int, frames: int = 1, eps: float = 1e-6, dres: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, stream=None, trace=None):
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                       trace=None):
     """(dx bf16 [N][C], dshift, dscale float [S][2][C]) for h = LN(x) (1 + scale) + shift; dres, if given, is
-    added to dx."""
+    added to dx.  out may be dres (in place), not dh or x."""
     n, c = x.shape
-    dx = torch.empty_like(x)
+    dx = torch.empty_like(x) if out is None else out
     dshift = torch.empty((n_samples, 2, c), dtype=torch.float32, device=x.device)
     dscale = torch.empty_like(dshift)
     if workspace is None:

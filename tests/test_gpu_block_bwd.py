@@ -137,6 +137,12 @@ def test_adaln_modulate_bwd(frames, c, with_dres):
     _check(_host(dsh), rsh, (k + 64) * U * a1 + 1e-6, "dshift", 1e-4)
     # dscale: xhat from fp32 statistics (relative error ~1e-6 per element) on top of the summation
     _check(_host(dsc), rsc, ((k + 64) * U + 4e-6) * a2 + 1e-6, "dscale", 1e-4)
+    if with_dres:  # dx written over dres: the same bits as out of place
+        dx2, _, _ = mf.adaln_modulate_bwd(dev(g["dy"], "bf16"), dev(d["x"], "bf16"), _f32(d["scale"]), _i32(cu), s,
+                                          frames, dres=dres, out=dres)
+        torch.cuda.synchronize()
+        assert dx2.data_ptr() == dres.data_ptr()
+        assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16))
 
 
 # ---------------------------------------------------------------------------
