@@ -244,51 +244,61 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
   };
   f32x16 acc[kMB][4];
   zero_acc(acc);
-  // k is a multiple of 256, so the slice count a multiple of 8
-  tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc);
-
-  // ---- epilogue
   const int C = a.n_out / (kEpi == kEpiQkvRope ? 3 : 1);
   const int part = kEpi == kEpiQkvRope ? n0 / C : 0;  // q, k or v (a tile never straddles two)
   uint16_t* out = kEpi == kEpiQkvRope ? (part == 0 ? a.q : part == 1 ? a.kk : a.v) : a.y;
   const bool rotate = kEpi == kEpiQkvRope && part < 2 && a.pos != nullptr;
   const float* gate = nullptr;
   if constexpr (kEpi == kEpiGatedResidual) gate = a.gate + (static_cast<size_t>(sample) * 2 + modality) * C;
+  const int rbase = m0 + kWaveRows * wm;
+  const int cbase = n0 + 128 * wn - part * C;  // first output column of the wave's block
+  // k is a multiple of 256, so the slice count a multiple of 8
+  tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc, [&](lds_char* sbuf) {
+    const WaveStage st{sbuf};
+    const WaveStage sp{sbuf};
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
-    const int tok = m0 + kWaveRows * wm + 32 * mb + r32;
-    if (tok >= mend) continue;
-    Pos3 p = {0, 0, 0};
-    if (rotate) p = load_pos(a.pos, tok, a.nax);
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int tok = rbase + 32 * mb + r32;
+      const bool ok = tok < mend;
+      Pos3 p = {0, 0, 0};
+      if (rotate && ok) p = load_pos(a.pos, tok, a.nax);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;  // 4 consecutive features
-        float xv[4];
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;  // 4 consecutive features
+          float xv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xv[j] = acc[mb][nb][4 * g + j] + (bias != nullptr ? bias[n + j] : 0.f);
-        const int c = n - part * C;
-        if constexpr (kEpi == kEpiQkvRope) {
-          if (rotate) rotate_n<D, 4>(xv, c % D, p, a.tab, a.max_pos, 1.0f, a.nax);
-        } else {
-          float r[4];
-          const u32x2 raw = *reinterpret_cast<const u32x2*>(a.x + static_cast<size_t>(tok) * C + c);
-          r[0] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] & 0xffffu));
-          r[1] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] >> 16));
-          r[2] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] & 0xffffu));
-          r[3] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] >> 16));
-          const float4 gv = *reinterpret_cast<const float4*>(gate + c);
-          if (a.proj != nullptr)
-            store4<uint16_t>(a.proj + static_cast<size_t>(tok) * C + c, xv[0], xv[1], xv[2], xv[3]);
-          xv[0] = r[0] + gv.x * xv[0];
-          xv[1] = r[1] + gv.y * xv[1];
-          xv[2] = r[2] + gv.z * xv[2];
-          xv[3] = r[3] + gv.w * xv[3];
+          for (int j = 0; j < 4; ++j) xv[j] = acc[mb][nb][4 * g + j] + (bias != nullptr ? bias[n + j] : 0.f);
+          const int c = n - part * C;
+          if constexpr (kEpi == kEpiQkvRope) {
+            if (rotate) rotate_n<D, 4>(xv, c % D, p, a.tab, a.max_pos, 1.0f, a.nax);
+          } else if (ok) {
+            float r[4];
+            const u32x2 raw = *reinterpret_cast<const u32x2*>(a.x + static_cast<size_t>(tok) * C + c);
+            r[0] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] & 0xffffu));
+            r[1] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] >> 16));
+            r[2] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] & 0xffffu));
+            r[3] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] >> 16));
+            const float4 gv = *reinterpret_cast<const float4*>(gate + c);
+            if (a.proj != nullptr)
+              store4<uint16_t>(a.proj + static_cast<size_t>(tok) * C + c, xv[0], xv[1], xv[2], xv[3]);
+            xv[0] = r[0] + gv.x * xv[0];
+            xv[1] = r[1] + gv.y * xv[1];
+            xv[2] = r[2] + gv.z * xv[2];
+            xv[3] = r[3] + gv.w * xv[3];
+          }
+          u32x2 v;
+          v[0] = pack_bf16x2(xv[0], xv[1]);
+          v[1] = pack_bf16x2(xv[2], xv[3]);
+          st.put(32 * mb + r32, 4 * nb + g, hh, v);
         }
-        store4<uint16_t>(out + static_cast<size_t>(tok) * C + c, xv[0], xv[1], xv[2], xv[3]);
-      }
-  }
+    }
+    uint16_t* o = out + static_cast<size_t>(rbase) * C + cbase;
+    sp.flush(lane, mend - rbase, [&](int row, int f, const u32x4& v) {
+      *reinterpret_cast<u32x4*>(o + static_cast<size_t>(row) * C + f) = v;
+    });
+  });
 }
 
 template <int D, int kEpi>

@@ -567,21 +567,26 @@ __global__ __launch_bounds__(kPWaves * 64) void dgrad_kernel(DgradArgs a) {
   };
   f32x16 acc[kMB][4];
   zero_acc(acc);
-  tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc);
   const int hh = lane >> 5, r32 = lane & 31;
+  const int rbase = m0 + kWaveRows * wm;
+  tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc, [&](lds_char* sbuf) {
+    const WaveStage st{sbuf};
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
-    const int tok = m0 + kWaveRows * wm + 32 * mb + r32;
-    if (tok >= mend) continue;
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;
-        store4<uint16_t>(a.out + static_cast<size_t>(tok) * a.n_out + n, acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1],
-                         acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]);
-      }
-  }
+        for (int g = 0; g < 4; ++g) {
+          u32x2 v;
+          v[0] = pack_bf16x2(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1]);
+          v[1] = pack_bf16x2(acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]);
+          st.put(32 * mb + r32, 4 * nb + g, hh, v);
+        }
+    uint16_t* out = a.out + static_cast<size_t>(rbase) * a.n_out + n0 + 128 * wn;
+    st.flush(lane, mend - rbase, [&](int row, int f, const u32x4& v) {
+      *reinterpret_cast<u32x4*>(out + static_cast<size_t>(row) * a.n_out + f) = v;
+    });
+  });
 }
 
 // Token chunks of the weight gradient.  The `pairs` (chunk, modality) work
@@ -668,7 +673,27 @@ __global__ __launch_bounds__(kPWaves * 64) void wgrad_kernel(WgradArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[kMB][4];
   zero_acc(acc);
-  if (ck.hi > ck.lo) {  // an empty chunk writes zeros, so the reduction can add every chunk
+  const int hh = lane >> 5, r32 = lane & 31;
+  // An empty chunk writes zeros, so the reduction can add every chunk.  The
+  // stores go through the wave's LDS buffer, half a block (32 rows) at a time.
+  auto store_block = [&](lds_char* sbuf) {
+    const WaveStageF32 st{sbuf};
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]};
+          st.put(r32, 8 * nb + 2 * g + hh, v);
+        }
+      float* o = out + static_cast<size_t>(m0 + kWaveRows * wm + 32 * mb) * a.n_cols + n0 + 128 * wn;
+      st.flush(lane, [&](int row, int f, const f32x4& v) {
+        *reinterpret_cast<f32x4*>(o + static_cast<size_t>(row) * a.n_cols + f) = v;
+      });
+    }
+  };
+  if (ck.hi > ck.lo) {
     const TileCopy256 copy(wave, lane, static_cast<unsigned>(a.pitch) * 2u);
     const long long lo = ck.lo;
     auto load = [&](int ks, lds_char* tA, lds_char* tB) {
@@ -676,20 +701,18 @@ __global__ __launch_bounds__(kPWaves * 64) void wgrad_kernel(WgradArgs a) {
       copy(a.a + kk, m0, a.n_rows, tA);
       copy(a.b + kk, n0, a.n_cols, tB);
     };
-    tile_gemm<2 * TileCopy256::kCopies>((ck.hi - ck.lo) / kKS, wm, wn, lane, load, acc);
-  }
-  const int hh = lane >> 5, r32 = lane & 31;
+    tile_gemm<2 * TileCopy256::kCopies>((ck.hi - ck.lo) / kKS, wm, wn, lane, load, acc, store_block);
+  } else {
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
-    const int row = m0 + kWaveRows * wm + 32 * mb + r32;
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;
-        store4<float>(out + static_cast<size_t>(row) * a.n_cols + n, acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1],
-                      acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]);
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int row = m0 + kWaveRows * wm + 32 * mb + r32;
+          const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;
+          store4<float>(out + static_cast<size_t>(row) * a.n_cols + n, 0.f, 0.f, 0.f, 0.f);
+        }
   }
 }
 

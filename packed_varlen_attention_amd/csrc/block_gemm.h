@@ -87,9 +87,9 @@ __host__ inline long long window_blocks(int mtiles, int n_ntiles) {
 // element e of block (mb, nb) is feature 128 wn + 32 nb + 8 (e/4) + 4 (lane/32)
 // + e%4 of row kWaveRows wm + 32 mb + lane%32 -- four consecutive features per
 // lane.
-template <int kCopies, class Load>
+template <int kCopies, class Load, class Epi>
 __device__ __forceinline__ void tile_gemm(int nsteps, int wm, int wn, int lane, const Load& load,
-                                          f32x16 (&acc)[kMB][4]) {
+                                          f32x16 (&acc)[kMB][4], const Epi& epi) {
   constexpr int kTileBytes = 256 * kKS * 2;  // 256 rows of 64 bytes
   // Four stages of a row tile and a feature tile, as separate objects so the
   // compiler can tell the stage being read from stages being filled.
@@ -156,8 +156,70 @@ __device__ __forceinline__ void tile_gemm(int nsteps, int wm, int wn, int lane, 
     step(ks + 2, B2{});
     step(ks + 3, B3{});
   }
-  wait_vmem();  // the trailing copies land before the workgroup's LDS is released
+  // The trailing copies land, and every wave is done with every stage, before
+  // the epilogue takes one 16 KB stage buffer per wave.
+  wait_vmem();
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // constant indices only: a runtime index would put the pointer arrays in scratch
+  lds_char* wbuf = sA[0];
+#pragma unroll
+  for (int i = 1; i < kStages; ++i)
+    if (wave == i) wbuf = sA[i];
+#pragma unroll
+  for (int i = 0; i < kStages; ++i)
+    if (wave == kStages + i) wbuf = sB[i];
+  epi(wbuf);
 }
+
+// A wave's 64-row x 128-feature block of bf16 results, staged through the
+// wave's own 16 KB LDS buffer so that the global stores are whole 256-byte
+// row segments instead of 16 bytes in each of 32 rows.  put() takes the four
+// consecutive features a lane holds (accumulator order); flush() stores each
+// row with 16 lanes x 16 bytes.  The 16-byte units of a row are XOR-swizzled
+// by the row, which spreads both access orders over the banks.
+struct WaveStage {
+  lds_char* buf;
+  __device__ __forceinline__ void put(int row, int unit, int half, u32x2 v) const {
+    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(buf + row * 256 + ((unit ^ (row & 15)) * 16) +
+                                                                   half * 8) = v;
+  }
+  // store(row, feature, u32x4 of 8 bf16) for every row < rows of the block
+  template <class Store>
+  __device__ __forceinline__ void flush(int lane, int rows, const Store& store) const {
+    const int unit = lane & 15;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      if (row < rows) {
+        const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            buf + row * 256 + ((unit ^ (row & 15)) * 16));
+        store(row, unit * 8, v);
+      }
+    }
+  }
+};
+
+// The fp32 counterpart for half a wave's block (32 rows x 128 features, 512
+// bytes a row, the lane's four features one 16-byte unit): flush() stores
+// each row with 32 lanes x 16 bytes.
+struct WaveStageF32 {
+  lds_char* buf;
+  __device__ __forceinline__ void put(int row, int unit, const f32x4& v) const {
+    *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(buf + row * 512 + ((unit ^ (row & 31)) * 16)) = v;
+  }
+  template <class Store>
+  __device__ __forceinline__ void flush(int lane, const Store& store) const {
+    const int unit = lane & 31;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int row = 2 * i + (lane >> 5);
+      const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+          buf + row * 512 + ((unit ^ (row & 31)) * 16));
+      store(row, unit * 4, v);
+    }
+  }
+};
 
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[kMB][4]) {
 #pragma unroll
