@@ -441,7 +441,9 @@ mf_status mf_out_gated_residual(const void* o, const void* x, const void* w_text
  * Weight and bias gradients are float [out][in] / float[out] per modality and
  * are OVERWRITTEN (not accumulated); modulation gradients are float
  * [n_samples][2][channels].  A modality without tokens gets zero gradients.
- * Rows outside every piece take no part in the sums.
+ * Rows outside every piece take no part in the sums, and their rows of dh
+ * and d_o are not written (the forward projections do not write them
+ * either); the adaLN backward writes dx for every row.
  *
  * The weight gradient gathers each modality's rows into token-contiguous
  * operands in the workspace, so n_tokens is at most 2^23 - 512 for
