@@ -255,13 +255,13 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
   // k is a multiple of 256, so the slice count a multiple of 8
   tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc, [&](lds_char* sbuf) {
     const WaveStage st{sbuf};
-    const WaveStage sp{sbuf};
+    const int rows = mend - rbase;
+    // the projection (+ bias) and, for q and k, the rotation, in place in acc
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       const int tok = rbase + 32 * mb + r32;
-      const bool ok = tok < mend;
       Pos3 p = {0, 0, 0};
-      if (rotate && ok) p = load_pos(a.pos, tok, a.nax);
+      if (rotate && tok < mend) p = load_pos(a.pos, tok, a.nax);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -270,34 +270,64 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
           float xv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) xv[j] = acc[mb][nb][4 * g + j] + (bias != nullptr ? bias[n + j] : 0.f);
-          const int c = n - part * C;
           if constexpr (kEpi == kEpiQkvRope) {
-            if (rotate) rotate_n<D, 4>(xv, c % D, p, a.tab, a.max_pos, 1.0f, a.nax);
-          } else if (ok) {
-            float r[4];
-            const u32x2 raw = *reinterpret_cast<const u32x2*>(a.x + static_cast<size_t>(tok) * C + c);
-            r[0] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] & 0xffffu));
-            r[1] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] >> 16));
-            r[2] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] & 0xffffu));
-            r[3] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] >> 16));
-            const float4 gv = *reinterpret_cast<const float4*>(gate + c);
-            if (a.proj != nullptr)
-              store4<uint16_t>(a.proj + static_cast<size_t>(tok) * C + c, xv[0], xv[1], xv[2], xv[3]);
-            xv[0] = r[0] + gv.x * xv[0];
-            xv[1] = r[1] + gv.y * xv[1];
-            xv[2] = r[2] + gv.z * xv[2];
-            xv[3] = r[3] + gv.w * xv[3];
+            if (rotate) rotate_n<D, 4>(xv, (n - part * C) % D, p, a.tab, a.max_pos, 1.0f, a.nax);
           }
-          u32x2 v;
-          v[0] = pack_bf16x2(xv[0], xv[1]);
-          v[1] = pack_bf16x2(xv[2], xv[3]);
-          st.put(32 * mb + r32, 4 * nb + g, hh, v);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[mb][nb][4 * g + j] = xv[j];
         }
     }
-    uint16_t* o = out + static_cast<size_t>(rbase) * C + cbase;
-    sp.flush(lane, mend - rbase, [&](int row, int f, const u32x4& v) {
-      *reinterpret_cast<u32x4*>(o + static_cast<size_t>(row) * C + f) = v;
-    });
+    auto put_acc = [&]() {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2 v;
+            v[0] = pack_bf16x2(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1]);
+            v[1] = pack_bf16x2(acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]);
+            st.put(32 * mb + r32, 4 * nb + g, hh, v);
+          }
+    };
+    auto flush_to = [&](uint16_t* dst) {
+      uint16_t* o = dst + static_cast<size_t>(rbase) * C + cbase;
+      st.flush(lane, rows, [&](int row, int f, const u32x4& v) {
+        *reinterpret_cast<u32x4*>(o + static_cast<size_t>(row) * C + f) = v;
+      });
+    };
+    if constexpr (kEpi == kEpiQkvRope) {
+      put_acc();
+      flush_to(out);
+    } else {
+      if (a.proj != nullptr) {  // the pre-gate projection, for the backward
+        put_acc();
+        flush_to(a.proj);
+      }
+      // y = x + gate (o W^T + b): the residual rows come in whole through the
+      // staging buffer, and y goes back out the same way
+      const uint16_t* xb = a.x + static_cast<size_t>(rbase) * C + cbase;
+      st.fill(lane, rows, [&](int row) { return xb + static_cast<size_t>(row) * C; });
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;
+            const float4 gv = *reinterpret_cast<const float4*>(gate + c);
+            const u32x2 raw = st.get(32 * mb + r32, 4 * nb + g, hh);
+            const float r0 = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] & 0xffffu));
+            const float r1 = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] >> 16));
+            const float r2 = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] & 0xffffu));
+            const float r3 = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] >> 16));
+            u32x2 v;
+            v[0] = pack_bf16x2(r0 + gv.x * acc[mb][nb][4 * g], r1 + gv.y * acc[mb][nb][4 * g + 1]);
+            v[1] = pack_bf16x2(r2 + gv.z * acc[mb][nb][4 * g + 2], r3 + gv.w * acc[mb][nb][4 * g + 3]);
+            st.put(32 * mb + r32, 4 * nb + g, hh, v);
+          }
+      flush_to(out);
+    }
   });
 }
 

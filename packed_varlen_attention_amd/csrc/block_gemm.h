@@ -184,6 +184,23 @@ struct WaveStage {
     *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(buf + row * 256 + ((unit ^ (row & 15)) * 16) +
                                                                    half * 8) = v;
   }
+  __device__ __forceinline__ u32x2 get(int row, int unit, int half) const {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(buf + row * 256 +
+                                                                             ((unit ^ (row & 15)) * 16) + half * 8);
+  }
+  // The block's rows < rows from global memory (src(row) = first of the row's
+  // 128 bf16), 16 lanes x 16 bytes a row, into the staged layout.
+  template <class Src>
+  __device__ __forceinline__ void fill(int lane, int rows, const Src& src) const {
+    const int unit = lane & 15;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      if (row < rows)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(buf + row * 256 + ((unit ^ (row & 15)) * 16)) =
+            *reinterpret_cast<const u32x4*>(src(row) + unit * 8);
+    }
+  }
   // store(row, feature, u32x4 of 8 bf16) for every row < rows of the block
   template <class Store>
   __device__ __forceinline__ void flush(int lane, int rows, const Store& store) const {
