@@ -485,7 +485,8 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the packed segments are independent; see DESIGN.md for how the path shards)", file=sys.stderr)
+              "(the packed segments are independent: data parallelism gives each GPU its own pack, and the "
+              "attention path needs no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
