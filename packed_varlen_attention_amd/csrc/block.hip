@@ -256,52 +256,58 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
   tile_gemm<2 * TileCopy256::kCopies>(a.k / kKS, wm, wn, lane, load, acc, [&](lds_char* sbuf) {
     const WaveStage st{sbuf};
     const int rows = mend - rbase;
-    // the projection (+ bias) and, for q and k, the rotation, in place in acc
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const int tok = rbase + 32 * mb + r32;
-      Pos3 p = {0, 0, 0};
-      if (rotate && tok < mend) p = load_pos(a.pos, tok, a.nax);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;  // 4 consecutive features
-          float xv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xv[j] = acc[mb][nb][4 * g + j] + (bias != nullptr ? bias[n + j] : 0.f);
-          if constexpr (kEpi == kEpiQkvRope) {
-            if (rotate) rotate_n<D, 4>(xv, (n - part * C) % D, p, a.tab, a.max_pos, 1.0f, a.nax);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[mb][nb][4 * g + j] = xv[j];
-        }
-    }
-    auto put_acc = [&]() {
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            u32x2 v;
-            v[0] = pack_bf16x2(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1]);
-            v[1] = pack_bf16x2(acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]);
-            st.put(32 * mb + r32, 4 * nb + g, hh, v);
-          }
-    };
     auto flush_to = [&](uint16_t* dst) {
       uint16_t* o = dst + static_cast<size_t>(rbase) * C + cbase;
       st.flush(lane, rows, [&](int row, int f, const u32x4& v) {
         *reinterpret_cast<u32x4*>(o + static_cast<size_t>(row) * C + f) = v;
       });
     };
+    // the lane's 4 consecutive features of block (nb, g) plus the bias
+    auto proj4 = [&](int mb, int nb, int g, float (&xv)[4]) {
+      const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;
+      float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (bias != nullptr) b4 = *reinterpret_cast<const float4*>(bias + n);
+      xv[0] = acc[mb][nb][4 * g] + b4.x;
+      xv[1] = acc[mb][nb][4 * g + 1] + b4.y;
+      xv[2] = acc[mb][nb][4 * g + 2] + b4.z;
+      xv[3] = acc[mb][nb][4 * g + 3] + b4.w;
+    };
+    auto put4 = [&](int mb, int nb, int g, const float (&xv)[4]) {
+      u32x2 v;
+      v[0] = pack_bf16x2(xv[0], xv[1]);
+      v[1] = pack_bf16x2(xv[2], xv[3]);
+      st.put(32 * mb + r32, 4 * nb + g, hh, v);
+    };
     if constexpr (kEpi == kEpiQkvRope) {
-      put_acc();
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        const int tok = rbase + 32 * mb + r32;
+        Pos3 p = {0, 0, 0};
+        if (rotate && tok < mend) p = load_pos(a.pos, tok, a.nax);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float xv[4];
+            proj4(mb, nb, g, xv);
+            if (rotate) rotate_n<D, 4>(xv, (n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh - part * C) % D, p, a.tab,
+                                       a.max_pos, 1.0f, a.nax);
+            put4(mb, nb, g, xv);
+          }
+      }
       flush_to(out);
     } else {
       if (a.proj != nullptr) {  // the pre-gate projection, for the backward
-        put_acc();
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float xv[4];
+              proj4(mb, nb, g, xv);
+              put4(mb, nb, g, xv);
+            }
         flush_to(a.proj);
       }
       // y = x + gate (o W^T + b): the residual rows come in whole through the
@@ -314,17 +320,15 @@ __global__ __launch_bounds__(kPWaves * 64) void proj_kernel(ProjArgs a) {
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int c = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;
-            const float4 gv = *reinterpret_cast<const float4*>(gate + c);
+            float xv[4];
+            proj4(mb, nb, g, xv);
+            const float4 gv = *reinterpret_cast<const float4*>(gate + n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh);
             const u32x2 raw = st.get(32 * mb + r32, 4 * nb + g, hh);
-            const float r0 = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] & 0xffffu));
-            const float r1 = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] >> 16));
-            const float r2 = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] & 0xffffu));
-            const float r3 = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] >> 16));
-            u32x2 v;
-            v[0] = pack_bf16x2(r0 + gv.x * acc[mb][nb][4 * g], r1 + gv.y * acc[mb][nb][4 * g + 1]);
-            v[1] = pack_bf16x2(r2 + gv.z * acc[mb][nb][4 * g + 2], r3 + gv.w * acc[mb][nb][4 * g + 3]);
-            st.put(32 * mb + r32, 4 * nb + g, hh, v);
+            xv[0] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] & 0xffffu)) + gv.x * xv[0];
+            xv[1] = bf16_bits_to_f32(static_cast<uint16_t>(raw[0] >> 16)) + gv.y * xv[1];
+            xv[2] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] & 0xffffu)) + gv.z * xv[2];
+            xv[3] = bf16_bits_to_f32(static_cast<uint16_t>(raw[1] >> 16)) + gv.w * xv[3];
+            put4(mb, nb, g, xv);
           }
       flush_to(out);
     }
