@@ -34,6 +34,10 @@ namespace mf {
 namespace {
 
 constexpr int kSub = 64;  // rows per partial-sum block (a quarter of a projection tile)
+// 64-feature tiles per transpose workgroup: the gathered form works out its
+// column map once for eight; the plain weight transpose takes one
+template <bool kGather>
+constexpr int tr_feat_tiles() { return kGather ? 8 : 1; }
 
 __device__ __forceinline__ int round256(int v) { return (v + 255) & ~255; }
 
@@ -160,7 +164,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
   __shared__ int rows[64];
   const int t = threadIdx.x;
   const long long c0 = static_cast<long long>(blockIdx.x) * 64;
-  const int f0 = blockIdx.y * 64;
   long long n_cols;
   if constexpr (kGather) n_cols = min(static_cast<long long>(round256(a.kr[0])) + round256(a.kr[1]), a.pitch);
   else n_cols = a.n_rows;
@@ -175,43 +178,49 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
     rows[t] = r;
   }
   __syncthreads();
-  const int si = f0 / a.seg;
-  const uint16_t* src = a.src[si] + (f0 - si * a.seg);
   const int chunk = t & 7;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (t >> 3) + 32 * i;
-    const int row = rows[r];
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row >= 0) v = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(row) * a.seg + 8 * chunk);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) tile[r][4 * chunk + j] = v[j];
-  }
-  __syncthreads();
   const int cc = t & 7;  // columns 8 cc .. 8 cc + 7
+  constexpr int kTiles = tr_feat_tiles<kGather>();
+  const int ft_end = min((blockIdx.y + 1) * kTiles, a.n_feat / 64);
+  for (int ft = blockIdx.y * kTiles; ft < ft_end; ++ft) {
+    const int f0 = ft * 64;
+    const int si = f0 / a.seg;
+    const uint16_t* src = a.src[si] + (f0 - si * a.seg);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int f = (t >> 3) + 32 * i;
-    float sum = 0.f;
-    uint32_t w[4];
+    for (int i = 0; i < 2; ++i) {
+      const int r = (t >> 3) + 32 * i;
+      const int row = rows[r];
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row >= 0) v = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(row) * a.seg + 8 * chunk);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = (tile[8 * cc + 2 * j][f >> 1] >> (16 * (f & 1))) & 0xffffu;
-      const uint32_t hi = (tile[8 * cc + 2 * j + 1][f >> 1] >> (16 * (f & 1))) & 0xffffu;
-      w[j] = lo | (hi << 16);
-      sum += bf16_bits_to_f32(static_cast<uint16_t>(lo));
-      sum += bf16_bits_to_f32(static_cast<uint16_t>(hi));
+      for (int j = 0; j < 4; ++j) tile[r][4 * chunk + j] = v[j];
     }
-    if (c0 + 8 * cc < n_cols) {
-      u32x4 o = {w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<u32x4*>(a.dst + static_cast<size_t>(f0 + f) * a.pitch + c0 + 8 * cc) = o;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int f = (t >> 3) + 32 * i;
+      float sum = 0.f;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (tile[8 * cc + 2 * j][f >> 1] >> (16 * (f & 1))) & 0xffffu;
+        const uint32_t hi = (tile[8 * cc + 2 * j + 1][f >> 1] >> (16 * (f & 1))) & 0xffffu;
+        w[j] = lo | (hi << 16);
+        sum += bf16_bits_to_f32(static_cast<uint16_t>(lo));
+        sum += bf16_bits_to_f32(static_cast<uint16_t>(hi));
+      }
+      if (c0 + 8 * cc < n_cols) {
+        u32x4 o = {w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(a.dst + static_cast<size_t>(f0 + f) * a.pitch + c0 + 8 * cc) = o;
+      }
+      if (a.part != nullptr) {
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 2, 64);
+        sum += __shfl_xor(sum, 4, 64);
+        if (cc == 0) a.part[static_cast<size_t>(blockIdx.x) * a.n_feat + f0 + f] = sum;
+      }
     }
-    if (a.part != nullptr) {
-      sum += __shfl_xor(sum, 1, 64);
-      sum += __shfl_xor(sum, 2, 64);
-      sum += __shfl_xor(sum, 4, 64);
-      if (cc == 0) a.part[static_cast<size_t>(blockIdx.x) * a.n_feat + f0 + f] = sum;
-    }
+    __syncthreads();  // the tile is read before the next feature tile overwrites it
   }
 }
 
@@ -791,7 +800,8 @@ hipError_t launch_transpose(const void* src, int rows, int cols, void* dst, hipS
   a.n_rows = rows;
   a.dst = static_cast<uint16_t*>(dst);
   a.pitch = rows;
-  const dim3 grid(static_cast<unsigned>((rows + 63) / 64), static_cast<unsigned>(cols / 64));
+  const dim3 grid(static_cast<unsigned>((rows + 63) / 64),
+                  static_cast<unsigned>((cols / 64 + tr_feat_tiles<false>() - 1) / tr_feat_tiles<false>()));
   hipLaunchKernelGGL(transpose_kernel<false>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -812,7 +822,8 @@ hipError_t launch_gather_t(const void* const* src, int n_src, int seg, const int
   a.per = frames + 1;
   a.n_tokens = n_tokens;
   a.part = part;
-  const dim3 grid(static_cast<unsigned>(pitch / 64), static_cast<unsigned>(a.n_feat / 64));
+  const dim3 grid(static_cast<unsigned>(pitch / 64),
+                  static_cast<unsigned>((a.n_feat / 64 + tr_feat_tiles<true>() - 1) / tr_feat_tiles<true>()));
   hipLaunchKernelGGL(transpose_kernel<true>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
