@@ -904,24 +904,6 @@ mf_status mf_qkv_rope_bwd(const void* dq, const void* dk, const void* dv, const 
   e = tr.run("modality_cols",
              [&] { return mf::launch_modality_cols(cu_pieces, n_samples, frames, n_tokens, col0, kr, s); });
   if (e != hipSuccess) return MF_ERR_HIP;
-  const void* g[3] = {dq, dk, dv};
-  if (pos != nullptr && n_tokens > 0) {
-    // gradients with respect to the un-rotated projections: the inverse rotation
-    float2* tab = reinterpret_cast<float2*>(ws + w.tab);
-    uint16_t* dqk = reinterpret_cast<uint16_t*>(ws + w.dqk);
-    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, nax, theta, s); });
-    if (e != hipSuccess) return MF_ERR_HIP;
-    e = tr.run("rope_inverse", [&] {
-      hipError_t r = mf::launch_rope_apply(dq, mf::kDtypeBf16, dqk, mf::kDtypeBf16, pos, nax, tab, max_pos, n_tokens,
-                                           n_heads, head_dim, true, true, s);
-      if (r != hipSuccess) return r;
-      return mf::launch_rope_apply(dk, mf::kDtypeBf16, dqk + nc, mf::kDtypeBf16, pos, nax, tab, max_pos, n_tokens,
-                                   n_heads, head_dim, true, true, s);
-    });
-    if (e != hipSuccess) return MF_ERR_HIP;
-    g[0] = dqk;
-    g[1] = dqk + nc;
-  }
   uint16_t* wt = reinterpret_cast<uint16_t*>(ws + w.wt);
   const size_t wsz = static_cast<size_t>(3) * channels * channels;
   e = tr.run("transpose_w", [&] {
@@ -930,6 +912,32 @@ mf_status mf_qkv_rope_bwd(const void* dq, const void* dk, const void* dv, const 
     return mf::launch_transpose(w_image, 3 * channels, channels, wt + wsz, s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
+  // The gather-transpose of G = [dq' | dk' | dv] applies the inverse rotation
+  // on the way (gradients with respect to the un-rotated projections) and
+  // leaves dq', dk' token-major in the workspace for the activation gradient.
+  const void* g[3] = {dq, dk, dv};
+  mf::GatherRotation rot = {};
+  if (pos != nullptr) {
+    float2* tab = reinterpret_cast<float2*>(ws + w.tab);
+    uint16_t* dqk = reinterpret_cast<uint16_t*>(ws + w.dqk);
+    e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, nax, theta, s); });
+    if (e != hipSuccess) return MF_ERR_HIP;
+    rot = {pos, nax, max_pos, head_dim, tab, dqk, dqk + nc};
+  }
+  float* bpart = reinterpret_cast<float*>(ws + w.bpart);
+  e = tr.run("gather_t", [&] {
+    hipError_t r = mf::launch_gather_t(g, 3, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.at,
+                                       w.pitch, bpart, pos != nullptr ? &rot : nullptr, s);
+    if (r != hipSuccess) return r;
+    const void* hs[1] = {h};
+    return mf::launch_gather_t(hs, 1, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.bt, w.pitch,
+                               nullptr, nullptr, s);
+  });
+  if (e != hipSuccess) return MF_ERR_HIP;
+  if (pos != nullptr) {
+    g[0] = rot.out_q;
+    g[1] = rot.out_k;
+  }
   if (n_tokens > 0) {
     e = tr.run("dgrad", [&] {
       return mf::launch_dgrad(g, 3, channels, wt, wt + wsz, cu_pieces, tstart, n_samples, frames, n_tokens, channels,
@@ -937,16 +945,6 @@ mf_status mf_qkv_rope_bwd(const void* dq, const void* dk, const void* dv, const 
     });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
-  float* bpart = reinterpret_cast<float*>(ws + w.bpart);
-  e = tr.run("gather_t", [&] {
-    hipError_t r = mf::launch_gather_t(g, 3, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.at,
-                                       w.pitch, bpart, s);
-    if (r != hipSuccess) return r;
-    const void* hs[1] = {h};
-    return mf::launch_gather_t(hs, 1, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.bt, w.pitch,
-                               nullptr, s);
-  });
-  if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("wgrad", [&] {
     return mf::launch_wgrad(ws + w.at, ws + w.bt, w.pitch, 3 * channels, channels, kr, w.splits,
                             reinterpret_cast<float*>(ws + w.split), dw_text, dw_image, s);
@@ -1026,11 +1024,11 @@ mf_status mf_out_gated_residual_bwd(const void* dy, const void* o, const void* p
   float* bpart = reinterpret_cast<float*>(ws + w.bpart);
   e = tr.run("gather_t", [&] {
     hipError_t r = mf::launch_gather_t(us, 1, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.at,
-                                       w.pitch, bpart, s);
+                                       w.pitch, bpart, nullptr, s);
     if (r != hipSuccess) return r;
     const void* os[1] = {o};
     return mf::launch_gather_t(os, 1, channels, cu_pieces, col0, kr, n_samples, frames, n_tokens, ws + w.bt, w.pitch,
-                               nullptr, s);
+                               nullptr, nullptr, s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("wgrad", [&] {

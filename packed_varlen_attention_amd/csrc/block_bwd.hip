@@ -152,13 +152,19 @@ struct TrArgs {
   const int* kr;
   int n_samples, per, n_tokens;
   float* part;  // [pitch / 64][n_feat] column sums of 64-column blocks, or nullptr
+  // inverse rotation of sources 0 and 1 (dq, dk) on the way through, with
+  // the rotated-back rows also written token-major to rot_out[0], rot_out[1]
+  const int* pos;
+  int nax, max_pos;
+  const float2* tab;
+  uint16_t* rot_out[2];
 };
 
 // dst[f][c] = src[row(c)][f] over one block of 64 columns x 64 features,
 // staged through LDS; row(c) is c (plain) or the gathered column's token
 // (zero for padding columns).  Optionally the sum of each feature over the
 // block's 64 columns.
-template <bool kGather>
+template <bool kGather, int kRotD>
 __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
   __shared__ uint32_t tile[64][33];  // [column][feature pair], one dword of padding per row
   __shared__ int rows[64];
@@ -191,7 +197,24 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
       const int r = (t >> 3) + 32 * i;
       const int row = rows[r];
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row >= 0) v = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(row) * a.seg + 8 * chunk);
+      if (row >= 0) {
+        v = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(row) * a.seg + 8 * chunk);
+        if constexpr (kRotD > 0) {
+          if (si < 2) {  // dq or dk: back to the un-rotated projection's gradient
+            const int c = f0 - si * a.seg + 8 * chunk;
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              x[2 * j] = bf16_bits_to_f32(static_cast<uint16_t>(v[j] & 0xffffu));
+              x[2 * j + 1] = bf16_bits_to_f32(static_cast<uint16_t>(v[j] >> 16));
+            }
+            rotate_n<kRotD, 8>(x, c % kRotD, load_pos(a.pos, row, a.nax), a.tab, a.max_pos, -1.0f, a.nax);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+            *reinterpret_cast<u32x4*>(a.rot_out[si] + static_cast<size_t>(row) * a.seg + c) = v;
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) tile[r][4 * chunk + j] = v[j];
     }
@@ -802,13 +825,13 @@ hipError_t launch_transpose(const void* src, int rows, int cols, void* dst, hipS
   a.pitch = rows;
   const dim3 grid(static_cast<unsigned>((rows + 63) / 64),
                   static_cast<unsigned>((cols / 64 + tr_feat_tiles<false>() - 1) / tr_feat_tiles<false>()));
-  hipLaunchKernelGGL(transpose_kernel<false>, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((transpose_kernel<false, 0>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_t(const void* const* src, int n_src, int seg, const int* cu_pieces, const int* col0,
                            const int* kr, int n_samples, int frames, int n_tokens, void* dst, long long pitch,
-                           float* part, hipStream_t stream) {
+                           float* part, const GatherRotation* rot, hipStream_t stream) {
   TrArgs a = {};
   for (int i = 0; i < 3; ++i) a.src[i] = static_cast<const uint16_t*>(src[i < n_src ? i : 0]);
   a.seg = seg;
@@ -824,7 +847,22 @@ hipError_t launch_gather_t(const void* const* src, int n_src, int seg, const int
   a.part = part;
   const dim3 grid(static_cast<unsigned>(pitch / 64),
                   static_cast<unsigned>((a.n_feat / 64 + tr_feat_tiles<true>() - 1) / tr_feat_tiles<true>()));
-  hipLaunchKernelGGL(transpose_kernel<true>, grid, dim3(256), 0, stream, a);
+  if (rot != nullptr) {
+    a.pos = rot->pos;
+    a.nax = rot->nax;
+    a.max_pos = rot->max_pos;
+    a.tab = rot->tab;
+    a.rot_out[0] = static_cast<uint16_t*>(rot->out_q);
+    a.rot_out[1] = static_cast<uint16_t*>(rot->out_k);
+    if (rot->head_dim == 128)
+      hipLaunchKernelGGL((transpose_kernel<true, 128>), grid, dim3(256), 0, stream, a);
+    else if (rot->head_dim == 64)
+      hipLaunchKernelGGL((transpose_kernel<true, 64>), grid, dim3(256), 0, stream, a);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((transpose_kernel<true, 0>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

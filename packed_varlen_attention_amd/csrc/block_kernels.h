@@ -40,12 +40,22 @@ hipError_t launch_modality_cols(const int* cu_pieces, int n_samples, int frames,
                                 hipStream_t stream);
 // dst [cols][rows] = src [rows][cols]^T (bf16, rows and cols multiples of 64).
 hipError_t launch_transpose(const void* src, int rows, int cols, void* dst, hipStream_t stream);
+// Inverse rotation applied by launch_gather_t to its first two sources (dq,
+// dk) on the way through; the rotated-back rows also go token-major to
+// out_q and out_k ([n_tokens][seg], rows inside the pieces only).
+struct GatherRotation {
+  const int* pos;
+  int nax, max_pos, head_dim;
+  const float2* tab;
+  void* out_q;
+  void* out_k;
+};
 // dst [n_src seg][pitch]: the modality-gathered, transposed rows of the
 // n_src sources [n_tokens][seg]; part [pitch / 64][n_src seg] column sums of
-// 64-column blocks, or nullptr.
+// 64-column blocks, or nullptr; rot, or nullptr.
 hipError_t launch_gather_t(const void* const* src, int n_src, int seg, const int* cu_pieces, const int* col0,
                            const int* kr, int n_samples, int frames, int n_tokens, void* dst, long long pitch,
-                           float* part, hipStream_t stream);
+                           float* part, const GatherRotation* rot, hipStream_t stream);
 hipError_t launch_gate_bwd(const void* dy, const void* proj, const float* gate, const int* cu_pieces,
                            const int* tstart, int n_samples, int frames, int n_tokens, int channels, void* u,
                            float* part, hipStream_t stream);
