@@ -184,7 +184,9 @@ struct TileCopy {
   // Copy matrix rows [r0, r0 + kRows) of `base` into `tile`; 0 <= r0 < valid.
   __device__ __forceinline__ void operator()(const void* base, int r0, int valid, lds_char* tile) const {
     const char* src = static_cast<const char*>(base) + static_cast<size_t>(r0) * pitch;  // block-uniform
-    const unsigned last = static_cast<unsigned>(valid - 1 - r0) * pitch + chunk;
+    // Only this tile's rows are ever addressed, so the clamp row is bounded by
+    // the tile height: (kRows - 1) * pitch + chunk stays below 2^32.
+    const unsigned last = static_cast<unsigned>(min(valid - 1 - r0, kRows - 1)) * pitch + chunk;
 #pragma unroll
     for (int r = 0; r < kCopies; ++r) {
       unsigned o = min(off0 + static_cast<unsigned>(r * kStride) * pitch, last);

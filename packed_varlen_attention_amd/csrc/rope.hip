@@ -103,7 +103,7 @@ int rope_table_width(int head_dim, int nax) {
 hipError_t launch_rope_table(float2* tab, int max_pos, int head_dim, int nax, double theta, hipStream_t stream) {
   const long long total = static_cast<long long>(max_pos) * rope_table_width(head_dim, nax);
   if (total <= 0) return hipSuccess;
-  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (total > 0x7fffffffLL - 255) return hipErrorInvalidValue;  // the grid's last index fits an int
   hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, stream, tab,
                      max_pos, head_dim, nax, theta);
   return hipGetLastError();

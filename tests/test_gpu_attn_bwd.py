@@ -129,3 +129,39 @@ def test_more_segments_than_the_scheduler_sorts():
     assert_close_large_values(host_f64(dq)[:n], rq[:n], "dQ 1300 segments")
     assert_close_large_values(host_f64(dk)[:n], rk[:n], "dK 1300 segments")
     assert_close_large_values(host_f64(dv)[:n], rv[:n], "dV 1300 segments")
+
+
+def test_rows_more_than_4gib_past_a_tile_base():
+    """A segment whose rows reach more than 2^32 bytes past a tile's first
+    row: 16384 heads of D = 128 make a token row 4 MiB, so the 1100-token
+    segment spans 4.3 GiB.  The tile copies clamp rows past the segment end
+    with a 32-bit byte offset, which must stay below 2^32 (a wrapped clamp
+    would re-read the wrong rows of one K/V and one Q/dO tile).  Two heads
+    are drawn and repeated across all heads on the device; the oracle
+    recomputes the first and the last head, and heads with the same inputs
+    must give identical gradients."""
+    heads = 16384
+    c = Case([(100, 40, 25)], 1 << 20, 2, 128, "bf16", seed=36, with_dout=True)
+    assert c.n == 1100 and (c.n - 1) * heads * 128 * 2 >= 1 << 32
+
+    def rep(t):
+        return t.repeat(1, heads // 2, 1)
+
+    mf = _mf()
+    q, k, v, do = rep(c.tq), rep(c.tk), rep(c.tv), rep(c.tdo)
+    note(f"mf_varlen_attn_fwd+bwd N={c.n} H={heads} D=128 bf16 (4.3 GiB per tensor)")
+    o, lse = mf.attn_fwd(q, k, v, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    dq, dk, dv = mf.attn_bwd(q, k, v, o, lse, do, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    torch.cuda.synchronize()
+    del q, k, v, do, o, lse
+    for g, name in ((dq, "dQ"), (dk, "dK"), (dv, "dV")):
+        assert torch.equal(g[:, 0], g[:, heads - 2]) and torch.equal(g[:, 1], g[:, heads - 1]), name
+    for src, h in ((0, 0), (1, heads - 1)):
+        sl = slice(src, src + 1)
+        rq, rk, rv = oracle.attn_bwd(c.q[:, sl], c.k[:, sl], c.v[:, sl], c.do[:, sl], c.cu, c.pos, THETA)
+        for g, r, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+            got = host_f64(g[:, h:h + 1])
+            assert_close(got, r, G_MAX, G_MEAN, f"{name} 4 MiB rows head {h}")
+            assert_close_scaled(got, r, f"{name} 4 MiB rows head {h}")
+    del dq, dk, dv
+    torch.cuda.empty_cache()
