@@ -24,7 +24,10 @@
  *     no global state and never allocates device memory: scratch space comes
  *     from the caller's `workspace`.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     Every call only enqueues work on it and never synchronises.
+ *     Every call only enqueues work on it and never synchronises.  Calls
+ *     make no allocation, copy, memset or host synchronisation, so a
+ *     sequence of them can be captured in a HIP graph and replayed; a replay
+ *     reads the inputs' memory as it is at replay time.
  *   - Every call validates its host arguments first; on an error it returns a
  *     negative mf_status and launches nothing.  A launch failure reported by
  *     the HIP runtime returns MF_ERR_HIP.
