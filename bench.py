@@ -541,14 +541,17 @@ def main():
     from packed_varlen_attention_amd.api import attn_workspace
     ws_f = attn_workspace(tq, n_packed, max_pos, False)
     ws_b = attn_workspace(tq, n_packed, max_pos, True)
+    # the forward keeps its rotated bf16 Q and K here for the backward, as a
+    # training step keeps activations
+    rot = mf.rotated_buffer(tq)
 
     def step(traces=None):
         tp, tf, tb = traces if traces else (None, None, None)
         do_pack(out=packres, trace=tp)
         mf.attn_fwd(tq, tk, tv, packres.cu_seqlens, max_seqlen, packres.pos, w.theta, max_pos, out=o, lse=lse,
-                    workspace=ws_f, trace=tf, n_segments=n_packed)
+                    workspace=ws_f, trace=tf, n_segments=n_packed, rotated=rot)
         mf.attn_bwd(tq, tk, tv, o, lse, tdo, packres.cu_seqlens, max_seqlen, packres.pos, w.theta, max_pos,
-                    workspace=ws_b, grads=grads, trace=tb, n_segments=n_packed)
+                    workspace=ws_b, grads=grads, trace=tb, n_segments=n_packed, rotated=rot)
 
     for _ in range(args.warmup):
         step()

@@ -74,7 +74,7 @@ typedef int32_t mf_status;
 #define MF_BF16 0
 #define MF_F32 1
 
-#define MF_ABI_VERSION 4
+#define MF_ABI_VERSION 5
 
 /* One sample descriptor: text tokens, then a grid_h x grid_w latent grid. */
 typedef struct mf_sample {
@@ -191,14 +191,23 @@ size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t 
  *              rotation (then theta and max_pos are ignored).
  * softmax_scale 0 selects 1/sqrt(head_dim).
  * head_dim     64 or 128.
+ * rotated      NULL, or a caller-owned, 16-byte aligned bf16 buffer of
+ *              2 * n_tokens * n_heads * head_dim elements that keeps the
+ *              rotated Q and K for the backward.  It is used only when the
+ *              call rotates or converts them (pos non-NULL, or dtype
+ *              MF_F32), and is then filled with R(pos) q rounded to bf16
+ *              ([n_tokens][n_heads][head_dim]), followed by R(pos) k
+ *              rounded to bf16; rows outside every segment are not written.
+ *              It must not overlap any other argument.
  * workspace    >= mf_varlen_attn_workspace_size(..., backward = 0) bytes.
  */
 mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                              int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
                              int32_t max_seqlen, const int32_t* pos, double theta,
                              int32_t max_pos, int32_t n_tokens, int32_t n_heads,
-                             int32_t head_dim, float softmax_scale, void* workspace,
-                             size_t workspace_bytes, void* stream, mf_trace* trace);
+                             int32_t head_dim, float softmax_scale, void* rotated,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             mf_trace* trace);
 
 /*
  * mf_varlen_attn_bwd -- gradients of the attention above with respect to
@@ -212,6 +221,12 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
  * With P = softmax(S): dv = P^T dout, dS = P * (dout v^T - rowsum(dout*o)),
  * dq = R(pos)^T (scale dS kr), dk = R(pos)^T (scale dS^T qr).  Deterministic:
  * no atomics, the same inputs give bit-identical outputs.
+ * rotated      NULL, or the buffer the forward call on the same q, k, pos,
+ *              theta, dtype and cu_seqlens filled, unmodified since.  When
+ *              the call would rotate or convert Q and K, it reads them from
+ *              there instead, which skips two passes over Q and K; the
+ *              results are bit-identical to those with NULL.  Otherwise
+ *              it is ignored.
  * workspace    >= mf_varlen_attn_workspace_size(..., backward = 1) bytes.
  */
 mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -219,8 +234,9 @@ mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
                              int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
                              int32_t max_seqlen, const int32_t* pos, double theta,
                              int32_t max_pos, int32_t n_tokens, int32_t n_heads,
-                             int32_t head_dim, float softmax_scale, void* workspace,
-                             size_t workspace_bytes, void* stream, mf_trace* trace);
+                             int32_t head_dim, float softmax_scale, const void* rotated,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             mf_trace* trace);
 
 /*
  * Editing (frame-aware 3D RoPE).  For instruction-based editing, a sample's
@@ -284,16 +300,18 @@ mf_status mf_varlen_attn3d_fwd(const void* q, const void* k, const void* v, void
                                int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
                                int32_t max_seqlen, const int32_t* pos, double theta,
                                int32_t max_pos, int32_t n_tokens, int32_t n_heads,
-                               int32_t head_dim, float softmax_scale, void* workspace,
-                               size_t workspace_bytes, void* stream, mf_trace* trace);
+                               int32_t head_dim, float softmax_scale, void* rotated,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               mf_trace* trace);
 
 mf_status mf_varlen_attn3d_bwd(const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
                                int32_t max_seqlen, const int32_t* pos, double theta,
                                int32_t max_pos, int32_t n_tokens, int32_t n_heads,
-                               int32_t head_dim, float softmax_scale, void* workspace,
-                               size_t workspace_bytes, void* stream, mf_trace* trace);
+                               int32_t head_dim, float softmax_scale, const void* rotated,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               mf_trace* trace);
 
 /*
  * Rectified-flow objective on the packed latents.  Training regresses the

@@ -17,7 +17,7 @@ from ._binding import (  # noqa: F401
 from .api import (  # noqa: F401
     PROBE_VECTORS, PackResult, attn_bwd, attn_fwd, cfg_combine, mfma_probe, pack, pack_edit, rf_loss, rf_noise,
     rope2d_apply, rope3d_apply, adaln_modulate, block_workspace, out_gated_residual, qkv_rope, adaln_modulate_bwd,
-    out_gated_residual_bwd, qkv_rope_bwd,
+    out_gated_residual_bwd, qkv_rope_bwd, rotated_buffer,
 )
 
 load_library()

@@ -85,6 +85,9 @@ class MFError(RuntimeError):
 
 _lib: Optional[ctypes.CDLL] = None
 
+# MF_ABI_VERSION of include/mf.h that the argument lists below follow.
+ABI_VERSION = 5
+
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -107,6 +110,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mf_status_string.argtypes = [_i32]
     lib.mf_abi_version.restype = _i32
     lib.mf_abi_version.argtypes = []
+    if lib.mf_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {lib.mf_abi_version()}, the binding expects {ABI_VERSION}: "
+                          "rebuild it with `python -m packed_varlen_attention_amd.build`")
     lib.mf_pack.restype = _i32
     lib.mf_pack.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]
     lib.mf_rope2d_workspace_size.restype = _sz
@@ -117,10 +123,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mf_varlen_attn_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.mf_varlen_attn_fwd.restype = _i32
     lib.mf_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _dbl, _i32,
-                                       _i32, _i32, _i32, _f32, _vp, _sz, _vp, _vp]
+                                       _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp, _vp]
     lib.mf_varlen_attn_bwd.restype = _i32
     lib.mf_varlen_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
-                                       _vp, _dbl, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp, _vp]
+                                       _vp, _dbl, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp, _vp]
     lib.mf_mfma_probe.restype = _i32
     lib.mf_mfma_probe.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp]
     lib.mf_pack_edit.restype = _i32
@@ -296,26 +302,26 @@ def _entry(pos, which: str):
 
 def mf_varlen_attn_fwd(q, k, v, o, lse, cu_seqlens, n_segments: int, max_seqlen: int, pos,
                        theta: float, max_pos: int, softmax_scale: float, workspace, stream=None,
-                       trace=None) -> None:
+                       trace=None, rotated=None) -> None:
     n, h, d = q.shape
     call, name = _entry(pos, "fwd")
     st = call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dtype_code(q),
                                   _ptr(cu_seqlens), int(n_segments), int(max_seqlen), _ptr(pos),
                                   float(theta), int(max_pos), int(n), int(h), int(d), float(softmax_scale),
-                                  _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                  _ptr(rotated), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                   _stream(stream), _trace(trace))
     _check(st, name)
 
 
 def mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, n_segments: int, max_seqlen: int,
                        pos, theta: float, max_pos: int, softmax_scale: float, workspace,
-                       stream=None, trace=None) -> None:
+                       stream=None, trace=None, rotated=None) -> None:
     n, h, d = q.shape
     call, name = _entry(pos, "bwd")
     st = call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                   _ptr(dk), _ptr(dv), dtype_code(q), _ptr(cu_seqlens), int(n_segments),
                                   int(max_seqlen), _ptr(pos), float(theta), int(max_pos), int(n), int(h),
-                                  int(d), float(softmax_scale), _ptr(workspace),
+                                  int(d), float(softmax_scale), _ptr(rotated), _ptr(workspace),
                                   int(workspace.numel() * workspace.element_size()), _stream(stream),
                                   _trace(trace))
     _check(st, name)

@@ -87,7 +87,9 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
              pos: Optional[torch.Tensor] = None, theta: float = 10000.0, max_pos: int = 0,
              softmax_scale: float = 0.0, with_lse: bool = True, workspace: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             stream=None, trace=None, n_segments: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+             stream=None, trace=None, n_segments: Optional[int] = None,
+             rotated: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """rotated: an optional rotated_buffer(q) that keeps the rotated bf16 Q and K for attn_bwd."""
     n, h, _ = q.shape
     nseg = int(cu_seqlens.numel()) - 1 if n_segments is None else int(n_segments)
     o = torch.empty_like(q) if out is None else out
@@ -96,7 +98,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
     if workspace is None:
         workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, False)
     B.mf_varlen_attn_fwd(q, k, v, o, lse if with_lse else None, cu_seqlens, nseg, max_seqlen, pos, theta,
-                         max_pos, softmax_scale, workspace, stream, trace)
+                         max_pos, softmax_scale, workspace, stream, trace, rotated)
     return o, (lse if with_lse else None)
 
 
@@ -104,8 +106,9 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, pos: Optional[torch.Tensor] = None,
              theta: float = 10000.0, max_pos: int = 0, softmax_scale: float = 0.0,
              workspace: Optional[torch.Tensor] = None, grads=None,
-             stream=None, trace=None, n_segments: Optional[int] = None
-             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             stream=None, trace=None, n_segments: Optional[int] = None,
+             rotated: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """rotated: the buffer attn_fwd filled on the same q, k and positions; Q and K are then not rotated again."""
     nseg = int(cu_seqlens.numel()) - 1 if n_segments is None else int(n_segments)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
@@ -113,8 +116,13 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if workspace is None:
         workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, True)
     B.mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nseg, max_seqlen, pos, theta, max_pos,
-                         softmax_scale, workspace, stream, trace)
+                         softmax_scale, workspace, stream, trace, rotated)
     return dq, dk, dv
+
+
+def rotated_buffer(q: torch.Tensor) -> torch.Tensor:
+    """A bf16 [2][n][H][D] buffer for the forward's rotated Q and K (see attn_fwd / attn_bwd)."""
+    return torch.empty((2,) + tuple(q.shape), dtype=torch.bfloat16, device=q.device)
 
 
 PROBE_VECTORS = 4096  # bf16x8 operand vectors mf_mfma_probe reads

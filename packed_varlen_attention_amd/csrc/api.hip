@@ -16,6 +16,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned16_or_null(const void* p) { return p == nullptr || aligned16(p); }
 
 mf_status from_hip(hipError_t e) { return e == hipSuccess ? MF_OK : MF_ERR_HIP; }
 
@@ -53,6 +54,11 @@ bool trace_ok(const mf_trace* t) {
   for (int i = 0; i < t->capacity; ++i)
     if (t->start[i] == nullptr || t->stop[i] == nullptr) return false;
   return true;
+}
+
+// Elements in one half of the caller's `rotated` buffer: one bf16 [n][H][D] tensor.
+size_t rotated_half(int32_t n_tokens, int32_t n_heads, int32_t head_dim) {
+  return static_cast<size_t>(n_tokens) * n_heads * head_dim;
 }
 
 // Workspace of the attention calls, in order; each part 256-byte aligned.
@@ -266,12 +272,13 @@ namespace {
 mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
                         const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
                         double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                        float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
+                        float softmax_scale, void* rotated, void* workspace, size_t workspace_bytes, void* stream,
                         mf_trace* trace) {
   mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, nax, theta, max_pos, n_tokens,
                                    n_heads, head_dim, softmax_scale);
   if (st != MF_OK) return st;
   if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (!aligned16_or_null(rotated)) return MF_ERR_INVALID_ARG;
   if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return MF_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MF_ERR_INVALID_ARG;
@@ -292,12 +299,17 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
     if (e != hipSuccess) return MF_ERR_HIP;
   }
   // K rotated once into bf16 (also converts float32 input); Q is rotated
-  // inside the attention kernel when it is loaded.
-  if (pos != nullptr || dtype == MF_F32) {
-    kr = ws + w.kr_off;
+  // inside the attention kernel when it is loaded.  With `rotated`, K goes
+  // to its second half and the kernel stores the rotated Q in its first.
+  const bool rot_pass = pos != nullptr || dtype == MF_F32;
+  uint16_t* keep = rot_pass ? static_cast<uint16_t*>(rotated) : nullptr;
+  if (rot_pass) {
+    void* kdst = keep != nullptr ? static_cast<void*>(keep + rotated_half(n_tokens, n_heads, head_dim))
+                                 : static_cast<void*>(ws + w.kr_off);
+    kr = kdst;
     e = tr.run("rope_k", [&] {
-      return mf::launch_rope_apply(k, dtype, ws + w.kr_off, MF_BF16, pos, nax, tab, max_pos, n_tokens, n_heads,
-                                   head_dim, pos != nullptr, false, s);
+      return mf::launch_rope_apply(k, dtype, kdst, MF_BF16, pos, nax, tab, max_pos, n_tokens, n_heads, head_dim,
+                                   pos != nullptr, false, s);
     });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
@@ -334,6 +346,7 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
     a.rcu = cu_seqlens;
     a.vfirst = vfirst;
   }
+  a.qr_out = keep;
   e = tr.run("attn_sched", [&] {
     if (merge) {
       hipError_t r = mf::launch_merge_tiny(cu_seqlens, n_segments, n_tokens, vcu, vfirst, s);
@@ -351,12 +364,13 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
                         const void* dout, void* dq, void* dk, void* dv, int32_t dtype, const int32_t* cu_seqlens,
                         int32_t n_segments, int32_t max_seqlen, const int32_t* pos, double theta,
                         int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                        float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
-                        mf_trace* trace) {
+                        float softmax_scale, const void* rotated, void* workspace, size_t workspace_bytes,
+                        void* stream, mf_trace* trace) {
   mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, nax, theta, max_pos, n_tokens,
                                    n_heads, head_dim, softmax_scale);
   if (st != MF_OK) return st;
   if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (!aligned16_or_null(rotated)) return MF_ERR_INVALID_ARG;
   if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
@@ -383,7 +397,11 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
     e = tr.run("rope_table", [&] { return mf::launch_rope_table(tab, max_pos, head_dim, nax, theta, s); });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
-  if (pos != nullptr || dtype == MF_F32) {
+  if ((pos != nullptr || dtype == MF_F32) && rotated != nullptr) {
+    // the forward's rotated bf16 Q and K
+    qr = rotated;
+    kr = static_cast<const uint16_t*>(rotated) + rotated_half(n_tokens, n_heads, head_dim);
+  } else if (pos != nullptr || dtype == MF_F32) {
     qr = ws + w.qr_off;
     kr = ws + w.kr_off;
     e = tr.run("rope_q", [&] {
@@ -471,43 +489,43 @@ extern "C" {
 mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
                              const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
                              double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
-                             mf_trace* trace) {
+                             float softmax_scale, void* rotated, void* workspace, size_t workspace_bytes,
+                             void* stream, mf_trace* trace) {
   return attn_fwd_impl(2, q, k, v, o, lse, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
-                       n_heads, head_dim, softmax_scale, workspace, workspace_bytes, stream, trace);
+                       n_heads, head_dim, softmax_scale, rotated, workspace, workspace_bytes, stream, trace);
 }
 
 mf_status mf_varlen_attn3d_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
                                const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
                                const int32_t* pos, double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads,
-                               int32_t head_dim, float softmax_scale, void* workspace, size_t workspace_bytes,
-                               void* stream, mf_trace* trace) {
+                               int32_t head_dim, float softmax_scale, void* rotated, void* workspace,
+                               size_t workspace_bytes, void* stream, mf_trace* trace) {
   if (pos == nullptr) return MF_ERR_INVALID_ARG;
   return attn_fwd_impl(3, q, k, v, o, lse, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
-                       n_heads, head_dim, softmax_scale, workspace, workspace_bytes, stream, trace);
+                       n_heads, head_dim, softmax_scale, rotated, workspace, workspace_bytes, stream, trace);
 }
 
 mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dout, void* dq, void* dk, void* dv, int32_t dtype, const int32_t* cu_seqlens,
                              int32_t n_segments, int32_t max_seqlen, const int32_t* pos, double theta,
                              int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                             float softmax_scale, void* workspace, size_t workspace_bytes, void* stream,
-                             mf_trace* trace) {
+                             float softmax_scale, const void* rotated, void* workspace, size_t workspace_bytes,
+                             void* stream, mf_trace* trace) {
   return attn_bwd_impl(2, q, k, v, o, lse, dout, dq, dk, dv, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta,
-                       max_pos, n_tokens, n_heads, head_dim, softmax_scale, workspace, workspace_bytes, stream,
-                       trace);
+                       max_pos, n_tokens, n_heads, head_dim, softmax_scale, rotated, workspace, workspace_bytes,
+                       stream, trace);
 }
 
 mf_status mf_varlen_attn3d_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                const void* dout, void* dq, void* dk, void* dv, int32_t dtype,
                                const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
                                const int32_t* pos, double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads,
-                               int32_t head_dim, float softmax_scale, void* workspace, size_t workspace_bytes,
-                               void* stream, mf_trace* trace) {
+                               int32_t head_dim, float softmax_scale, const void* rotated, void* workspace,
+                               size_t workspace_bytes, void* stream, mf_trace* trace) {
   if (pos == nullptr) return MF_ERR_INVALID_ARG;
   return attn_bwd_impl(3, q, k, v, o, lse, dout, dq, dk, dv, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta,
-                       max_pos, n_tokens, n_heads, head_dim, softmax_scale, workspace, workspace_bytes, stream,
-                       trace);
+                       max_pos, n_tokens, n_heads, head_dim, softmax_scale, rotated, workspace, workspace_bytes,
+                       stream, trace);
 }
 
 // ---------------------------------------------------------------------------
@@ -617,8 +635,6 @@ mf_status check_block_common(const int32_t* cu_pieces, int32_t n_samples, int32_
   if (cu_pieces == nullptr) return MF_ERR_INVALID_ARG;
   return check_block_sizes(n_samples, frames, n_tokens, channels);
 }
-
-bool aligned16_or_null(const void* p) { return p == nullptr || aligned16(p); }
 
 }  // namespace
 

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     TIn* __restrict__ o, float* __restrict__ lse, const int* __restrict__ cu, const int* __restrict__ order,
     const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax,
     const float2* __restrict__ tab, int max_pos, float scale_log2, const int* __restrict__ rcu,
-    const int* __restrict__ vfirst) {
+    const int* __restrict__ vfirst, uint16_t* __restrict__ qr_out) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;                   // 16-byte chunks per row
@@ -102,6 +102,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
       if (pos != nullptr) rotate_n<D, 8>(x, e0, qp, tab, max_pos, 1.0f, nax);
 #pragma unroll
       for (int j = 0; j < 8; ++j) qf[kk][j] = static_cast<__bf16>(x[j]);
+      // The caller may keep the rotated bf16 Q for the backward.
+      if (qr_out != nullptr && qok)
+        *reinterpret_cast<u32x4*>(qr_out + qrow * D + e0) = __builtin_bit_cast(u32x4, qf[kk]);
     }
   }
 
@@ -316,13 +319,15 @@ hipError_t launch_fwd_t(const AttnArgs& a, const void* q, const void* kr, const 
   hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, false>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
                      static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
                      static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst);
+                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst,
+                     static_cast<uint16_t*>(a.qr_out));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.vfirst == nullptr) return e;
   hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, true>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
                      static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
                      static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst);
+                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst,
+                     static_cast<uint16_t*>(a.qr_out));
   return hipGetLastError();
 }
 

@@ -66,6 +66,9 @@ struct AttnArgs {
   // segment v (both nullptr: every virtual segment is one real segment).
   const int* rcu;
   const int* vfirst;
+  // Forward only: if non-null, the rotated bf16 Q [n_tokens][n_heads][head_dim]
+  // is written here for the backward.
+  void* qr_out;
 };
 
 // q: caller's (rotated in-kernel), kr/vb: bf16 [N][H][D] (kr already rotated).

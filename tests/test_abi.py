@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     import packed_varlen_attention_amd as m
-    assert m.abi_version() == 4
+    assert m.abi_version() == 5 == m._binding.ABI_VERSION
     for code in (0, -1, -2, -3, -4):
         assert len(m.status_string(code)) > 0
     assert m.status_string(7) == "unknown status"
@@ -53,12 +53,12 @@ FAKE = 1 << 20  # a 256-byte-aligned non-null address; never dereferenced by the
 
 def _fwd(lib, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dtype=0, cu=FAKE, nseg=1, maxlen=8, pos=FAKE,
-                theta=10000.0, max_pos=16, n=8, h=1, d=128, scale=0.0, ws=FAKE, wsb=1 << 30, stream=None)
+                theta=10000.0, max_pos=16, n=8, h=1, d=128, scale=0.0, rot=None, ws=FAKE, wsb=1 << 30, stream=None)
     args.update(kw)
     return lib.mf_varlen_attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dtype"],
                                   args["cu"], args["nseg"], args["maxlen"], args["pos"], args["theta"],
-                                  args["max_pos"], args["n"], args["h"], args["d"], args["scale"], args["ws"],
-                                  args["wsb"], args["stream"], args.get("trace"))
+                                  args["max_pos"], args["n"], args["h"], args["d"], args["scale"], args["rot"],
+                                  args["ws"], args["wsb"], args["stream"], args.get("trace"))
 
 
 def test_forward_argument_errors(lib):
@@ -74,6 +74,8 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, scale=-1.0) == -1
     assert _fwd(lib, wsb=16) == -3
     assert _fwd(lib, ws=None) == -1
+    assert _fwd(lib, rot=FAKE + 8) == -1    # the rotated-Q/K buffer misaligned
+    assert _fwd(lib, rot=FAKE + 8, n=0) == -1
     # nothing to do is OK and launches nothing
     assert _fwd(lib, n=0) == 0
     assert _fwd(lib, nseg=0) == 0
@@ -89,17 +91,19 @@ def test_forward_argument_errors(lib):
 def test_backward_argument_errors(lib):
     def bwd(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, dtype=0, cu=FAKE,
-                 nseg=1, maxlen=8, pos=FAKE, theta=1e4, max_pos=16, n=8, h=2, d=64, scale=0.0, ws=FAKE,
+                 nseg=1, maxlen=8, pos=FAKE, theta=1e4, max_pos=16, n=8, h=2, d=64, scale=0.0, rot=None, ws=FAKE,
                  wsb=1 << 30)
         a.update(kw)
         return lib.mf_varlen_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
                                       a["dv"], a["dtype"], a["cu"], a["nseg"], a["maxlen"], a["pos"], a["theta"],
-                                      a["max_pos"], a["n"], a["h"], a["d"], a["scale"], a["ws"], a["wsb"], None, None)
+                                      a["max_pos"], a["n"], a["h"], a["d"], a["scale"], a["rot"], a["ws"], a["wsb"],
+                                      None, None)
     assert bwd(lse=None) == -1
     assert bwd(dq=None) == -1
     assert bwd(d=32) == -2
     assert bwd(wsb=1) == -3
     assert bwd(dk=FAKE + 4) == -1
+    assert bwd(rot=FAKE + 4) == -1
 
 
 def test_pack_and_rope_argument_errors(lib):
@@ -157,12 +161,12 @@ def test_editing_argument_errors(lib):
         a = dict(pos=FAKE, d=128)
         a.update(kw)
         return lib.mf_varlen_attn3d_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 8, a["pos"], 1e4, 16, 8, 1,
-                                        a["d"], 0.0, FAKE, 1 << 30, None, None)
+                                        a["d"], 0.0, None, FAKE, 1 << 30, None, None)
     assert fwd3(pos=None) == -1
     assert fwd3(pos=FAKE + 2) == -1
     assert fwd3(d=96) == -2
     assert lib.mf_varlen_attn3d_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 8, None,
-                                    1e4, 16, 8, 1, 64, 0.0, FAKE, 1 << 30, None, None) == -1
+                                    1e4, 16, 8, 1, 64, 0.0, None, FAKE, 1 << 30, None, None) == -1
 
 
 def test_editing_workspace_sizes(lib):
