@@ -341,3 +341,24 @@ def test_block_bwd_argument_errors(lib):
     assert out(fr=0) == -1
     assert out(wsb=wso - 1) == -3
     assert out(ws=FAKE + 16) == -1
+
+
+def test_binding_refuses_another_abi_version(tmp_path):
+    """The argument lists follow one ABI version; a library built from other
+    sources is refused at load, before any call."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "old.c"
+    src.write_text('int mf_abi_version(void) { return 4; }\nconst char* mf_status_string(int s) { return "x"; }\n')
+    so = tmp_path / "libold.so"
+    subprocess.run(["gcc", "-shared", "-fPIC", str(src), "-o", str(so)], check=True)
+    import packed_varlen_attention_amd._binding as B
+    saved = B._lib
+    B._lib = None
+    try:
+        with pytest.raises(ImportError, match="ABI version 4"):
+            B.load_library(str(so))
+    finally:
+        B._lib = saved
