@@ -10,7 +10,8 @@ on the mixed native-resolution training pack (50 000-token budget, 24 heads x
 head_dim 128, bf16).  Inputs are resident in GPU memory before timing starts.
 
 Prints ONE JSON line.  value = (forward + backward algorithmic FLOPs) / step
-time, with forward = 4 sum(L_i^2) D H and backward = 10 sum(L_i^2) D H.
+time (the median of the timed steps), with forward = 4 sum(L_i^2) D H and
+backward = 10 sum(L_i^2) D H.
 """
 from __future__ import annotations
 
@@ -136,8 +137,10 @@ def cpu_baseline(w, samples, q, k, v, do, threads: int, min_seconds: float = 10.
     flops = 14.0 * sum_l2 * w.head_dim * heads  # forward 4 + backward 10 per head
     return {
         "value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(nthreads), "kind": "oracle",
+        "blas_threads": int(nthreads), "host_affinity_cores": avail,
         "sample": f"fp64 numpy oracle, forward+backward of {heads} of {w.n_heads} heads over all "
-                  f"{p['n_packed']} segments ({p['n_tokens']} tokens), {secs:.1f} s",
+                  f"{p['n_packed']} segments ({p['n_tokens']} tokens), {secs:.1f} s; "
+                  f"{int(nthreads)} BLAS threads of the {avail} cores in the process's affinity mask",
     }
 
 
@@ -557,25 +560,29 @@ def main():
         step()
     traces = [(mf.KernelTrace(4), mf.KernelTrace(8), mf.KernelTrace(8)) for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
+    marks[0].record(stream)
     for i in range(args.steps):
         step(traces[i])
-    e1.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    ms_step = float(np.median(step_ms))
+    ms_total = marks[0].elapsed_time(marks[-1])
 
-    # per-kernel mean duration over the timed steps (events on the launch stream)
-    kern = {}
-    call_ms = {"pack": 0.0, "fwd": 0.0, "bwd": 0.0}
-    for tr in traces:
+    # per-kernel median duration over the timed steps (events on the launch
+    # stream); each call's time is the median of its kernels' per-step sums
+    per_step = [{} for _ in range(args.steps)]
+    call_steps = {"pack": [0.0] * args.steps, "fwd": [0.0] * args.steps, "bwd": [0.0] * args.steps}
+    for i, tr in enumerate(traces):
         for label, t in zip(("pack", "fwd", "bwd"), tr):
             for name, ms in t.results():
                 key = name if label != "bwd" or name not in ("rope_table", "rope_k") else name + "@bwd"
-                kern[key] = kern.get(key, 0.0) + ms / args.steps
-                call_ms[label] += ms / args.steps
+                per_step[i][key] = per_step[i].get(key, 0.0) + ms
+                call_steps[label][i] += ms
+    kern = {key: float(np.median([d.get(key, 0.0) for d in per_step])) for key in per_step[0]}
+    call_ms = {label: float(np.median(v)) for label, v in call_steps.items()}
 
     fwd_flops = 4.0 * sum_l2 * D * H
     bwd_flops = 10.0 * sum_l2 * D * H
@@ -615,6 +622,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_mean": round(ms_total / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

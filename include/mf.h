@@ -197,8 +197,9 @@ size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t 
  *              call rotates or converts them (pos non-NULL, or dtype
  *              MF_F32), and is then filled with R(pos) q rounded to bf16
  *              ([n_tokens][n_heads][head_dim]), followed by R(pos) k
- *              rounded to bf16; rows outside every segment are not written.
- *              It must not overlap any other argument.
+ *              rounded to bf16.  In the Q half, rows outside every segment
+ *              are not written; the K half is written for every row in
+ *              [0, n_tokens).  It must not overlap any other argument.
  * workspace    >= mf_varlen_attn_workspace_size(..., backward = 0) bytes.
  */
 mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

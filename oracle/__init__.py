@@ -38,6 +38,6 @@ forms, invariants, brute force and library routines (see those files).
 """
 from .pack import pack, positions, gather, pack_edit, positions_edit, gather_edit  # noqa: F401
 from .rope import inv_freq, rope2d, rope3d, rope_axes, blocks3d  # noqa: F401
-from .attention import attn_fwd, attn_bwd, attn_fwd_rows  # noqa: F401
+from .attention import attn_fwd, attn_bwd, attn_bwd_given, attn_fwd_rows  # noqa: F401
 from . import flow  # noqa: F401
 from . import block  # noqa: F401

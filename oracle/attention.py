@@ -165,3 +165,50 @@ def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
     if pos is None:
         return dqr, dkr, dv
     return rope_axes(dqr, pos, theta, inverse=True), rope_axes(dkr, pos, theta, inverse=True), dv
+
+
+def attn_bwd_given(q: np.ndarray, k: np.ndarray, v: np.ndarray, o: np.ndarray, lse: np.ndarray,
+                   dout: np.ndarray, cu_seqlens: Sequence[int], pos: Optional[np.ndarray],
+                   theta: float = 10000.0, scale: Optional[float] = None, chunk: int = 1024):
+    """dQ, dK, dV [N][H][D] (float64) of the backward step taken as a function
+    of given forward outputs: O [N][H][D] and LSE [H][N] are inputs, as in the
+    training shape of the workloads (Q, K, V, O, LSE and dO given).
+
+    Per (segment, head): P = exp(scale * Qr Kr^T - LSE) row by row,
+    Delta = rowsum(dO * O) from the given O, dV = P^T dO, dP = dO V^T,
+    dS = P * (dP - Delta), dQr = scale * dS Kr, dKr = scale * dS^T Qr; dQ and
+    dK are then rotated back.  With the exact O and LSE of ``attn_fwd`` this is
+    ``attn_bwd``; with rounded O and LSE it is the exact gradient step on those
+    rounded values, which separates a backward's own rounding error from the
+    rounding its inputs already carry.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    n, h_count, d = v.shape
+    sc = _scale(d, scale)
+    qr = _rotated(q, pos, theta)
+    kr = _rotated(k, pos, theta)
+    dqr = np.zeros_like(v)
+    dkr = np.zeros_like(v)
+    dv = np.zeros_like(v)
+    for _, a, b in _segments(cu_seqlens):
+        if b <= a:
+            continue
+        for h in range(h_count):
+            kk = kr[a:b, h, :]
+            vv = v[a:b, h, :]
+            for c0 in range(a, b, chunk):
+                c1 = min(b, c0 + chunk)
+                qq = qr[c0:c1, h, :]
+                dd = do[c0:c1, h, :]
+                p = np.exp(sc * (qq @ kk.T) - lse[h, c0:c1, None])
+                delta = (dd * o[c0:c1, h, :]).sum(axis=1, keepdims=True)
+                dv[a:b, h, :] += p.T @ dd
+                ds = p * (dd @ vv.T - delta)
+                dqr[c0:c1, h, :] = sc * (ds @ kk)
+                dkr[a:b, h, :] += sc * (ds.T @ qq)
+    if pos is None:
+        return dqr, dkr, dv
+    return rope_axes(dqr, pos, theta, inverse=True), rope_axes(dkr, pos, theta, inverse=True), dv

@@ -8,9 +8,10 @@ What the pages say:
 * the backbone follows MMDiT: text and image tokens are concatenated for
   joint self-attention, with normalisation and projection layers specific
   to each modality (Mage-Flow paper section 3.2.1 "Model Architecture and
-  Native Packing", paperlayer.ai summary; ai.thesatyajit.com explainer,
-  Figure 5 caption: modality-specific norms, joint self-attention,
-  per-sample 2D RoPE);
+  Native Packing", paperlayer.ai summary; the ai.thesatyajit.com
+  explainer's Figure 5 caption likewise shows each modality normalised on
+  its own before the shared attention, with the rotary embedding applied
+  per sample);
 * the training system fuses the memory-bound chains of the transformer
   blocks; on the transformer side the fused chains combine adaptive
   normalisation, rotary embeddings and gated residual updates (paper

@@ -300,10 +300,37 @@ def _entry(pos, which: str):
     return getattr(lib(), name), name
 
 
+def _span(t: torch.Tensor):
+    start = t.data_ptr()
+    return start, start + t.numel() * t.element_size()
+
+
+def _check_rotated(rotated, q, others) -> None:
+    """The C ABI takes the rotated buffer as a bare pointer with no size: check
+    here that it is a bf16 tensor of at least 2 * q.numel() elements that
+    overlaps none of the call's other tensors."""
+    if rotated is None:
+        return
+    if rotated.dtype != torch.bfloat16 or not rotated.is_contiguous():
+        raise ValueError("rotated must be a contiguous bfloat16 tensor (see rotated_buffer)")
+    if rotated.numel() < 2 * q.numel():
+        raise ValueError(f"rotated holds {rotated.numel()} elements; the call needs 2 * {q.numel()}")
+    if rotated.device != q.device:
+        raise ValueError("rotated must be on the device of q")
+    a0, a1 = _span(rotated)
+    for t in others:
+        if t is None or t.numel() == 0:
+            continue
+        b0, b1 = _span(t)
+        if a0 < b1 and b0 < a1:
+            raise ValueError("rotated overlaps another argument of the call")
+
+
 def mf_varlen_attn_fwd(q, k, v, o, lse, cu_seqlens, n_segments: int, max_seqlen: int, pos,
                        theta: float, max_pos: int, softmax_scale: float, workspace, stream=None,
                        trace=None, rotated=None) -> None:
     n, h, d = q.shape
+    _check_rotated(rotated, q, (q, k, v, o, lse, cu_seqlens, pos, workspace))
     call, name = _entry(pos, "fwd")
     st = call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dtype_code(q),
                                   _ptr(cu_seqlens), int(n_segments), int(max_seqlen), _ptr(pos),
@@ -317,6 +344,7 @@ def mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, n_segments
                        pos, theta: float, max_pos: int, softmax_scale: float, workspace,
                        stream=None, trace=None, rotated=None) -> None:
     n, h, d = q.shape
+    _check_rotated(rotated, q, (q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, pos, workspace))
     call, name = _entry(pos, "bwd")
     st = call(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                   _ptr(dk), _ptr(dv), dtype_code(q), _ptr(cu_seqlens), int(n_segments),

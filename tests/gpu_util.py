@@ -53,14 +53,15 @@ def assert_close(got, ref, max_abs: float, mean_abs: float, label: str) -> None:
     assert mn <= mean_abs, f"{label}: mean-abs {mn} > {mean_abs}"
 
 
-def assert_close_scaled(got, ref, label: str, rel_rms_max: float = 8e-3, qscale: float = 1.0) -> None:
-    """Bar for inputs scaled away from N(0, 1) (the peaky gates): the fixed
-    2e-2 max-abs bar holds for outputs up to |4|, so it grows with max|ref|
-    beyond that, and with the Q scale, which multiplies the logits and so the
-    logit error the bf16 rounding of rotated Q and K leaves; the relative RMS
-    error must stay at the bf16 level."""
+def assert_close_scaled(got, ref, label: str, rel_rms_max: float = 8e-3) -> None:
+    """Bar for outputs beyond the |x| <= 4 range the fixed max-abs 2e-2 bar is
+    written for: the bf16 roundings on the path (operands, P, dS, O) each
+    carry a relative error of at most 2^-9, so the absolute error an element
+    can pick up grows with the magnitude of the values it is made of, and the
+    bar grows with max|ref| / 4 beyond 4.  The relative RMS error must stay at
+    the bf16 level (8e-3, about 4 units of 2^-9)."""
     ref = np.asarray(ref, dtype=np.float64)
-    scale = qscale * (max(1.0, float(np.abs(ref).max()) / 4.0) if ref.size else 1.0)
+    scale = max(1.0, float(np.abs(ref).max()) / 4.0) if ref.size else 1.0
     mx, mn = errors(got, ref)
     rel = float(np.sqrt(np.mean((np.asarray(got) - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
     print(f"  {label}: max_abs={mx:.3e} (bar {2e-2 * scale:.3e}) rel_rms={rel:.3e} max|ref|={np.abs(ref).max():.3e}",
@@ -70,28 +71,39 @@ def assert_close_scaled(got, ref, label: str, rel_rms_max: float = 8e-3, qscale:
     assert rel <= rel_rms_max, f"{label}: relative rms {rel} > {rel_rms_max}"
 
 
-def assert_close_large_values(got, ref, label: str, rel_large: float = 1.5e-2, rel_rms_max: float = 8e-3) -> None:
-    """Bar for outputs whose magnitude exceeds the |x| <= 4 range the fixed
-    2e-2 max-abs bar is written for (gradients of segments with only a few
-    keys): elements with |ref| <= 4 keep max-abs 2e-2 (and the whole tensor
-    mean-abs 2e-3); larger elements get a relative bound.  The bf16 rounding
-    of the rotated Q and K moves a logit s by about |s| * 2^-8, i.e. the
-    softmax weights, dS and the gradients by ~1% relative where |s| ~ 2-3,
-    so 1.5% covers it; a wrong or missing term is off by O(100%)."""
+def assert_close_large_values(got, ref, label: str, rtol: float = 1e-2, rel_rms_max: float = 8e-3) -> None:
+    """Bar for gradients of segments of a handful of tokens, which reach past
+    |4|: each element within 2e-2 + rtol |ref| (the default max-abs bar plus
+    a relative term), the whole tensor within mean-abs 2e-3 and relative RMS
+    8e-3.  A bf16 result x carries its own rounding, up to 2^-8 |x| (half a
+    unit in the last place of an 8-bit significand, 0.016 at |x| = 4), and in a
+    short segment it sums only a few terms, each rounded to bf16 with the
+    same relative bound (P, dS, the rotated Q and K); rtol = 1e-2 is about
+    2.6 units of 2^-8."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     err = np.abs(got - ref)
-    big = np.abs(ref) > 4.0
-    small_max = float(err[~big].max()) if (~big).any() else 0.0
-    big_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
-    rel = float(np.sqrt(np.mean((got - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
-    print(f"  {label}: max_abs(|ref|<=4)={small_max:.3e} max_rel(|ref|>4, n={int(big.sum())})={big_rel:.3e} "
-          f"mean_abs={float(err.mean()):.3e} rel_rms={rel:.3e}", flush=True)
+    bar = 2e-2 + rtol * np.abs(ref)
+    worst = float((err / bar).max()) if err.size else 0.0
+    rrms = float(np.sqrt(np.mean((got - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30)) if err.size else 0.0
+    print(f"  {label}: max(err/bar)={worst:.3f} max_abs={float(err.max()) if err.size else 0:.3e} "
+          f"mean_abs={float(err.mean()) if err.size else 0:.3e} rel_rms={rrms:.3e} "
+          f"max|ref|={float(np.abs(ref).max()) if err.size else 0:.3e}", flush=True)
     assert np.isfinite(got).all(), f"{label}: non-finite values"
-    assert small_max <= 2e-2, f"{label}: max-abs {small_max} > 2e-2 where |ref| <= 4"
-    assert big_rel <= rel_large, f"{label}: relative error {big_rel} > {rel_large} where |ref| > 4"
-    assert float(err.mean()) <= 2e-3, f"{label}: mean-abs {float(err.mean())} > 2e-3"
-    assert rel <= rel_rms_max, f"{label}: relative rms {rel} > {rel_rms_max}"
+    assert worst <= 1.0, f"{label}: error {worst:.3f}x (2e-2 + {rtol} |ref|)"
+    assert (float(err.mean()) if err.size else 0.0) <= 2e-3, f"{label}: mean-abs {float(err.mean())} > 2e-3"
+    assert rrms <= rel_rms_max, f"{label}: relative rms {rrms} > {rel_rms_max}"
+
+
+def assert_rel_rms(got, ref, label: str, rel_rms_max: float = 8e-3) -> None:
+    """Relative RMS error at the bf16 level (8e-3, about 4 units of 2^-9)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rrms = float(np.sqrt(np.mean((got - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
+    print(f"  {label}: rel_rms={rrms:.3e} max_abs={float(np.abs(got - ref).max()):.3e} "
+          f"max|ref|={float(np.abs(ref).max()):.3e}", flush=True)
+    assert np.isfinite(got).all(), f"{label}: non-finite values"
+    assert rrms <= rel_rms_max, f"{label}: relative rms {rrms} > {rel_rms_max}"
 
 
 # The attention kernels cover runs of tiny segments with one multi-segment
@@ -167,3 +179,52 @@ class Case:
     def describe(self) -> str:
         return (f"N={self.n} segments={len(self.cu) - 1} H={self.heads} D={self.d} {self.dtype} "
                 f"max_seqlen={self.max_seqlen}" + (" editing" if self.editing else ""))
+
+
+# One head of each XCD's group (heads x, x + 8, x + 16 share an XCD in the
+# attention schedule), spread over the three heads of a group.
+HEADS_PER_XCD = (0, 9, 18, 3, 12, 21, 6, 23)
+
+
+def bench_step(c: Case, backward: bool, theta: float = THETA):
+    """The benchmark's exact call sequence on the case's inputs: the pack on
+    the GPU (its cu_seqlens and positions, checked bit-exact against the
+    oracle's), explicit workspaces, the host segment count, and the rotated
+    buffer the forward fills and the backward reads.  Returns (o, lse) or
+    (o, lse, dq, dk, dv)."""
+    import packed_varlen_attention_amd as mf
+    from packed_varlen_attention_amd.api import attn_workspace
+
+    samples = samples_dev(c.samples)
+    note(f"bench-form pack + fwd{'+bwd' if backward else ''} {c.describe()}")
+    packres = (mf.pack_edit if c.editing else mf.pack)(samples, c.budget)
+    torch.cuda.synchronize()
+    n_packed, n, max_seqlen, max_pos = (int(x) for x in packres.counts.cpu().tolist())
+    assert n == c.n and max_seqlen == c.max_seqlen
+    assert np.array_equal(packres.cu_seqlens.cpu().numpy()[: n_packed + 1], c.cu)
+    nax = 3 if c.editing else 2
+    assert np.array_equal(packres.pos.cpu().numpy()[:n].reshape(-1, nax), c.pos.reshape(-1, nax))
+    o = torch.empty_like(c.tq)
+    lse = torch.empty((c.heads, n), dtype=torch.float32, device="cuda")
+    rot = mf.rotated_buffer(c.tq)
+    ws_f = attn_workspace(c.tq, n_packed, max_pos, False)
+    mf.attn_fwd(c.tq, c.tk, c.tv, packres.cu_seqlens, max_seqlen, packres.pos, theta, max_pos, out=o, lse=lse,
+                workspace=ws_f, n_segments=n_packed, rotated=rot)
+    if not backward:
+        torch.cuda.synchronize()
+        return o, lse
+    ws_b = attn_workspace(c.tq, n_packed, max_pos, True)
+    grads = (torch.empty_like(c.tq), torch.empty_like(c.tk), torch.empty_like(c.tv))
+    mf.attn_bwd(c.tq, c.tk, c.tv, o, lse, c.tdo, packres.cu_seqlens, max_seqlen, packres.pos, theta, max_pos,
+                workspace=ws_b, grads=grads, n_segments=n_packed, rotated=rot)
+    torch.cuda.synchronize()
+    return (o, lse) + grads
+
+
+def oracle_per_head(fn, heads, workers: int = 4):
+    """Evaluate ``fn(h)`` for each head on a few threads (numpy's matrix
+    products and elementwise loops release the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(max_workers=min(workers, len(heads))) as ex:
+        return list(ex.map(fn, heads))

@@ -362,3 +362,26 @@ def test_binding_refuses_another_abi_version(tmp_path):
             B.load_library(str(so))
     finally:
         B._lib = saved
+
+
+def test_binding_checks_the_rotated_buffer():
+    """The ABI passes the rotated buffer as a bare pointer; the binding refuses
+    a wrong dtype, a buffer smaller than 2 * q.numel() elements and one that
+    overlaps another argument, before any call."""
+    import torch
+
+    from packed_varlen_attention_amd import _binding as B
+
+    q = torch.empty((10, 2, 64), dtype=torch.bfloat16)
+    k = torch.empty_like(q)
+    B._check_rotated(None, q, (q, k))
+    B._check_rotated(torch.empty((2,) + tuple(q.shape), dtype=torch.bfloat16), q, (q, k))
+    with pytest.raises(ValueError):
+        B._check_rotated(torch.empty((2,) + tuple(q.shape), dtype=torch.float32), q, (q, k))
+    with pytest.raises(ValueError):
+        B._check_rotated(torch.empty(2 * q.numel() - 1, dtype=torch.bfloat16), q, (q, k))
+    big = torch.empty(4 * q.numel(), dtype=torch.bfloat16)
+    q2 = big[: q.numel()].view(q.shape)
+    with pytest.raises(ValueError):
+        B._check_rotated(big[q.numel() // 2: q.numel() // 2 + 2 * q.numel()], q2, (q2, k))
+    B._check_rotated(big[q.numel(): 3 * q.numel()], q2, (q2, k))

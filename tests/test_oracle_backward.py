@@ -130,3 +130,69 @@ def test_chunking_is_invisible():
     b = oracle.attn_bwd(q, k, v, do, p["cu_seqlens"], pos, THETA, chunk=1000)
     for x, y in zip(a, b):
         assert np.allclose(x, y, atol=1e-13)
+
+
+def _ragged(seed=5, heads=2, d=64):
+    samples = [(7, 3, 5), (1, 0, 0), (20, 4, 4), (0, 2, 9)]
+    p = oracle.pack(samples, 1 << 20)
+    pos = oracle.positions(samples, p["n_packed"])
+    n = p["n_tokens"]
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((n, heads, d)) for _ in range(4))
+    return p["cu_seqlens"], pos, q, k, v, do
+
+
+def test_given_forward_outputs_reduce_to_the_backward():
+    """With the exact O and LSE of attn_fwd, the backward taken as a function
+    of given outputs is attn_bwd (pinned above by finite differences)."""
+    cu, pos, q, k, v, do = _ragged()
+    o, lse = oracle.attn_fwd(q, k, v, cu, pos, THETA)
+    for a, b in zip(oracle.attn_bwd_given(q, k, v, o, lse, do, cu, pos, THETA),
+                    oracle.attn_bwd(q, k, v, do, cu, pos, THETA)):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_given_o_enters_only_through_delta():
+    """Perturbing the given O by E changes Delta by rowsum(dO * E) = c per
+    query and nothing else, so dS moves by -c P: dV is unchanged, dQr moves
+    by -scale * c * (P Kr) (attention with Kr in place of V) and dKr by
+    -scale * P^T (c Qr)."""
+    cu, pos, q, k, v, do = _ragged(6)
+    o, lse = oracle.attn_fwd(q, k, v, cu, pos, THETA)
+    e = np.random.default_rng(7).standard_normal(o.shape) * 1e-3
+    base = oracle.attn_bwd_given(q, k, v, o, lse, do, cu, pos, THETA)
+    moved = oracle.attn_bwd_given(q, k, v, o + e, lse, do, cu, pos, THETA)
+    assert np.allclose(moved[2], base[2], rtol=0, atol=1e-14)
+    sc = 1.0 / np.sqrt(q.shape[2])
+    c = (do * e).sum(axis=2)  # [N][H]
+    qr = oracle.rope_axes(q, pos, THETA)
+    kr = oracle.rope_axes(k, pos, THETA)
+    p_kr, _ = oracle.attn_fwd(q, k, kr, cu, pos, THETA)  # P Kr per query
+    want_dqr = -sc * c[:, :, None] * p_kr
+    got_dqr = oracle.rope_axes(moved[0] - base[0], pos, THETA)  # back to rotated space
+    assert np.allclose(got_dqr, want_dqr, rtol=1e-9, atol=1e-12)
+    # dKr: -scale * sum_q P[q, key] c_q Qr[q]; P^T (c Qr) is attention of the
+    # keys over the queries' weights, computed per segment from the softmax
+    want_dkr = np.zeros_like(q)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        for h in range(q.shape[1]):
+            sco = sc * qr[a:b, h] @ kr[a:b, h].T
+            pm = np.exp(sco - sco.max(axis=1, keepdims=True))
+            pm /= pm.sum(axis=1, keepdims=True)
+            want_dkr[a:b, h] = -sc * pm.T @ (c[a:b, h, None] * qr[a:b, h])
+    got_dkr = oracle.rope_axes(moved[1] - base[1], pos, THETA)
+    assert np.allclose(got_dkr, want_dkr, rtol=1e-9, atol=1e-12)
+
+
+def test_given_lse_scales_the_weights():
+    """Adding a constant t to the given LSE multiplies every weight P by
+    exp(-t); Delta comes from the given O and does not move, so dS, and with
+    it dQ, dK and dV, scale by exactly exp(-t)."""
+    cu, pos, q, k, v, do = _ragged(8)
+    o, lse = oracle.attn_fwd(q, k, v, cu, pos, THETA)
+    t = 0.37
+    base = oracle.attn_bwd_given(q, k, v, o, lse, do, cu, pos, THETA)
+    shifted = oracle.attn_bwd_given(q, k, v, o, lse + t, do, cu, pos, THETA)
+    for a, b in zip(shifted, base):
+        assert np.allclose(a, np.exp(-t) * b, rtol=1e-12, atol=1e-14)
