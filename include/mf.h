@@ -70,11 +70,12 @@ typedef int32_t mf_status;
 #define MF_ERR_UNSUPPORTED (-2)  /* head_dim not 64/128, unknown dtype */
 #define MF_ERR_WORKSPACE (-3)    /* workspace smaller than the size query returns */
 #define MF_ERR_HIP (-4)          /* the HIP runtime reported a launch error */
+#define MF_ERR_SCRATCH (-5)      /* sizes beyond the fixed scratch of mf_varlen_attn_fwd_noalloc */
 
 #define MF_BF16 0
 #define MF_F32 1
 
-#define MF_ABI_VERSION 5
+#define MF_ABI_VERSION 6
 
 /* One sample descriptor: text tokens, then a grid_h x grid_w latent grid. */
 typedef struct mf_sample {
@@ -209,6 +210,39 @@ mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* 
                              int32_t head_dim, float softmax_scale, void* rotated,
                              void* workspace, size_t workspace_bytes, void* stream,
                              mf_trace* trace);
+
+/*
+ * mf_varlen_attn_fwd_noalloc -- mf_varlen_attn_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): it takes no workspace and calls no
+ * allocator.  Its scratch -- the rotary table and the work schedule -- lives
+ * in a fixed 4 MiB array in the library's device image (each GPU the library
+ * runs on holds its own copy until the process ends); the rotated K goes to
+ * the caller's `rotated` buffer.
+ *
+ * Arguments, layouts and results are those of mf_varlen_attn_fwd (2D RoPE),
+ * bit for bit, with these limits:
+ *   dtype     MF_BF16 only (MF_ERR_UNSUPPORTED otherwise: float32 input would
+ *             need bf16 copies of K and V as large as the inputs);
+ *   rotated   required when pos is non-NULL (MF_ERR_INVALID_ARG if NULL);
+ *   sizes     the table, max_pos * head_dim / 4 (cos, sin) float pairs
+ *             rounded up to 256 bytes, plus 4 * n_segments + 3 int32 of
+ *             schedule must fit 4 MiB, else MF_ERR_SCRATCH before any launch
+ *             (at head_dim 128: max_pos up to 8192 with any n_segments the
+ *             ABI accepts).
+ * The array's device address is looked up on the first call on each device,
+ * with the caller's current device; the stream must belong to that device.
+ * Every launch writes the scratch it reads first, so nothing needs clearing;
+ * each call overwrites what the previous one left.  Calls that overlap on one
+ * GPU (concurrent streams, or threads sharing a device) share the array and
+ * race: serialise them.
+ */
+mf_status mf_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
+                                     int32_t max_seqlen, const int32_t* pos, double theta,
+                                     int32_t max_pos, int32_t n_tokens, int32_t n_heads,
+                                     int32_t head_dim, float softmax_scale, void* rotated,
+                                     void* stream, mf_trace* trace);
 
 /*
  * mf_varlen_attn_bwd -- gradients of the attention above with respect to

@@ -33,6 +33,7 @@ EXPORTED = (
     "mf_cfg_combine", "mf_block_workspace_size", "mf_adaln_modulate", "mf_qkv_rope", "mf_out_gated_residual",
     "mf_adaln_modulate_bwd_workspace_size", "mf_adaln_modulate_bwd", "mf_qkv_rope_bwd_workspace_size",
     "mf_qkv_rope_bwd", "mf_out_gated_residual_bwd_workspace_size", "mf_out_gated_residual_bwd",
+    "mf_varlen_attn_fwd_noalloc",
 )
 
 
@@ -86,7 +87,7 @@ class MFError(RuntimeError):
 _lib: Optional[ctypes.CDLL] = None
 
 # MF_ABI_VERSION of include/mf.h that the argument lists below follow.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -124,6 +125,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mf_varlen_attn_fwd.restype = _i32
     lib.mf_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _dbl, _i32,
                                        _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp, _vp]
+    lib.mf_varlen_attn_fwd_noalloc.restype = _i32
+    lib.mf_varlen_attn_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _dbl, _i32,
+                                               _i32, _i32, _i32, _f32, _vp, _vp, _vp]
     lib.mf_varlen_attn_bwd.restype = _i32
     lib.mf_varlen_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                        _vp, _dbl, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp, _vp]
@@ -338,6 +342,21 @@ def mf_varlen_attn_fwd(q, k, v, o, lse, cu_seqlens, n_segments: int, max_seqlen:
                                   _ptr(rotated), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                   _stream(stream), _trace(trace))
     _check(st, name)
+
+
+def mf_varlen_attn_fwd_noalloc(q, k, v, o, lse, cu_seqlens, n_segments: int, max_seqlen: int, pos,
+                               theta: float, max_pos: int, softmax_scale: float, rotated, stream=None,
+                               trace=None) -> None:
+    """The forward without a workspace (2D positions or none; bf16 only)."""
+    n, h, d = q.shape
+    if pos is not None and not (pos.dim() == 2 and pos.shape[1] == 2):
+        raise ValueError("pos must be an int32 [n, 2] tensor")
+    _check_rotated(rotated, q, (q, k, v, o, lse, cu_seqlens, pos))
+    st = lib().mf_varlen_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dtype_code(q),
+                                          _ptr(cu_seqlens), int(n_segments), int(max_seqlen), _ptr(pos),
+                                          float(theta), int(max_pos), int(n), int(h), int(d), float(softmax_scale),
+                                          _ptr(rotated), _stream(stream), _trace(trace))
+    _check(st, "mf_varlen_attn_fwd_noalloc")
 
 
 def mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, n_segments: int, max_seqlen: int,

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "block_kernels.h"
 #include "mf_kernels.h"
 
@@ -136,6 +138,8 @@ const char* mf_status_string(mf_status status) {
       return "workspace too small";
     case MF_ERR_HIP:
       return "HIP runtime error at launch";
+    case MF_ERR_SCRATCH:
+      return "sizes exceed the fixed scratch of the no-allocation call (max_pos or n_segments too large)";
     default:
       return "unknown status";
   }
@@ -269,28 +273,18 @@ size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t 
 
 namespace {
 
-mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
-                        const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
-                        double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
-                        float softmax_scale, void* rotated, void* workspace, size_t workspace_bytes, void* stream,
-                        mf_trace* trace) {
-  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, nax, theta, max_pos, n_tokens,
-                                   n_heads, head_dim, softmax_scale);
-  if (st != MF_OK) return st;
-  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
-  if (!aligned16_or_null(rotated)) return MF_ERR_INVALID_ARG;
-  if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return MF_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MF_ERR_INVALID_ARG;
-  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return MF_ERR_INVALID_ARG;
-  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, n_segments, pos ? max_pos : 0, dtype, false);
-  if (workspace_bytes < w.total) return MF_ERR_WORKSPACE;
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
-
+// The forward's launches, on scratch the caller has carved: tab (the rotary
+// table, when pos is non-null), sched (the schedule, 2 n_segments + 1 ints,
+// then the virtual-segment offsets, 2 (n_segments + 1) ints), kr_ws (a bf16 tensor for the
+// rotated K, used only when the call rotates or converts and `rotated` is
+// null) and vb_ws (a bf16 copy of v, float32 input only).
+mf_status attn_fwd_run(int nax, const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                       const int32_t* cu_seqlens, int32_t n_segments, int32_t max_pos, const int32_t* pos,
+                       double theta, int32_t n_tokens, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                       int32_t max_seqlen, void* rotated, float2* tab, int* sched, void* kr_ws, void* vb_ws,
+                       void* stream, mf_trace* trace) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   Tracer tr(trace, s);
-  char* ws = static_cast<char*>(workspace);
-  float2* tab = reinterpret_cast<float2*>(ws + w.tab_off);
   const void* kr = k;
   const void* vb = v;
   hipError_t e = hipSuccess;
@@ -304,8 +298,7 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
   const bool rot_pass = pos != nullptr || dtype == MF_F32;
   uint16_t* keep = rot_pass ? static_cast<uint16_t*>(rotated) : nullptr;
   if (rot_pass) {
-    void* kdst = keep != nullptr ? static_cast<void*>(keep + rotated_half(n_tokens, n_heads, head_dim))
-                                 : static_cast<void*>(ws + w.kr_off);
+    void* kdst = keep != nullptr ? static_cast<void*>(keep + rotated_half(n_tokens, n_heads, head_dim)) : kr_ws;
     kr = kdst;
     e = tr.run("rope_k", [&] {
       return mf::launch_rope_apply(k, dtype, kdst, MF_BF16, pos, nax, tab, max_pos, n_tokens, n_heads, head_dim,
@@ -314,10 +307,10 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
     if (e != hipSuccess) return MF_ERR_HIP;
   }
   if (dtype == MF_F32) {
-    vb = ws + w.vb_off;
+    vb = vb_ws;
     e = tr.run("convert_v", [&] {
-      return mf::launch_rope_apply(v, dtype, ws + w.vb_off, MF_BF16, nullptr, 2, nullptr, 0, n_tokens, n_heads,
-                                   head_dim, false, false, s);
+      return mf::launch_rope_apply(v, dtype, vb_ws, MF_BF16, nullptr, 2, nullptr, 0, n_tokens, n_heads, head_dim,
+                                   false, false, s);
     });
     if (e != hipSuccess) return MF_ERR_HIP;
   }
@@ -334,7 +327,7 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
   a.tab = tab;
   a.max_pos = max_pos;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
-  a.order = reinterpret_cast<int*>(ws + w.sched_off);
+  a.order = sched;
   a.pt = a.order + n_segments;
   // Multi-segment tiles for runs of tiny segments, when they can hold half of
   // the tokens at all (that needs a mean segment length of at most 256).
@@ -359,6 +352,30 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
   e = tr.run("attn_fwd", [&] { return mf::launch_attn_fwd(a, q, kr, vb, o, lse, s); });
   return from_hip(e);
 }
+
+mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                        const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, const int32_t* pos,
+                        double theta, int32_t max_pos, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                        float softmax_scale, void* rotated, void* workspace, size_t workspace_bytes, void* stream,
+                        mf_trace* trace) {
+  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, nax, theta, max_pos, n_tokens,
+                                   n_heads, head_dim, softmax_scale);
+  if (st != MF_OK) return st;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (!aligned16_or_null(rotated)) return MF_ERR_INVALID_ARG;
+  if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return MF_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MF_ERR_INVALID_ARG;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return MF_ERR_INVALID_ARG;
+  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, n_segments, pos ? max_pos : 0, dtype, false);
+  if (workspace_bytes < w.total) return MF_ERR_WORKSPACE;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  return attn_fwd_run(nax, q, k, v, o, lse, dtype, cu_seqlens, n_segments, max_pos, pos, theta, n_tokens, n_heads,
+                      head_dim, softmax_scale, max_seqlen, rotated, reinterpret_cast<float2*>(ws + w.tab_off),
+                      reinterpret_cast<int*>(ws + w.sched_off), ws + w.kr_off, ws + w.vb_off, stream, trace);
+}
+
 
 mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, int32_t dtype, const int32_t* cu_seqlens,
@@ -503,6 +520,86 @@ mf_status mf_varlen_attn3d_fwd(const void* q, const void* k, const void* v, void
   if (pos == nullptr) return MF_ERR_INVALID_ARG;
   return attn_fwd_impl(3, q, k, v, o, lse, dtype, cu_seqlens, n_segments, max_seqlen, pos, theta, max_pos, n_tokens,
                        n_heads, head_dim, softmax_scale, rotated, workspace, workspace_bytes, stream, trace);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Forward without a workspace, for callers that cannot allocate device
+// memory.  Its scratch (the rotary table and the schedule) lives in a fixed
+// array in this library's device image; each GPU holds its own copy, whose
+// address is looked up once per device, with that device current, on the
+// first call there.  Every launch writes the scratch it reads before reading
+// it, so nothing has to start at zero; the contents left by one call are
+// overwritten by the next.  Calls that overlap on one GPU share the array and
+// race.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr int kScratchDevices = 64;
+
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchDevices];  // device address of `scratch`, per device ordinal
+
+// This device's address of `scratch` (host code may never use the array's
+// name as a device address: it names a host-side stand-in).
+mf_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MF_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kScratchDevices) return MF_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return MF_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mf_status mf_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                                     const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                                     const int32_t* pos, double theta, int32_t max_pos, int32_t n_tokens,
+                                     int32_t n_heads, int32_t head_dim, float softmax_scale, void* rotated,
+                                     void* stream, mf_trace* trace) {
+  mf_status st = check_attn_common(dtype, cu_seqlens, n_segments, max_seqlen, pos, 2, theta, max_pos, n_tokens,
+                                   n_heads, head_dim, softmax_scale);
+  if (st != MF_OK) return st;
+  // float32 input would need bf16 copies of K and V as large as the inputs
+  if (dtype != MF_BF16) return MF_ERR_UNSUPPORTED;
+  if (!trace_ok(trace)) return MF_ERR_INVALID_ARG;
+  if (!aligned16_or_null(rotated)) return MF_ERR_INVALID_ARG;
+  // the rotated K goes to the caller's buffer, never to the scratch
+  if (pos != nullptr && rotated == nullptr) return MF_ERR_INVALID_ARG;
+  if (n_tokens == 0 || n_segments == 0 || max_seqlen == 0) return MF_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return MF_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MF_ERR_INVALID_ARG;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return MF_ERR_INVALID_ARG;
+  const size_t tab_bytes =
+      pos != nullptr ? align_up(static_cast<size_t>(max_pos) * mf::rope_table_width(head_dim, 2) * sizeof(float2))
+                     : 0;
+  const size_t sched_bytes = (4 * static_cast<size_t>(n_segments) + 3) * sizeof(int32_t);
+  if (tab_bytes + sched_bytes > kScratchBytes) return MF_ERR_SCRATCH;
+  void* base = nullptr;
+  st = scratch_address(&base);
+  if (st != MF_OK) return st;
+  char* sp = static_cast<char*>(base);
+  return attn_fwd_run(2, q, k, v, o, lse, dtype, cu_seqlens, n_segments, max_pos, pos, theta, n_tokens, n_heads,
+                      head_dim, softmax_scale, max_seqlen, rotated, reinterpret_cast<float2*>(sp),
+                      reinterpret_cast<int*>(sp + tab_bytes), nullptr, nullptr, stream, trace);
 }
 
 mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

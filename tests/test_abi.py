@@ -42,8 +42,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     import packed_varlen_attention_amd as m
-    assert m.abi_version() == 5 == m._binding.ABI_VERSION
-    for code in (0, -1, -2, -3, -4):
+    assert m.abi_version() == 6 == m._binding.ABI_VERSION
+    for code in (0, -1, -2, -3, -4, -5):
         assert len(m.status_string(code)) > 0
     assert m.status_string(7) == "unknown status"
 
@@ -385,3 +385,19 @@ def test_binding_checks_the_rotated_buffer():
     with pytest.raises(ValueError):
         B._check_rotated(big[q.numel() // 2: q.numel() // 2 + 2 * q.numel()], q2, (q2, k))
     B._check_rotated(big[q.numel(): 3 * q.numel()], q2, (q2, k))
+
+
+def test_noalloc_forward_argument_errors(lib):
+    """The no-allocation forward refuses, before any launch: float32 input,
+    a rotation without the rotated buffer, and a table plus schedule beyond
+    its fixed 4 MiB scratch (MF_ERR_SCRATCH)."""
+    def call(**kw):
+        a = dict(dtype=0, pos=FAKE, max_pos=16, nseg=1, d=128, rot=FAKE)
+        a.update(kw)
+        return lib.mf_varlen_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, a["dtype"], FAKE, a["nseg"], 8, a["pos"],
+                                              10000.0, a["max_pos"], 8, 1, a["d"], 0.0, a["rot"], None, None)
+    assert call(dtype=1) == -2
+    assert call(rot=None) == -1
+    assert call(rot=FAKE + 8) == -1
+    assert call(max_pos=16385) == -5          # 16385 x 256 B of table > 4 MiB
+    assert call(d=96) == -2
