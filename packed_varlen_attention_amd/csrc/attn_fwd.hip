@@ -9,9 +9,11 @@
 // all eight share each K/V tile.  With <= 256 registers per lane each SIMD
 // runs two waves, interleaving their matrix and vector work.  The loop walks
 // the segment's keys in tiles of 64, software-pipelined:
-//   K and V tiles are copied global -> LDS directly (no registers), double-
-//   buffered, with K one tile ahead of V, so the scores of tile j+1 are
-//   computed while the softmax and P V of tile j run; one barrier per tile;
+//   K and V tiles are copied global -> LDS directly (no registers) into
+//   three buffers each, two tiles ahead, each copy a block-uniform tile base
+//   plus a fixed 32-bit lane offset; K runs one tile ahead of V, so the
+//   scores of tile j+1 are computed while the softmax and P V of tile j run;
+//   one barrier per tile;
 //   S^T = K Q^T      32x32x16 bf16 MFMA, Q in registers (rotated at load);
 //   online softmax   per query column, lane-local; the output is rescaled only
 //                    when the running max grows by more than 2^8 (exact: the
@@ -19,7 +21,8 @@
 //   O^T += V^T P^T   32x32x16 bf16 MFMA, V^T read by LDS transpose reads.
 // Computing S^T rather than S puts each query's scores, running max and sum
 // and output accumulator in the same lane, so no shuffles are needed except
-// one max exchange between the two lane halves per tile.
+// one max exchange between the two lane halves per tile (v_permlane32_swap,
+// a register-to-register swap, not a round trip through LDS).
 #include <type_traits>
 
 #include "mf_device.h"
@@ -32,6 +35,17 @@ namespace {
 constexpr int kQT = kFwdTile;  // query rows per workgroup
 constexpr int kKT = 64;        // keys per LDS tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag
+
+// v_permlane32_swap: each lane gets its own value and the one of the lane
+// 32 away (in the same order in both halves).
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <typename T>
 __device__ __forceinline__ void load_q8(const T* p, bool ok, float (&x)[8]) {
@@ -52,11 +66,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     const int* __restrict__ vfirst, uint16_t* __restrict__ qr_out) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kKT * kRowBytes;
-  constexpr int kRowsPerInst = 1024 / kRowBytes;  // rows one wave-wide 16-byte load covers
-  constexpr int kInstPerWave = kKT / kRowsPerInst / 8;
   // LDS: three K and three V tiles, as six separate objects so the compiler
   // can tell the tile being read from the tiles being filled by in-flight
   // copies (otherwise it waits for every copy before each transpose read).
@@ -108,30 +119,13 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     }
   }
 
-  // ---- global -> LDS tile copies (rows past the segment end re-read its
-  // last row; their scores are masked).  Per lane and load: a constant row /
-  // chunk offset inside the tile plus a block-uniform tile base.
   const size_t hD = static_cast<size_t>(heads) * D;
   const uint16_t* kseg = kr + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
   const uint16_t* vseg = vb + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
-  int ld_row[kInstPerWave], ld_off[kInstPerWave];
-#pragma unroll
-  for (int r = 0; r < kInstPerWave; ++r) {
-    const int inst = wave * kInstPerWave + r;
-    ld_row[r] = inst * kRowsPerInst + lane / CH;
-    ld_off[r] = ((lane % CH) ^ Tile<D>::swz(ld_row[r])) * 8;
-  }
+  const TileCopy<D, kKT, 8> copy(wave, lane, static_cast<unsigned>(hD * 2));
   lds_char* const sKb[3] = {(lds_char*)(smemK0), (lds_char*)(smemK1), (lds_char*)(smemK2)};
   lds_char* const sVb[3] = {(lds_char*)(smemV0), (lds_char*)(smemV1), (lds_char*)(smemV2)};
-  auto load_rows = [&](const uint16_t* seg, int k0, lds_char* dst) {
-    const bool tail = k0 + kKT > L;
-#pragma unroll
-    for (int r = 0; r < kInstPerWave; ++r) {
-      const int row = tail ? min(k0 + ld_row[r], L - 1) : k0 + ld_row[r];
-      const uint16_t* src = seg + static_cast<size_t>(row) * hD + ld_off[r];
-      __builtin_amdgcn_global_load_lds(src, dst + (wave * kInstPerWave + r) * 1024, 16, 0, 0);
-    }
-  };
+  auto load_rows = [&](const uint16_t* seg, int k0, lds_char* dst) { copy(seg, k0, L, dst); };
 
   // ---- LDS fragment offsets (bytes), fixed per lane; tile bases add on top.
   int roff[NKK];  // A-operand rows: row perm32(lane % 32), chunk 2kk + h
@@ -239,7 +233,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, scur[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = half_max(mx);
     const float mt = mx * scale_log2;
     if (__any(mt > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mt);
@@ -274,7 +268,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) scur[kb] = snext[kb];
     // Wait for everything but this step's own copies (they complete in order).
-    wait_vmem_keep<2 * kInstPerWave>();
+    wait_vmem_keep<2 * TileCopy<D, kKT, 8>::kCopies>();
     barrier_keep_loads();
   };
   using B0 = std::integral_constant<int, 0>;
@@ -292,7 +286,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   }
   wait_vmem();  // the last step's copies land before the workgroup's LDS is released
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = half_sum(l_run);
   if (qok) {
     const float inv = 1.0f / l_tot;
     TIn* orow = o + qrow * D;
