@@ -34,6 +34,9 @@ namespace {
 
 constexpr int kQT = kFwdTile;  // query rows per workgroup
 constexpr int kKT = 64;        // keys per LDS tile
+constexpr int kWaves = kQT / 32;  // waves per workgroup, 32 query rows each
+constexpr int kWavesPerSimd = 2;  // resident waves per SIMD (sets the register budget)
+constexpr int kKB = kKT / 32;  // 32-key blocks per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag
 
 // v_permlane32_swap: each lane gets its own value and the one of the lane
@@ -58,7 +61,7 @@ __device__ __forceinline__ void load_q8(const T* p, bool ok, float (&x)[8]) {
 }
 
 template <int D, typename TIn, bool kMulti>
-__global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void attn_fwd_kernel(
     const TIn* __restrict__ q, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     TIn* __restrict__ o, float* __restrict__ lse, const int* __restrict__ cu, const int* __restrict__ order,
     const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax,
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   const size_t hD = static_cast<size_t>(heads) * D;
   const uint16_t* kseg = kr + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
   const uint16_t* vseg = vb + static_cast<size_t>(s0) * hD + static_cast<size_t>(head) * D;
-  const TileCopy<D, kKT, 8> copy(wave, lane, static_cast<unsigned>(hD * 2));
+  const TileCopy<D, kKT, kWaves> copy(wave, lane, static_cast<unsigned>(hD * 2));
   lds_char* const sKb[3] = {(lds_char*)(smemK0), (lds_char*)(smemK1), (lds_char*)(smemK2)};
   lds_char* const sVb[3] = {(lds_char*)(smemV0), (lds_char*)(smemV1), (lds_char*)(smemV2)};
   auto load_rows = [&](const uint16_t* seg, int k0, lds_char* dst) { copy(seg, k0, L, dst); };
@@ -141,15 +144,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     coff[db][0] = Tile<D>::off(row0, col >> 3) + ((col >> 2) & 1) * 8;
     coff[db][1] = Tile<D>::off(row0 + 4, col >> 3) + ((col >> 2) & 1) * 8;
   }
-  auto s_tile = [&](const lds_char* sK, f32x16 (&acc)[2]) {
+  auto s_tile = [&](const lds_char* sK, f32x16 (&acc)[kKB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kKB; ++kb) {
         const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
             sK + roff[kk] + kb * 32 * kRowBytes);
         acc[kb] = mfma32(a, qf[kk], acc[kb]);
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
   // V tile j+1), leaving its own in flight across the next step.
   const int ntiles = (L + kKT - 1) / kKT;
   const int last_k0 = (ntiles - 1) * kKT;
-  f32x16 scur[2], snext[2];
+  f32x16 scur[kKB], snext[kKB];
   load_rows(kseg, 0, sKb[0]);
   load_rows(vseg, 0, sVb[0]);
   if (ntiles > 1) load_rows(kseg, kKT, sKb[1]);
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
         int qlo, qhi;
         member_bounds(rcu, f0, f1, s0, s1, min(qi, L - 1), qlo, qhi);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + kb * 32 + acc_row(i, hh);
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
           }
       } else {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (k0 + kb * 32 + acc_row(i, hh) >= L) scur[kb][i] = -INFINITY;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, scur[kb][i]);
     mx = half_max(mx);
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
     // Straight-line region: exp/sum/convert of tile j, S of tile j+1, P V of tile j.
     bf16x8 pf[kKT / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(scur[kb][i], scale_log2, -m_run));
@@ -266,9 +269,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(col_frag(sV, c, db), pf[c], oacc[db]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) scur[kb] = snext[kb];
+    for (int kb = 0; kb < kKB; ++kb) scur[kb] = snext[kb];
     // Wait for everything but this step's own copies (they complete in order).
-    wait_vmem_keep<2 * TileCopy<D, kKT, 8>::kCopies>();
+    wait_vmem_keep<2 * TileCopy<D, kKT, kWaves>::kCopies>();
     barrier_keep_loads();
   };
   using B0 = std::integral_constant<int, 0>;
@@ -310,14 +313,14 @@ hipError_t launch_fwd_t(const AttnArgs& a, const void* q, const void* kr, const 
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   // The ordinary tiles, then (with merged tiny segments) the multi-segment
   // ones; each launch's blocks exit at once on the other kind of item.
-  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, false>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, false>), dim3(static_cast<unsigned>(blocks)), dim3(kWaves * 64), 0, stream,
                      static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
                      static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
                      a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst,
                      static_cast<uint16_t*>(a.qr_out));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.vfirst == nullptr) return e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, true>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, true>), dim3(static_cast<unsigned>(blocks)), dim3(kWaves * 64), 0, stream,
                      static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
                      static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
                      a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst,
