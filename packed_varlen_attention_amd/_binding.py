@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmf.so")
+# MF_LIBRARY selects another build of the same library (e.g. the copy with
+# host sanitizers that build.py --sanitize-host writes); there is no fallback.
+LIB_PATH = os.environ.get("MF_LIBRARY") or os.path.join(_PKG, "libmf.so")
 
 MF_OK = 0
 MF_ERR_INVALID_ARG = -1

@@ -2,6 +2,7 @@
 include/mf.h declares, and rejects bad host arguments before launching
 anything (these calls never reach a kernel, so no GPU is needed)."""
 import ctypes
+import os
 import pathlib
 import re
 
@@ -9,7 +10,8 @@ import pytest
 
 ROOT = pathlib.Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "mf.h"
-LIB = ROOT / "packed_varlen_attention_amd" / "libmf.so"
+# MF_LIBRARY runs these checks against another build (the host-sanitized one).
+LIB = pathlib.Path(os.environ.get("MF_LIBRARY") or ROOT / "packed_varlen_attention_amd" / "libmf.so")
 
 
 def _declared():
