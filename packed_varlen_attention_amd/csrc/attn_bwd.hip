@@ -120,10 +120,11 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     }
 
   const int ntiles = (L + kQB - 1) / kQB;
-  auto step = [&](int j) {
-    const int q0 = j * kQB;
-    const int b = j & 1;
-    if (j + 1 < ntiles) load_tile(q0 + kQB, b ^ 1);
+  // A wave whose 32 keys all lie past the segment's end (short segments)
+  // skips the products; it still copies its share of each tile and meets the
+  // barrier.
+  const bool wave_keys = kbase + wave * 32 < L;
+  auto compute = [&](int q0, int b) {
     const lds_char* sQ = sQ0 + b * kTileBytes;
     const lds_char* sO = sO0 + b * kTileBytes;
     const __attribute__((address_space(3))) float* st =
@@ -169,6 +170,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dkacc[db] = mfma32(col_frag(sQ, c, db), dsb[c], dkacc[db]);
+  };
+  auto step = [&](int j) {
+    const int q0 = j * kQB;
+    const int b = j & 1;
+    if (j + 1 < ntiles) load_tile(q0 + kQB, b ^ 1);
+    if (wave_keys) compute(q0, b);
     wait_vmem();
     __syncthreads();
   };
@@ -244,6 +251,23 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
   int qlo = 0, qhi = L;
   if constexpr (kMulti) member_bounds(rcu, f0, f1, s0, s1, min(qi, L - 1), qlo, qhi);
   const long long qrow = (static_cast<long long>(s0) + min(qi, L - 1)) * heads + head;
+  // Keys this wave's queries can meet (in a multi-segment tile, the union of
+  // their segments; wave-uniform).  Key tiles outside it give this wave
+  // dS = 0 exactly, so it skips their work and only takes part in the copies
+  // and barriers; so does a wave whose 32 query rows all lie past the
+  // segment's end.
+  int wklo = 0, wkhi = L;
+  const bool wave_q = qbase + wave * 32 < L;
+  if constexpr (kMulti) {
+    int lo = qlo, hi = qhi;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off, 64));
+      hi = max(hi, __shfl_xor(hi, off, 64));
+    }
+    wklo = __builtin_amdgcn_readfirstlane(lo);
+    wkhi = __builtin_amdgcn_readfirstlane(hi);
+  }
 
   bf16x8 qf[NKK], df[NKK];
 #pragma unroll
@@ -325,10 +349,9 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
   // only for those issued before it; b = j % 3 is compile-time.
   const int ntiles = (L + kKT - 1) / kKT;
   const int last_k0 = (ntiles - 1) * kKT;
-  auto step = [&](int j, auto buf_tag) {
+  // The work of one key tile: S^T and dP^T, dS, dQ^T += Kr^T dS^T.
+  auto compute = [&](int k0, auto buf_tag) {
     constexpr int b = decltype(buf_tag)::value;
-    const int k0 = j * kKT;
-    load_tile(min(k0 + 2 * kKT, last_k0), sKb[(b + 2) % 3], sVb[(b + 2) % 3]);
     const lds_char* sK = sKb[b];
     const lds_char* sV = sVb[b];
     bf16x8 dsb[kKT / 16];
@@ -366,6 +389,12 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
     for (int c = 0; c < kKT / 16; ++c)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(col_frag(sK, c, db), dsb[c], dqacc[db]);
+  };
+  auto step = [&](int j, auto buf_tag) {
+    constexpr int b = decltype(buf_tag)::value;
+    const int k0 = j * kKT;
+    load_tile(min(k0 + 2 * kKT, last_k0), sKb[(b + 2) % 3], sVb[(b + 2) % 3]);
+    if (wave_q && (!kMulti || (k0 < wkhi && k0 + kKT > wklo))) compute(k0, buf_tag);
     wait_vmem_keep<2 * kInstPerWave>();
     barrier_keep_loads();
   };

@@ -203,15 +203,13 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void attn_fwd_kernel(
   // One pipeline step: softmax + P V of tile j, scores of tile j + 1.  Only
   // the last tile masks keys; that branch and the rescale branch are rare.
   // b (= j % 3) is compile-time, so every LDS address names its buffer
-  // statically.
-  auto step = [&](int j, auto buf_tag) {
+  // statically.  A wave whose 32 query rows all lie past the segment's end
+  // (short segments, a segment's last tile) skips this work; it still issues
+  // its copies and meets every barrier.
+  const bool wave_q = qbase + wave * 32 < L;
+  auto compute = [&](int j, auto buf_tag) {
     constexpr int b = decltype(buf_tag)::value;
     const int k0 = j * kKT;
-    // Every step issues both copies, so the wait below has a fixed count;
-    // past the end they re-read the last tile into buffers no later step
-    // reads.
-    load_rows(kseg, min(k0 + 3 * kKT, last_k0), sKb[b]);
-    load_rows(vseg, min(k0 + 2 * kKT, last_k0), sVb[(b + 2) % 3]);
     if (kMulti || k0 + kKT > L) {  // keys past the segment's end, or outside the query's segment
       if constexpr (kMulti) {
         int qlo, qhi;
@@ -270,6 +268,16 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void attn_fwd_kernel(
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(col_frag(sV, c, db), pf[c], oacc[db]);
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) scur[kb] = snext[kb];
+  };
+  auto step = [&](int j, auto buf_tag) {
+    constexpr int b = decltype(buf_tag)::value;
+    const int k0 = j * kKT;
+    // Every step issues both copies, so the wait below has a fixed count;
+    // past the end they re-read the last tile into buffers no later step
+    // reads.
+    load_rows(kseg, min(k0 + 3 * kKT, last_k0), sKb[b]);
+    load_rows(vseg, min(k0 + 2 * kKT, last_k0), sVb[(b + 2) % 3]);
+    if (wave_q) compute(j, buf_tag);
     // Wait for everything but this step's own copies (they complete in order).
     wait_vmem_keep<2 * TileCopy<D, kKT, kWaves>::kCopies>();
     barrier_keep_loads();
