@@ -120,10 +120,10 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
     }
 
   const int ntiles = (L + kQB - 1) / kQB;
-  // A wave whose 32 keys all lie past the segment's end (short segments)
-  // skips the products; it still copies its share of each tile and meets the
-  // barrier.
-  const bool wave_keys = kbase + wave * 32 < L;
+  // In a segment that fits one workgroup, a wave whose 32 keys all lie past
+  // the segment's end skips the products; it still copies its share of each
+  // tile and meets the barrier.
+  const bool wave_keys = kbase + wave * 32 < L || L > kKB;
   auto compute = [&](int q0, int b) {
     const lds_char* sQ = sQ0 + b * kTileBytes;
     const lds_char* sO = sO0 + b * kTileBytes;
@@ -254,10 +254,11 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
   // Keys this wave's queries can meet (in a multi-segment tile, the union of
   // their segments; wave-uniform).  Key tiles outside it give this wave
   // dS = 0 exactly, so it skips their work and only takes part in the copies
-  // and barriers; so does a wave whose 32 query rows all lie past the
-  // segment's end.
+  // and barriers; so does, in a segment that fits one query tile, a wave
+  // whose 32 query rows all lie past the segment's end (longer segments keep
+  // such waves busy, as the forward does, to keep their tiles in step).
   int wklo = 0, wkhi = L;
-  const bool wave_q = qbase + wave * 32 < L;
+  const bool wave_q = qbase + wave * 32 < L || L > kQT;
   if constexpr (kMulti) {
     int lo = qlo, hi = qhi;
 #pragma unroll

@@ -203,10 +203,13 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void attn_fwd_kernel(
   // One pipeline step: softmax + P V of tile j, scores of tile j + 1.  Only
   // the last tile masks keys; that branch and the rescale branch are rare.
   // b (= j % 3) is compile-time, so every LDS address names its buffer
-  // statically.  A wave whose 32 query rows all lie past the segment's end
-  // (short segments, a segment's last tile) skips this work; it still issues
-  // its copies and meets every barrier.
-  const bool wave_q = qbase + wave * 32 < L;
+  // statically.  In a segment that fits one query tile, a wave whose 32
+  // query rows all lie past the segment's end skips this work; it still
+  // issues its copies and meets every barrier.  Longer segments keep their
+  // idle waves busy: a last tile that finished early would start the next
+  // (segment, head) sooner and break the XCD's shared sweep over K and V
+  // (measured: 24% more HBM fetch on a pack of long segments, same time).
+  const bool wave_q = qbase + wave * 32 < L || L > kQT;
   auto compute = [&](int j, auto buf_tag) {
     constexpr int b = decltype(buf_tag)::value;
     const int k0 = j * kKT;
