@@ -46,6 +46,32 @@ def test_small_packs_all_elements(dtype, d):
     assert_close(host_f64(dv)[:n], rv[:n], G_MAX, G_MEAN, f"dV {dtype} D{d}")
 
 
+# Segment lengths around the tile sizes: one forward / dq query tile holds
+# 256 rows and one dkdv workgroup 128 keys.  In a segment that fits one such
+# tile, waves whose rows (keys) all lie past the end skip their products; at
+# 257 and beyond they do not.  Every element is checked either way.
+TILE_EDGES = [(127, 0, 0), (128, 0, 0), (129, 0, 0), (224, 0, 0), (225, 0, 0), (31, 0, 0), (255, 0, 0),
+              (256, 0, 0), (257, 0, 0), (288, 0, 0), (16, 15, 16), (1, 16, 16)]
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_segments_at_tile_edges(d):
+    c = Case(TILE_EDGES, 1 << 20, 3, d, "bf16", seed=37, with_dout=True)
+    mf = _mf()
+    note(f"mf_varlen_attn_fwd+bwd tile edges {c.describe()}")
+    o, lse = mf.attn_fwd(c.tq, c.tk, c.tv, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    dq, dk, dv = mf.attn_bwd(c.tq, c.tk, c.tv, o, lse, c.tdo, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_fwd(c.q, c.k, c.v, c.cu, c.pos, THETA)
+    rq, rk, rv = oracle.attn_bwd(c.q, c.k, c.v, c.do, c.cu, c.pos, THETA)
+    n = c.n
+    assert_close(host_f64(o)[:n], ro[:n], 2e-2, 2e-3, f"O D{d}")
+    assert_close(host_f64(lse)[:, :n], rl[:, :n], 1e-2, 1e-2, f"LSE D{d}")
+    assert_close(host_f64(dq)[:n], rq[:n], G_MAX, G_MEAN, f"dQ D{d}")
+    assert_close(host_f64(dk)[:n], rk[:n], G_MAX, G_MEAN, f"dK D{d}")
+    assert_close(host_f64(dv)[:n], rv[:n], G_MAX, G_MEAN, f"dV D{d}")
+
+
 def test_tiny_workload():
     w = workloads.tiny()
     c = Case(w.samples, w.budget, w.n_heads, w.head_dim, w.dtype, w.seed, with_dout=True)
