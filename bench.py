@@ -43,8 +43,8 @@ KERNEL_SOURCE = {
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed50k", choices=["mixed50k", "cfg1024", "stress", "edit50k", "captions"],
                     help="bench line workload (mixed50k is the metric's; others for exploration; edit50k runs "
                          "the editing path with frame-aware 3D RoPE)")
