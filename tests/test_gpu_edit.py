@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import THETA, Case, assert_close, dev, host_f64, merged_segments, note, samples_dev
+from gpu_util import (HEADS_PER_XCD, THETA, Case, assert_close, bench_step, dev, host_f64, merged_segments, note,
+                      oracle_per_head, samples_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -188,27 +189,37 @@ def test_frame_axis_changes_the_result_and_segments_stay_local():
 
 
 def test_edit50k_full_size():
-    """The edit50k pack at full size in the benchmark's launch configuration:
-    forward on sampled rows, backward on one full head."""
+    """The edit50k pack at full size through the benchmark's exact call (GPU
+    pack, explicit workspaces, host segment count, the rotated buffer the
+    forward fills and the backward reads): every element of O and LSE for one
+    head of each XCD's group of heads, and every element of dQ, dK and dV for
+    the same heads."""
     w = workloads.edit50k()
     c = Case(w.samples, w.budget, w.n_heads, w.head_dim, w.dtype, w.seed, with_dout=True, editing=True)
-    o, lse = _fwd(c)
-    rng = np.random.default_rng(6)
-    rows = []
-    for s in range(len(c.cu) - 1):
-        a, b = int(c.cu[s]), int(c.cu[s + 1])
-        rows += [(a, int(rng.integers(0, c.heads))), (b - 1, int(rng.integers(0, c.heads)))]
-    rows += [(int(rng.integers(0, c.n)), int(rng.integers(0, c.heads))) for _ in range(200)]
-    ref_o, ref_l = oracle.attn_fwd_rows(c.q, c.k, c.v, c.cu, c.pos, rows, THETA)
-    t = torch.tensor([r[0] for r in rows]).cuda()
-    hd = torch.tensor([r[1] for r in rows]).cuda()
-    assert_close(host_f64(o[t, hd]), ref_o, O_MAX, O_MEAN, "O edit50k sampled")
-    assert_close(host_f64(lse[hd, t]), ref_l, LSE_MAX, LSE_MAX, "LSE edit50k sampled")
-    dq, dk, dv = _fwd_bwd(c)
-    h = 5
-    note(f"oracle 3D backward head {h}")
-    sl = slice(h, h + 1)
-    rq, rk, rv = oracle.attn_bwd(c.q[:, sl], c.k[:, sl], c.v[:, sl], c.do[:, sl], c.cu, c.pos, THETA)
-    assert_close(host_f64(dq[:, sl]), rq, O_MAX, O_MEAN, "dQ edit50k head 5")
-    assert_close(host_f64(dk[:, sl]), rk, O_MAX, O_MEAN, "dK edit50k head 5")
-    assert_close(host_f64(dv[:, sl]), rv, O_MAX, O_MEAN, "dV edit50k head 5")
+    o, lse, dq, dk, dv = bench_step(c, backward=True)
+    n = c.n
+
+    def ref_fwd(h):
+        sl = slice(h, h + 1)
+        return oracle.attn_fwd(c.q[:, sl], c.k[:, sl], c.v[:, sl], c.cu, c.pos, THETA)
+
+    note(f"oracle 3D forward, heads {HEADS_PER_XCD}")
+    refs = oracle_per_head(ref_fwd, HEADS_PER_XCD)
+    got_o, got_l = host_f64(o), host_f64(lse)
+    for h, (ro, rl) in zip(HEADS_PER_XCD, refs):
+        assert_close(got_o[:n, h:h + 1], ro[:n], O_MAX, O_MEAN, f"O edit50k head {h}")
+        assert_close(got_l[h:h + 1, :n], rl[:, :n], LSE_MAX, LSE_MAX, f"LSE edit50k head {h}")
+
+    bwd_heads = HEADS_PER_XCD
+
+    def ref_bwd(h):
+        sl = slice(h, h + 1)
+        return oracle.attn_bwd(c.q[:, sl], c.k[:, sl], c.v[:, sl], c.do[:, sl], c.cu, c.pos, THETA)
+
+    note(f"oracle 3D backward, heads {bwd_heads}")
+    grefs = oracle_per_head(ref_bwd, bwd_heads)
+    gq, gk, gv = host_f64(dq), host_f64(dk), host_f64(dv)
+    for h, (rq, rk, rv) in zip(bwd_heads, grefs):
+        assert_close(gq[:n, h:h + 1], rq[:n], O_MAX, O_MEAN, f"dQ edit50k head {h}")
+        assert_close(gk[:n, h:h + 1], rk[:n], O_MAX, O_MEAN, f"dK edit50k head {h}")
+        assert_close(gv[:n, h:h + 1], rv[:n], O_MAX, O_MEAN, f"dV edit50k head {h}")
