@@ -542,8 +542,8 @@ def main():
     lse = torch.empty((H, N), dtype=torch.float32, device=dev)
     grads = (torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv))
     from packed_varlen_attention_amd.api import attn_workspace
-    ws_f = attn_workspace(tq, n_packed, max_pos, False)
-    ws_b = attn_workspace(tq, n_packed, max_pos, True)
+    ws_f = attn_workspace(tq, n_packed, max_pos, False, rotated=True)
+    ws_b = attn_workspace(tq, n_packed, max_pos, True, rotated=True)
     # the forward keeps its rotated bf16 Q and K here for the backward, as a
     # training step keeps activations
     rot = mf.rotated_buffer(tq)

@@ -75,7 +75,7 @@ typedef int32_t mf_status;
 #define MF_BF16 0
 #define MF_F32 1
 
-#define MF_ABI_VERSION 6
+#define MF_ABI_VERSION 7
 
 /* One sample descriptor: text tokens, then a grid_h x grid_w latent grid. */
 typedef struct mf_sample {
@@ -169,10 +169,20 @@ mf_status mf_rope2d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_
                           int32_t inverse, void* workspace, size_t workspace_bytes,
                           void* stream, mf_trace* trace);
 
-/* Bytes of workspace the attention calls need (backward != 0: backward). */
+/*
+ * Bytes of workspace the attention calls need.  flags: MF_WS_BACKWARD for
+ * the backward call (else the forward); MF_WS_ROTATED when the call will be
+ * given a `rotated` buffer, which then holds the rotated Q and K and the
+ * workspace reserves no copies of its own (2 * n_tokens * n_heads *
+ * head_dim * 2 bytes less for the backward, half that for the forward).  A
+ * call given `rotated` accepts either size; one given none needs the size
+ * queried without MF_WS_ROTATED.  Any other flag bit returns 0.
+ */
+#define MF_WS_BACKWARD 1
+#define MF_WS_ROTATED 2
 size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim,
                                      int32_t n_segments, int32_t max_pos, int32_t dtype,
-                                     int32_t backward);
+                                     int32_t flags);
 
 /*
  * mf_varlen_attn_fwd -- block-diagonal multi-head attention over packed
@@ -201,7 +211,8 @@ size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t 
  *              rounded to bf16.  In the Q half, rows outside every segment
  *              are not written; the K half is written for every row in
  *              [0, n_tokens).  It must not overlap any other argument.
- * workspace    >= mf_varlen_attn_workspace_size(..., backward = 0) bytes.
+ * workspace    >= mf_varlen_attn_workspace_size(...) bytes for the forward
+ *              (MF_WS_ROTATED may be set when `rotated` is non-NULL).
  */
 mf_status mf_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                              int32_t dtype, const int32_t* cu_seqlens, int32_t n_segments,
@@ -262,7 +273,8 @@ mf_status mf_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v
  *              there instead, which skips two passes over Q and K; the
  *              results are bit-identical to those with NULL.  Otherwise
  *              it is ignored.
- * workspace    >= mf_varlen_attn_workspace_size(..., backward = 1) bytes.
+ * workspace    >= mf_varlen_attn_workspace_size(...) bytes for the backward
+ *              (MF_WS_BACKWARD; MF_WS_ROTATED may be set when `rotated` is non-NULL).
  */
 mf_status mf_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, void* dq, void* dk, void* dv,

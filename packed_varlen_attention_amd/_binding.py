@@ -89,7 +89,11 @@ class MFError(RuntimeError):
 _lib: Optional[ctypes.CDLL] = None
 
 # MF_ABI_VERSION of include/mf.h that the argument lists below follow.
-ABI_VERSION = 6
+ABI_VERSION = 7
+
+# Flags of mf_varlen_attn_workspace_size.
+WS_BACKWARD = 1
+WS_ROTATED = 2
 
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -289,10 +293,11 @@ def mf_rope3d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: i
 
 
 def mf_varlen_attn_workspace_size(n_tokens: int, n_heads: int, head_dim: int, n_segments: int,
-                                  max_pos: int, dtype: int, backward: bool) -> int:
+                                  max_pos: int, dtype: int, backward: bool, rotated: bool = False) -> int:
+    """rotated: the call will be given a rotated buffer (no rotation copies reserved)."""
+    flags = (WS_BACKWARD if backward else 0) | (WS_ROTATED if rotated else 0)
     return int(lib().mf_varlen_attn_workspace_size(int(n_tokens), int(n_heads), int(head_dim),
-                                                   int(n_segments), int(max_pos), int(dtype),
-                                                   int(bool(backward))))
+                                                   int(n_segments), int(max_pos), int(dtype), flags))
 
 
 def _entry(pos, which: str):

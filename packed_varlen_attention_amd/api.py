@@ -77,9 +77,13 @@ def rope2d_apply(x: torch.Tensor, pos: torch.Tensor, theta: float, max_pos: int,
     return x
 
 
-def attn_workspace(q: torch.Tensor, n_segments: int, max_pos: int, backward: bool) -> torch.Tensor:
+def attn_workspace(q: torch.Tensor, n_segments: int, max_pos: int, backward: bool,
+                   rotated: bool = False) -> torch.Tensor:
+    """Workspace for attn_fwd (backward=False) or attn_bwd; rotated=True when the
+    call will be given a rotated buffer, which then holds the rotated Q and K
+    (the workspace reserves no copies of them)."""
     n, h, d = q.shape
-    size = B.mf_varlen_attn_workspace_size(n, h, d, n_segments, max_pos, B.dtype_code(q), backward)
+    size = B.mf_varlen_attn_workspace_size(n, h, d, n_segments, max_pos, B.dtype_code(q), backward, rotated)
     return torch.empty(max(size, 1), dtype=torch.uint8, device=q.device)
 
 
@@ -96,7 +100,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
     if with_lse and lse is None:
         lse = torch.empty((h, n), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, False)
+        workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, False, rotated is not None)
     B.mf_varlen_attn_fwd(q, k, v, o, lse if with_lse else None, cu_seqlens, nseg, max_seqlen, pos, theta,
                          max_pos, softmax_scale, workspace, stream, trace, rotated)
     return o, (lse if with_lse else None)
@@ -114,7 +118,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
     if workspace is None:
-        workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, True)
+        workspace = attn_workspace(q, nseg, max_pos if pos is not None else 0, True, rotated is not None)
     B.mf_varlen_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nseg, max_seqlen, pos, theta, max_pos,
                          softmax_scale, workspace, stream, trace, rotated)
     return dq, dk, dv

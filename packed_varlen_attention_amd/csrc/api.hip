@@ -70,7 +70,7 @@ struct AttnWorkspace {
 };
 
 AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
-                             int32_t max_pos, int32_t dtype, bool backward) {
+                             int32_t max_pos, int32_t dtype, bool backward, bool kept) {
   AttnWorkspace w;
   // schedules (order, tile prefix): one for the forward; dkdv's and dq's for
   // the backward; then the virtual segments (offsets, first segment) that
@@ -80,8 +80,10 @@ AttnWorkspace attn_workspace(int32_t n_tokens, int32_t n_heads, int32_t head_dim
   const size_t tensor_bf16 = static_cast<size_t>(n_tokens) * n_heads * head_dim * 2;
   // rotary table, sized for the wider (3-axis) layout so one size serves both
   w.tab = static_cast<size_t>(max_pos > 0 ? max_pos : 0) * mf::rope_table_width(head_dim, 3) * sizeof(float2);
-  w.kr = tensor_bf16;  // rotated (or converted) K
-  w.qr = backward ? tensor_bf16 : 0;
+  // rotated (or converted) K, and Q for the backward; none when the caller's
+  // `rotated` buffer holds them
+  w.kr = kept ? 0 : tensor_bf16;
+  w.qr = (backward && !kept) ? tensor_bf16 : 0;
   w.vb = dtype == MF_F32 ? tensor_bf16 : 0;
   w.dob = (backward && dtype == MF_F32) ? tensor_bf16 : 0;
   w.delta = backward ? 2 * static_cast<size_t>(n_tokens) * n_heads * sizeof(float) : 0;  // delta, lse2
@@ -263,10 +265,13 @@ mf_status mf_rope3d_apply(void* x, int32_t dtype, const int32_t* pos, int32_t n_
 }
 
 size_t mf_varlen_attn_workspace_size(int32_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_segments,
-                                     int32_t max_pos, int32_t dtype, int32_t backward) {
+                                     int32_t max_pos, int32_t dtype, int32_t flags) {
   if (n_tokens < 0 || n_heads < 1 || (head_dim != 64 && head_dim != 128)) return 0;
   if (n_segments < 0) return 0;
-  return attn_workspace(n_tokens, n_heads, head_dim, n_segments, max_pos, dtype, backward != 0).total;
+  if ((flags & ~(MF_WS_BACKWARD | MF_WS_ROTATED)) != 0) return 0;
+  return attn_workspace(n_tokens, n_heads, head_dim, n_segments, max_pos, dtype, (flags & MF_WS_BACKWARD) != 0,
+                        (flags & MF_WS_ROTATED) != 0)
+      .total;
 }
 
 }  // extern "C"
@@ -367,7 +372,8 @@ mf_status attn_fwd_impl(int nax, const void* q, const void* k, const void* v, vo
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return MF_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MF_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return MF_ERR_INVALID_ARG;
-  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, n_segments, pos ? max_pos : 0, dtype, false);
+  const AttnWorkspace w =
+      attn_workspace(n_tokens, n_heads, head_dim, n_segments, pos ? max_pos : 0, dtype, false, rotated != nullptr);
   if (workspace_bytes < w.total) return MF_ERR_WORKSPACE;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
   char* ws = static_cast<char*>(workspace);
@@ -395,7 +401,8 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return MF_ERR_INVALID_ARG;
-  const AttnWorkspace w = attn_workspace(n_tokens, n_heads, head_dim, n_segments, pos ? max_pos : 0, dtype, true);
+  const AttnWorkspace w =
+      attn_workspace(n_tokens, n_heads, head_dim, n_segments, pos ? max_pos : 0, dtype, true, rotated != nullptr);
   if (workspace_bytes < w.total) return MF_ERR_WORKSPACE;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MF_ERR_INVALID_ARG;
 

@@ -207,13 +207,13 @@ def bench_step(c: Case, backward: bool, theta: float = THETA):
     o = torch.empty_like(c.tq)
     lse = torch.empty((c.heads, n), dtype=torch.float32, device="cuda")
     rot = mf.rotated_buffer(c.tq)
-    ws_f = attn_workspace(c.tq, n_packed, max_pos, False)
+    ws_f = attn_workspace(c.tq, n_packed, max_pos, False, rotated=True)
     mf.attn_fwd(c.tq, c.tk, c.tv, packres.cu_seqlens, max_seqlen, packres.pos, theta, max_pos, out=o, lse=lse,
                 workspace=ws_f, n_segments=n_packed, rotated=rot)
     if not backward:
         torch.cuda.synchronize()
         return o, lse
-    ws_b = attn_workspace(c.tq, n_packed, max_pos, True)
+    ws_b = attn_workspace(c.tq, n_packed, max_pos, True, rotated=True)
     grads = (torch.empty_like(c.tq), torch.empty_like(c.tk), torch.empty_like(c.tv))
     mf.attn_bwd(c.tq, c.tk, c.tv, o, lse, c.tdo, packres.cu_seqlens, max_seqlen, packres.pos, theta, max_pos,
                 workspace=ws_b, grads=grads, n_segments=n_packed, rotated=rot)

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     import packed_varlen_attention_amd as m
-    assert m.abi_version() == 6 == m._binding.ABI_VERSION
+    assert m.abi_version() == 7 == m._binding.ABI_VERSION
     for code in (0, -1, -2, -3, -4, -5):
         assert len(m.status_string(code)) > 0
     assert m.status_string(7) == "unknown status"
@@ -134,6 +134,48 @@ def test_workspace_sizes(lib):
     assert fwd_bf16 % 256 == 0 and bwd_bf16 % 256 == 0
     assert lib.mf_varlen_attn_workspace_size(n, h, 96, 3, 640, 0, 0) == 0
     assert lib.mf_rope2d_workspace_size(128, 640) == table
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_without_rotation_copies(lib):
+    # MF_WS_ROTATED (2) leaves out the rotated K (forward) and the rotated Q
+    # and K (backward): the caller's `rotated` buffer holds them
+    n, h, d = 1000, 4, 128
+    tensor = _align(n * h * d * 2)
+    for dtype in (0, 1):
+        fwd = lib.mf_varlen_attn_workspace_size(n, h, d, 3, 640, dtype, 0)
+        bwd = lib.mf_varlen_attn_workspace_size(n, h, d, 3, 640, dtype, 1)
+        assert lib.mf_varlen_attn_workspace_size(n, h, d, 3, 640, dtype, 2) == fwd - tensor
+        assert lib.mf_varlen_attn_workspace_size(n, h, d, 3, 640, dtype, 3) == bwd - 2 * tensor
+    for bad in (4, 8, -1, 1 << 30):
+        assert lib.mf_varlen_attn_workspace_size(n, h, d, 3, 640, 0, bad) == 0
+
+
+def test_calls_accept_the_smaller_workspace_only_with_rotated(lib):
+    # The size check comes before the null-workspace check, so ws=None tells
+    # the two apart without launching: -3 = too small, -1 = size accepted.
+    fa = dict(n=8, h=1, d=128, nseg=1, max_pos=16)
+    fwd_full = lib.mf_varlen_attn_workspace_size(8, 1, 128, 1, 16, 0, 0)
+    fwd_small = lib.mf_varlen_attn_workspace_size(8, 1, 128, 1, 16, 0, 2)
+    assert fwd_small < fwd_full
+    assert _fwd(lib, ws=None, wsb=fwd_small, rot=FAKE, **fa) == -1
+    assert _fwd(lib, ws=None, wsb=fwd_small - 1, rot=FAKE, **fa) == -3
+    assert _fwd(lib, ws=None, wsb=fwd_small, rot=None, **fa) == -3
+    assert _fwd(lib, ws=None, wsb=fwd_full, rot=None, **fa) == -1
+
+    def bwd(wsb, rot):
+        return lib.mf_varlen_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 8, FAKE,
+                                      1e4, 16, 8, 2, 64, 0.0, rot, None, wsb, None, None)
+    bwd_full = lib.mf_varlen_attn_workspace_size(8, 2, 64, 1, 16, 0, 1)
+    bwd_small = lib.mf_varlen_attn_workspace_size(8, 2, 64, 1, 16, 0, 3)
+    assert bwd_small == bwd_full - 2 * _align(8 * 2 * 64 * 2)
+    assert bwd(bwd_small, FAKE) == -1
+    assert bwd(bwd_small - 1, FAKE) == -3
+    assert bwd(bwd_small, None) == -3
+    assert bwd(bwd_full, None) == -1
 
 
 def test_probe_argument_errors(lib):
