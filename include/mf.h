@@ -20,9 +20,10 @@
  *
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers owned by the caller.  Inputs are
- *     const; outputs are written only where documented.  The library keeps
- *     no global state and never allocates device memory: scratch space comes
- *     from the caller's `workspace`.
+ *     const; outputs are written only where documented.  The library never
+ *     allocates device memory: scratch space comes from the caller's
+ *     `workspace`.  Its only global state is the fixed scratch array of
+ *     mf_varlen_attn_fwd_noalloc and that array's address on each device.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and never synchronises.  Calls
  *     make no allocation, copy, memset or host synchronisation, so a
