@@ -4,11 +4,12 @@
 // concatenated text and image tokens; samples packed into one stream never
 // attend to each other).
 //
-// One workgroup = 8 waves = 256 query rows of one (segment, head), taken from
+// One workgroup = 4 waves = 128 query rows of one (segment, head), taken from
 // the longest-first, XCD-grouped schedule; each wave owns 32 query rows and
-// all eight share each K/V tile.  With <= 256 registers per lane each SIMD
-// runs two waves, interleaving their matrix and vector work.  The loop walks
-// the segment's keys in tiles of 64, software-pipelined:
+// all four share each K/V tile.  With <= 168 registers per lane and 48 KB of
+// LDS per workgroup, three workgroups share a CU, so each SIMD runs three
+// waves and interleaves their matrix, vector and LDS work.  The loop walks
+// the segment's keys in tiles of 32, software-pipelined:
 //   K and V tiles are copied global -> LDS directly (no registers) into
 //   three buffers each, two tiles ahead, each copy a block-uniform tile base
 //   plus a fixed 32-bit lane offset; K runs one tile ahead of V, so the
@@ -33,9 +34,9 @@ namespace mf {
 namespace {
 
 constexpr int kQT = kFwdTile;  // query rows per workgroup
-constexpr int kKT = 64;        // keys per LDS tile
+constexpr int kKT = 32;        // keys per LDS tile
 constexpr int kWaves = kQT / 32;  // waves per workgroup, 32 query rows each
-constexpr int kWavesPerSimd = 2;  // resident waves per SIMD (sets the register budget)
+constexpr int kWavesPerSimd = 3;  // resident waves per SIMD (sets the register budget)
 constexpr int kKB = kKT / 32;  // 32-key blocks per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag
 

@@ -42,7 +42,7 @@ hipError_t launch_merge_tiny(const int* cu_seqlens, int n_segments, int n_tokens
 // Blocks to launch for a schedule with the given tile size (an upper bound).
 long long sched_grid(int n_tokens, int n_segments, int heads, int tile);
 
-constexpr int kFwdTile = 256;   // query rows per forward workgroup (8 waves)
+constexpr int kFwdTile = 128;   // query rows per forward workgroup (4 waves)
 constexpr int kDqTile = 256;    // query rows per dq workgroup (8 waves)
 constexpr int kDkdvTile = 128;  // keys per dkdv workgroup
 

@@ -91,8 +91,8 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* __restrict__
 
 // Multi-segment tiles.  Tiny segments (at most kTinyLen tokens) that follow
 // one another in the stream and start in the same kTinyLen-token window of it
-// form one virtual segment, which the attention kernels cover with a single
-// tile and a per-lane block-diagonal mask.  Such a group spans at most
+// form one virtual segment, which the attention kernels cover with one or
+// two query tiles and a per-lane block-diagonal mask.  Such a group spans at most
 // 2 kTinyLen - 1 tokens (its last member starts inside the window and is at
 // most kTinyLen long); every other segment is a virtual segment of its own.
 // vcu[v] = first token of virtual segment v and vfirst[v] = its first

@@ -51,7 +51,8 @@ def test_small_packs_all_elements(dtype, d):
 # tile, waves whose rows (keys) all lie past the end skip their products; at
 # 257 and beyond they do not.  Every element is checked either way.
 TILE_EDGES = [(127, 0, 0), (128, 0, 0), (129, 0, 0), (224, 0, 0), (225, 0, 0), (31, 0, 0), (255, 0, 0),
-              (256, 0, 0), (257, 0, 0), (288, 0, 0), (16, 15, 16), (1, 16, 16)]
+              (256, 0, 0), (257, 0, 0), (288, 0, 0), (16, 15, 16), (1, 16, 16), (32, 0, 0), (33, 0, 0),
+              (64, 0, 0), (65, 0, 0)]
 
 
 @pytest.mark.parametrize("d", [128, 64])
