@@ -468,7 +468,8 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
   a.order = reinterpret_cast<int*>(ws + w.sched_off);
   a.pt = a.order + n_segments;
-  // dkdv walks key tiles of kDkdvTile, dq query tiles of kDqTile: one schedule each.
+  // dkdv walks key tiles of kDkdvTile, dq query tiles of kDqTile (kDqTileMerged
+  // when tiny segments are merged): one schedule each.
   mf::AttnArgs aq = a;
   aq.order = a.pt + n_segments + 1;
   aq.pt = aq.order + n_segments;
@@ -492,8 +493,8 @@ mf_status attn_bwd_impl(int nax, const void* q, const void* k, const void* v, co
     r = mf::launch_sched(cu_seqlens, n_segments, n_tokens, mf::kDkdvTile, const_cast<int*>(a.order),
                          const_cast<int*>(a.pt), s);
     if (r != hipSuccess) return r;
-    return mf::launch_sched(aq.cu_seqlens, n_segments, n_tokens, mf::kDqTile, const_cast<int*>(aq.order),
-                            const_cast<int*>(aq.pt), s);
+    return mf::launch_sched(aq.cu_seqlens, n_segments, n_tokens, merge ? mf::kDqTileMerged : mf::kDqTile,
+                            const_cast<int*>(aq.order), const_cast<int*>(aq.pt), s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
   // dq first: it also writes Delta and the log2-scaled LSE that dkdv reads.

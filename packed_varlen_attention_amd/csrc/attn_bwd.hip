@@ -5,7 +5,9 @@
 //   dV = P^T dO,  dKr = scale * dS^T Qr          dkdv kernel, per 32 keys/wave
 //                                                (K in registers, V rows in LDS)
 //   dQr = scale * dS Kr                          dq kernel,   per 32 queries/wave
-//                                                (8 waves, K/V tiles three-buffered)
+//                                                (8 waves and 64-key tiles, or 4
+//                                                and 32 where tiny segments are
+//                                                merged; K/V tiles three-buffered)
 // where dS = P * (dO V^T - Delta); dQ and dK are rotated back by the inverse
 // rotation in the epilogues.  Each output element is written by exactly one
 // lane and summed in a fixed order: results are deterministic (no atomics).
@@ -20,9 +22,6 @@ namespace {
 
 constexpr int kKB = kDkdvTile;  // keys per dkdv workgroup (32 per wave)
 constexpr int kQB = 32;         // queries per dkdv LDS tile
-constexpr int kQT = kDqTile;    // queries per dq workgroup (32 per wave)
-constexpr int kDqWaves = kQT / 32;
-constexpr int kKT = 64;         // keys per dq LDS tile
 
 template <int D, typename TOut>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(
@@ -207,14 +206,20 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(
   }
 }
 
-template <int D, typename TOut, bool kMulti>
-__global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(
+// dq in two shapes: QT queries per workgroup (32 per wave) and KT keys per
+// LDS tile.  256 x 64 for ordinary packs; 128 x 32 where runs of tiny
+// segments are merged, so that two short-lived workgroups share a CU.
+template <int D, typename TOut, bool kMulti, int QT, int KT>
+__global__ __launch_bounds__(QT / 32 * 64, 2) void dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     const uint16_t* __restrict__ dob, const TOut* __restrict__ o, const TOut* __restrict__ dout,
     const float* __restrict__ lse, float* __restrict__ lse2, float* __restrict__ delta,
     TOut* __restrict__ dq, const int* __restrict__ cu, const int* __restrict__ order, const int* __restrict__ pt,
     int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax, const float2* __restrict__ tab,
     int max_pos, float scale, float scale_log2, const int* __restrict__ rcu, const int* __restrict__ vfirst) {
+  constexpr int kQT = QT;
+  constexpr int kKT = KT;
+  constexpr int kDqWaves = QT / 32;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int kRowBytes = D * 2;
@@ -448,27 +453,41 @@ hipError_t launch_dkdv_t(const AttnArgs& a, const void* qr, const void* kr, cons
   return hipGetLastError();
 }
 
-template <int D, typename TOut>
+template <int D, typename TOut, int QT, int KT, bool kMerged>
 hipError_t launch_dq_t(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,
                        const void* o, const void* dout, const float* lse, float* lse2, float* delta, void* dq,
                        hipStream_t stream) {
-  const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kQT);
+  const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, QT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((dq_kernel<D, TOut, false>), dim3(static_cast<unsigned>(blocks)), dim3(kDqWaves * 64), 0, stream,
-                     static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
+  hipLaunchKernelGGL((dq_kernel<D, TOut, false, QT, KT>), dim3(static_cast<unsigned>(blocks)), dim3(QT / 32 * 64), 0,
+                     stream, static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
                      static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob),
                      static_cast<const TOut*>(o), static_cast<const TOut*>(dout), lse, lse2, delta,
                      static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
                      a.pos, a.nax, a.tab, a.max_pos, a.scale, a.scale * kLog2e, a.rcu, a.vfirst);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.vfirst == nullptr) return e;
-  hipLaunchKernelGGL((dq_kernel<D, TOut, true>), dim3(static_cast<unsigned>(blocks)), dim3(kDqWaves * 64), 0, stream,
-                     static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
-                     static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob),
-                     static_cast<const TOut*>(o), static_cast<const TOut*>(dout), lse, lse2, delta,
-                     static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     a.pos, a.nax, a.tab, a.max_pos, a.scale, a.scale * kLog2e, a.rcu, a.vfirst);
-  return hipGetLastError();
+  if constexpr (kMerged) {
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dq_kernel<D, TOut, true, QT, KT>), dim3(static_cast<unsigned>(blocks)), dim3(QT / 32 * 64),
+                       0, stream, static_cast<const uint16_t*>(qr), static_cast<const uint16_t*>(kr),
+                       static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(dob),
+                       static_cast<const TOut*>(o), static_cast<const TOut*>(dout), lse, lse2, delta,
+                       static_cast<TOut*>(dq), a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
+                       a.pos, a.nax, a.tab, a.max_pos, a.scale, a.scale * kLog2e, a.rcu, a.vfirst);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// The merged shape runs exactly when the call merged tiny segments (vfirst
+// set); its schedule was built with kDqTileMerged.
+template <int D, typename TOut>
+hipError_t launch_dq_any(const AttnArgs& a, const void* qr, const void* kr, const void* vb, const void* dob,
+                         const void* o, const void* dout, const float* lse, float* lse2, float* delta, void* dq,
+                         hipStream_t stream) {
+  if (a.vfirst != nullptr)
+    return launch_dq_t<D, TOut, kDqTileMerged, 32, true>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream);
+  return launch_dq_t<D, TOut, kDqTile, 64, false>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream);
 }
 
 }  // namespace
@@ -487,10 +506,11 @@ hipError_t launch_attn_bwd_dq(const AttnArgs& a, const void* qr, const void* kr,
                               hipStream_t stream) {
   if (a.head_dim == 128)
     return a.dtype == kDtypeBf16
-               ? launch_dq_t<128, uint16_t>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream)
-               : launch_dq_t<128, float>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream);
-  return a.dtype == kDtypeBf16 ? launch_dq_t<64, uint16_t>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream)
-                               : launch_dq_t<64, float>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream);
+               ? launch_dq_any<128, uint16_t>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream)
+               : launch_dq_any<128, float>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream);
+  return a.dtype == kDtypeBf16
+             ? launch_dq_any<64, uint16_t>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream)
+             : launch_dq_any<64, float>(a, qr, kr, vb, dob, o, dout, lse, lse2, delta, dq, stream);
 }
 
 }  // namespace mf

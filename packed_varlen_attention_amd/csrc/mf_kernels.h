@@ -44,6 +44,7 @@ long long sched_grid(int n_tokens, int n_segments, int heads, int tile);
 
 constexpr int kFwdTile = 128;   // query rows per forward workgroup (4 waves)
 constexpr int kDqTile = 256;    // query rows per dq workgroup (8 waves)
+constexpr int kDqTileMerged = 128;  // the same when tiny segments are merged (4 waves)
 constexpr int kDkdvTile = 128;  // keys per dkdv workgroup
 
 struct AttnArgs {
