@@ -41,7 +41,26 @@ def _layouts():
     threshold = [(127, 0, 0), (128, 0, 0), (0, 1, 1), (129, 0, 0), (1, 0, 0), (126, 1, 1), (1, 1, 1), (0, 0, 0),
                  (0, 8, 16), (64, 0, 0), (1, 0, 0)]
     ones = [(1, 0, 0)] * 60 + [(0, 0, 0)] * 5 + [(0, 1, 1)] * 40 + [(2, 0, 0)] * 30 + [(1, 1, 2)] * 20 + [(1, 0, 0)] * 30
-    return {"all_tiny": all_tiny, "mixed": mixed, "threshold": threshold, "ones": ones}
+    # groups of 200-255 tokens: each spans two 128-row query tiles of the forward (and of dq's merged shape)
+    wide = [(100, 0, 0), (120, 0, 0), (8, 0, 0), (127, 0, 0), (1, 0, 0), (60, 0, 0), (68, 0, 0), (128, 0, 0),
+            (90, 0, 0), (37, 0, 0), (100, 0, 0), (26, 0, 0)]
+    return {"all_tiny": all_tiny, "mixed": mixed, "threshold": threshold, "ones": ones, "wide": wide}
+
+
+def _group_spans(cu):
+    """Token spans of the multi-segment groups gpu_util.merged_segments forms."""
+    merged = merged_segments(cu)
+    spans, run = [], []
+    for s in range(len(cu) - 1):
+        if s in merged and run and (s - 1) in run and int(cu[s]) // 128 == int(cu[run[0]]) // 128:
+            run.append(s)
+            continue
+        if len(run) > 1:
+            spans.append(int(cu[run[-1] + 1]) - int(cu[run[0]]))
+        run = [s] if s in merged else []
+    if len(run) > 1:
+        spans.append(int(cu[run[-1] + 1]) - int(cu[run[0]]))
+    return spans
 
 
 LAYOUTS = _layouts()
@@ -54,6 +73,8 @@ def test_forward_and_backward_against_oracle(name, d):
     c = Case(LAYOUTS[name], 1 << 20, 3, d, "bf16", seed=91, with_dout=True)
     merged = merged_segments(c.cu)
     assert merged, "layout must produce multi-segment tiles"
+    if name == "wide":
+        assert max(_group_spans(c.cu)) > 128, "layout must produce groups that span two 128-row tiles"
     note(f"tiny segments {name} D={d} {c.describe()} merged={len(merged)}")
     o, lse = mf.attn_fwd(c.tq, c.tk, c.tv, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
     dq, dk, dv = mf.attn_bwd(c.tq, c.tk, c.tv, o, lse, c.tdo, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
