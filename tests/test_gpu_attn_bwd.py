@@ -46,10 +46,11 @@ def test_small_packs_all_elements(dtype, d):
     assert_close(host_f64(dv)[:n], rv[:n], G_MAX, G_MEAN, f"dV {dtype} D{d}")
 
 
-# Segment lengths around the tile sizes: one forward / dq query tile holds
-# 256 rows and one dkdv workgroup 128 keys.  In a segment that fits one such
-# tile, waves whose rows (keys) all lie past the end skip their products; at
-# 257 and beyond they do not.  Every element is checked either way.
+# Segment lengths around the tile sizes: a forward query tile holds 128 rows
+# and a forward key tile 32 keys, a dq query tile 256 rows (64-key tiles), a
+# dkdv workgroup 128 keys.  In a segment that fits one such tile, waves whose
+# rows (keys) all lie past the end skip their products; in longer segments
+# they do not.  Every element is checked either way.
 TILE_EDGES = [(127, 0, 0), (128, 0, 0), (129, 0, 0), (224, 0, 0), (225, 0, 0), (31, 0, 0), (255, 0, 0),
               (256, 0, 0), (257, 0, 0), (288, 0, 0), (16, 15, 16), (1, 16, 16), (32, 0, 0), (33, 0, 0),
               (64, 0, 0), (65, 0, 0)]

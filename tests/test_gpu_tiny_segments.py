@@ -90,6 +90,25 @@ def test_forward_and_backward_against_oracle(name, d):
     assert_close_large_values(host_f64(dv), rv, "dV")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_float32_groups_spanning_two_tiles(d):
+    # float32 input takes the conversion passes and the float32 instances of the merged shapes
+    mf = _mf()
+    c = Case(LAYOUTS["wide"], 1 << 20, 2, d, "f32", seed=93, with_dout=True)
+    assert max(_group_spans(c.cu)) > 128
+    note(f"tiny segments wide f32 D={d} {c.describe()}")
+    o, lse = mf.attn_fwd(c.tq, c.tk, c.tv, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    dq, dk, dv = mf.attn_bwd(c.tq, c.tk, c.tv, o, lse, c.tdo, c.tcu, c.max_seqlen, c.tpos, THETA, c.max_pos)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_fwd(c.q, c.k, c.v, c.cu, c.pos, THETA)
+    assert_close(host_f64(o)[: c.n], ro, O_MAX, O_MEAN, "O")
+    assert_close(host_f64(lse)[:, : c.n], rl, LSE_MAX, LSE_MAX, "LSE")
+    rq, rk, rv = oracle.attn_bwd(c.q, c.k, c.v, c.do, c.cu, c.pos, THETA)
+    assert_close_large_values(host_f64(dq), rq, "dQ")
+    assert_close_large_values(host_f64(dk), rk, "dK")
+    assert_close_large_values(host_f64(dv), rv, "dV")
+
+
 def test_members_of_a_shared_tile_are_isolated_bitwise():
     mf = _mf()
     c = Case(LAYOUTS["mixed"], 1 << 20, 2, 128, "bf16", seed=92, with_dout=True)
