@@ -14,7 +14,7 @@ the test checks two things:
 * an implementation with those roundings and no other error stays inside the
   bar, with margin, on the GPU test's own inputs, for every admissible
   rounding outcome: the forward's running max may lag a row's true maximum
-  by up to 8 in log2 units once a segment spans more than one 64-key tile,
+  by up to 8 in log2 units once a segment spans more than one 32-key tile,
   so the weights it rounds sit up to 2^8 above exp(S - max); the model draws
   that lag at random per row for such segments (``lag_seed``);
 * a planted mistake (one key dropped from every segment's softmax) falls
@@ -65,7 +65,7 @@ def _scores(qr, kr, sc, drop_last_key):
     return s
 
 
-KEY_TILE = 64
+KEY_TILE = 32  # keys per forward tile: the running max can lag from the second tile on
 LAGS = (None, 1, 2, 3, 4)  # no lag, then four random lag draws
 
 
