@@ -350,8 +350,8 @@ mf_status attn_fwd_run(int nax, const void* q, const void* k, const void* v, voi
       hipError_t r = mf::launch_merge_tiny(cu_seqlens, n_segments, n_tokens, vcu, vfirst, s);
       if (r != hipSuccess) return r;
     }
-    return mf::launch_sched(a.cu_seqlens, n_segments, n_tokens, mf::kFwdTile, const_cast<int*>(a.order),
-                            const_cast<int*>(a.pt), s);
+    return mf::launch_sched(a.cu_seqlens, n_segments, n_tokens, mf::fwd_tile(max_seqlen, n_tokens, n_segments),
+                            const_cast<int*>(a.order), const_cast<int*>(a.pt), s);
   });
   if (e != hipSuccess) return MF_ERR_HIP;
   e = tr.run("attn_fwd", [&] { return mf::launch_attn_fwd(a, q, kr, vb, o, lse, s); });

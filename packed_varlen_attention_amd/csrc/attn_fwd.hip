@@ -9,7 +9,9 @@
 // all four share each K/V tile.  With <= 168 registers per lane and 48 KB of
 // LDS per workgroup, three workgroups share a CU, so each SIMD runs three
 // waves and interleaves their matrix, vector and LDS work.  The loop walks
-// the segment's keys in tiles of 32, software-pipelined:
+// the segment's keys in tiles of 32, software-pipelined.  Packs whose
+// segments are all long (fwd_tile()) run the same kernel as 8 waves = 256 rows
+// on 64-key tiles instead, one workgroup per CU at two waves per SIMD:
 //   K and V tiles are copied global -> LDS directly (no registers) into
 //   three buffers each, two tiles ahead, each copy a block-uniform tile base
 //   plus a fixed 32-bit lane offset; K runs one tile ahead of V, so the
@@ -33,11 +35,6 @@ namespace mf {
 
 namespace {
 
-constexpr int kQT = kFwdTile;  // query rows per workgroup
-constexpr int kKT = 32;        // keys per LDS tile
-constexpr int kWaves = kQT / 32;  // waves per workgroup, 32 query rows each
-constexpr int kWavesPerSimd = 3;  // resident waves per SIMD (sets the register budget)
-constexpr int kKB = kKT / 32;  // 32-key blocks per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag
 
 // v_permlane32_swap: each lane gets its own value and the one of the lane
@@ -61,13 +58,19 @@ __device__ __forceinline__ void load_q8(const T* p, bool ok, float (&x)[8]) {
   }
 }
 
-template <int D, typename TIn, bool kMulti>
-__global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void attn_fwd_kernel(
+// QT query rows per workgroup (32 per wave), KT keys per LDS tile, WPS
+// resident waves per SIMD (sets the register budget).
+template <int D, typename TIn, bool kMulti, int QT, int KT, int WPS>
+__global__ __launch_bounds__(QT / 32 * 64, WPS) void attn_fwd_kernel(
     const TIn* __restrict__ q, const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vb,
     TIn* __restrict__ o, float* __restrict__ lse, const int* __restrict__ cu, const int* __restrict__ order,
     const int* __restrict__ pt, int n_seg, int n_tokens, int heads, const int* __restrict__ pos, int nax,
     const float2* __restrict__ tab, int max_pos, float scale_log2, const int* __restrict__ rcu,
     const int* __restrict__ vfirst, uint16_t* __restrict__ qr_out) {
+  constexpr int kQT = QT;
+  constexpr int kKT = KT;
+  constexpr int kWaves = QT / 32;
+  constexpr int kKB = KT / 32;  // 32-key blocks per tile
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int kRowBytes = D * 2;
@@ -318,26 +321,36 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void attn_fwd_kernel(
   }
 }
 
-template <int D, typename TIn>
+template <int D, typename TIn, int QT, int KT, int WPS>
 hipError_t launch_fwd_t(const AttnArgs& a, const void* q, const void* kr, const void* vb, void* o, float* lse,
                         hipStream_t stream) {
-  const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, kQT);
+  const long long blocks = sched_grid(a.n_tokens, a.n_segments, a.n_heads, QT);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   // The ordinary tiles, then (with merged tiny segments) the multi-segment
   // ones; each launch's blocks exit at once on the other kind of item.
-  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, false>), dim3(static_cast<unsigned>(blocks)), dim3(kWaves * 64), 0, stream,
-                     static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
-                     static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst,
-                     static_cast<uint16_t*>(a.qr_out));
+  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, false, QT, KT, WPS>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(QT / 32 * 64), 0, stream, static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr),
+                     static_cast<const uint16_t*>(vb), static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt,
+                     a.n_segments, a.n_tokens, a.n_heads, a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu,
+                     a.vfirst, static_cast<uint16_t*>(a.qr_out));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.vfirst == nullptr) return e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, true>), dim3(static_cast<unsigned>(blocks)), dim3(kWaves * 64), 0, stream,
-                     static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr), static_cast<const uint16_t*>(vb),
-                     static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt, a.n_segments, a.n_tokens, a.n_heads,
-                     a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu, a.vfirst,
-                     static_cast<uint16_t*>(a.qr_out));
+  hipLaunchKernelGGL((attn_fwd_kernel<D, TIn, true, QT, KT, WPS>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(QT / 32 * 64), 0, stream, static_cast<const TIn*>(q), static_cast<const uint16_t*>(kr),
+                     static_cast<const uint16_t*>(vb), static_cast<TIn*>(o), lse, a.cu_seqlens, a.order, a.pt,
+                     a.n_segments, a.n_tokens, a.n_heads, a.pos, a.nax, a.tab, a.max_pos, a.scale * kLog2e, a.rcu,
+                     a.vfirst, static_cast<uint16_t*>(a.qr_out));
   return hipGetLastError();
+}
+
+// The shape fwd_tile() picks for the call; the schedule was built with the
+// same tile.
+template <int D, typename TIn>
+hipError_t launch_fwd_any(const AttnArgs& a, const void* q, const void* kr, const void* vb, void* o, float* lse,
+                          hipStream_t stream) {
+  if (fwd_tile(a.max_seqlen, a.n_tokens, a.n_segments) == kFwdTileLong)
+    return launch_fwd_t<D, TIn, kFwdTileLong, 64, 2>(a, q, kr, vb, o, lse, stream);
+  return launch_fwd_t<D, TIn, kFwdTile, 32, 3>(a, q, kr, vb, o, lse, stream);
 }
 
 }  // namespace
@@ -345,11 +358,11 @@ hipError_t launch_fwd_t(const AttnArgs& a, const void* q, const void* kr, const 
 hipError_t launch_attn_fwd(const AttnArgs& a, const void* q, const void* kr, const void* vb, void* o, float* lse,
                            hipStream_t stream) {
   if (a.head_dim == 128) {
-    return a.dtype == kDtypeBf16 ? launch_fwd_t<128, uint16_t>(a, q, kr, vb, o, lse, stream)
-                                 : launch_fwd_t<128, float>(a, q, kr, vb, o, lse, stream);
+    return a.dtype == kDtypeBf16 ? launch_fwd_any<128, uint16_t>(a, q, kr, vb, o, lse, stream)
+                                 : launch_fwd_any<128, float>(a, q, kr, vb, o, lse, stream);
   }
-  return a.dtype == kDtypeBf16 ? launch_fwd_t<64, uint16_t>(a, q, kr, vb, o, lse, stream)
-                               : launch_fwd_t<64, float>(a, q, kr, vb, o, lse, stream);
+  return a.dtype == kDtypeBf16 ? launch_fwd_any<64, uint16_t>(a, q, kr, vb, o, lse, stream)
+                               : launch_fwd_any<64, float>(a, q, kr, vb, o, lse, stream);
 }
 
 }  // namespace mf

@@ -170,6 +170,19 @@ def test_full_size_eight_heads(name):
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse[:, :n]).all()
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_long_segments_take_the_256_row_shape(d):
+    """A pack whose segments are all long (the longest at least 12288 tokens,
+    the mean at least 8192) runs the forward's 256-row, 64-key form; both
+    segments end mid-tile in either shape.  Every element of O and LSE."""
+    c = Case([(12307, 0, 0), (13001, 0, 0)], 1 << 20, 1, d, "bf16", seed=29)
+    assert c.max_seqlen >= 12288 and c.n >= 8192 * (len(c.cu) - 1)
+    o, lse = _run(c)
+    ref_o, ref_l = _full_ref(c)
+    assert_close(host_f64(o)[: c.n], ref_o[: c.n], O_MAX, O_MEAN, f"O long segments D{d}")
+    assert_close(host_f64(lse)[:, : c.n], ref_l[:, : c.n], LSE_MAX, LSE_MAX, f"LSE long segments D{d}")
+
+
 def test_more_segments_than_the_scheduler_sorts():
     """Over 1024 segments the schedule keeps the given order instead of sorting
     by length: results must not depend on that."""
