@@ -46,9 +46,10 @@ constexpr int kFwdTile = 128;   // query rows per forward workgroup (4 waves, 32
 constexpr int kFwdTileLong = 256;  // the same for packs of long segments (8 waves, 64-key tiles)
 // The forward's shape for a call.  The 128-row form runs three workgroups per
 // CU; the 256-row form shares each K/V tile among twice the rows and is
-// faster once every sweep is long: 2% at 16k-token segments, and the 128-row
-// form 1% at 8k and 5-7% at 4k and 2k.  So the 256-row form is taken when the
-// longest segment has at least 12288 tokens and the mean one at least 8192.
+// faster once every sweep is long: by 2% on packs of 16k-token segments,
+// while the 128-row form is faster by 1% at 8k, 5% at 4k and 7% at 2k.  So
+// the 256-row form is taken when the longest segment has at least 12288
+// tokens and the mean one at least 8192.
 inline int fwd_tile(int max_seqlen, int n_tokens, int n_segments) {
   return max_seqlen >= 12288 && static_cast<long long>(n_tokens) >= 8192LL * n_segments ? kFwdTileLong : kFwdTile;
 }
